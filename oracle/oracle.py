@@ -1,0 +1,185 @@
+"""Python face of the CPU oracle (``srftq_oracle.c``), via ctypes and numpy.
+
+TEST INFRASTRUCTURE ONLY: imported by the test-suite, the smoke check and the
+CPU-baseline leg of the benchmark, never by the GPU library.  The oracle is a
+plain fp64 implementation of the definition of the sign-randomized Fourier
+(or Walsh-Hadamard) rotation followed by per-channel lambda scaling,
+per-group absmax scaling and symmetric int4/int8 rounding, as described in
+"When Quantization Is Free" (gist.science technical summary, "Metodologia"
+sections 1-3).  Each C function documents the reading it takes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "srftq_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+ROT = {"srft": 0, "srht": 1, "none": 2}
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (fp64, OpenMP, no FMA contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+               "-ffp-contract=off", "-fno-fast-math", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        build()
+        L = ctypes.CDLL(_LIB)
+        i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+        L.oracle_rotate.argtypes = [i64, i64, i32, i32, i32, vp, vp, vp]
+        L.oracle_unrotate.argtypes = [i64, i64, i32, i32, i32, vp, vp, vp]
+        L.oracle_quantize.argtypes = [i64, i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]
+        L.oracle_dequantize.argtypes = [i64, i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]
+        L.oracle_calibrate_lambda.argtypes = [i64, i64, i32, i32, i32, vp, vp, vp]
+        L.oracle_f16_array_to_f64.argtypes = [vp, vp, i64]
+        L.oracle_f64_array_to_f16.argtypes = [vp, vp, i64]
+        L.oracle_f64_to_f16.argtypes = [ctypes.c_double]
+        L.oracle_f64_to_f16.restype = ctypes.c_uint16
+        L.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
+        L.oracle_f16_to_f64.restype = ctypes.c_double
+        for f in ("oracle_rotate", "oracle_unrotate", "oracle_quantize",
+                  "oracle_dequantize", "oracle_calibrate_lambda", "oracle_num_threads"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _as4(x, d=None):
+    """Accept [T,H,d] or [B,T,H,d]; return the 4-D view and B, T, H, d."""
+    if x.ndim == 3:
+        x = x[None]
+    assert x.ndim == 4
+    B, T, H, dd = x.shape
+    return x, B, T, H, dd
+
+
+def _bits(x16: np.ndarray) -> np.ndarray:
+    """fp16 array (or uint16 bit array) as contiguous uint16 bits."""
+    if x16.dtype == np.float16:
+        return np.ascontiguousarray(x16).view(np.uint16)
+    assert x16.dtype == np.uint16
+    return np.ascontiguousarray(x16)
+
+
+def _signs(signs, B, H, d):
+    if signs is None:
+        return None
+    s = np.ascontiguousarray(np.asarray(signs, dtype=np.int8)).reshape(B, H, d)
+    return s
+
+
+def _lam(lam, B, H, d):
+    if lam is None:
+        return None
+    return np.ascontiguousarray(np.asarray(lam, dtype=np.float32)).reshape(B, H, d)
+
+
+def _check(st, what):
+    if st != 0:
+        raise ValueError(f"{what}: oracle status {st}")
+
+
+def rotate(x16, signs=None, rot="srft") -> np.ndarray:
+    """fp64 rotated coordinates y = M (s . x), same shape as x."""
+    x, B, T, H, d = _as4(_bits(x16))
+    s = _signs(signs, B, H, d)
+    y = np.empty((B, T, H, d), dtype=np.float64)
+    _check(lib().oracle_rotate(B, T, H, d, ROT[rot], _ptr(x), _ptr(s), _ptr(y)), "rotate")
+    return y.reshape(x16.shape)
+
+
+def unrotate(y, signs=None, rot="srft") -> np.ndarray:
+    """fp64 x = s . (M^T y), same shape as y."""
+    y4, B, T, H, d = _as4(np.ascontiguousarray(y, dtype=np.float64))
+    s = _signs(signs, B, H, d)
+    out = np.empty((B, T, H, d), dtype=np.float64)
+    _check(lib().oracle_unrotate(B, T, H, d, ROT[rot], _ptr(y4), _ptr(s), _ptr(out)), "unrotate")
+    return out.reshape(np.shape(y))
+
+
+def quantize(x16, signs=None, lam=None, group=16, bits=4, rot="srft", return_z=False):
+    """Return (codes uint8, scales fp16-bits uint16[, z fp32])."""
+    x, B, T, H, d = _as4(_bits(x16))
+    s = _signs(signs, B, H, d)
+    l = _lam(lam, B, H, d)
+    codes = np.empty((B, T, H, d * bits // 8), dtype=np.uint8)
+    scales = np.empty((B, T, H, d // group), dtype=np.uint16)
+    z = np.empty((B, T, H, d), dtype=np.float32) if return_z else None
+    _check(lib().oracle_quantize(B, T, H, d, group, bits, ROT[rot], _ptr(x), _ptr(s), _ptr(l),
+                                 _ptr(codes), _ptr(scales), _ptr(z)), "quantize")
+    lead = x16.shape[:-1]
+    out = (codes.reshape(*lead, -1), scales.reshape(*lead, -1))
+    if return_z:
+        out = out + (z.reshape(x16.shape),)
+    return out
+
+
+def dequantize(codes, scales, signs=None, lam=None, group=16, bits=4, rot="srft", d=None,
+               return_f64=False):
+    """Return fp16 bits (uint16) of the reconstruction (and fp64 values)."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint16)
+    if d is None:
+        d = codes.shape[-1] * 8 // bits
+    c4 = codes if codes.ndim == 4 else codes[None]
+    B, T, H = c4.shape[:3]
+    s = _signs(signs, B, H, d)
+    l = _lam(lam, B, H, d)
+    x = np.empty((B, T, H, d), dtype=np.uint16)
+    x64 = np.empty((B, T, H, d), dtype=np.float64) if return_f64 else None
+    _check(lib().oracle_dequantize(B, T, H, d, group, bits, ROT[rot], _ptr(c4),
+                                   _ptr(scales), _ptr(s), _ptr(l), _ptr(x), _ptr(x64)),
+           "dequantize")
+    lead = codes.shape[:-1]
+    if return_f64:
+        return x.reshape(*lead, d), x64.reshape(*lead, d)
+    return x.reshape(*lead, d)
+
+
+def calibrate_lambda(x16, signs=None, rot="srft") -> np.ndarray:
+    """fp32 lambda [B,H,d] (or [H,d] for 3-D x) = 1/RMS over tokens of rotated coords."""
+    x, B, T, H, d = _as4(_bits(x16))
+    s = _signs(signs, B, H, d)
+    lam = np.empty((B, H, d), dtype=np.float32)
+    _check(lib().oracle_calibrate_lambda(B, T, H, d, ROT[rot], _ptr(x), _ptr(s), _ptr(lam)),
+           "calibrate_lambda")
+    return lam if x16.ndim == 4 else lam[0]
+
+
+def f16_to_f64(h) -> np.ndarray:
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    out = np.empty(h.shape, dtype=np.float64)
+    lib().oracle_f16_array_to_f64(_ptr(h), _ptr(out), h.size)
+    return out
+
+
+def f64_to_f16(v) -> np.ndarray:
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    out = np.empty(v.shape, dtype=np.uint16)
+    lib().oracle_f64_array_to_f16(_ptr(v), _ptr(out), v.size)
+    return out
+
+
+def num_threads() -> int:
+    return int(lib().oracle_num_threads())

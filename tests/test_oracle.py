@@ -1,0 +1,401 @@
+"""Pins for the CPU oracle: each check ties it to something other than itself.
+
+Sources: "When Quantization Is Free" (gist.science technical summary),
+"Metodologia" 1 (SRFT(x) = pack(F diag(s) x), F the unitary DFT; SRHT as the
+Hadamard alternative) and 2 (pipeline order, per-group absmax, signed int4 /
+int8 rounding, two int4 per byte); HyperQuant summary, "Metodologia" 1 (the
+per-tile RHT = H D x).  The pins are closed forms, library routines the
+special cases reduce to (numpy's real FFT, scipy's Sylvester Hadamard,
+numpy's IEEE half conversion), brute force on tiny inputs, and invariants.
+"""
+import math
+
+import numpy as np
+import pytest
+import scipy.linalg
+
+from oracle import oracle
+
+
+def _f16(a):
+    return np.asarray(a, dtype=np.float64).astype(np.float16)
+
+
+def _rand_x(rng, shape, scale=1.0):
+    return _f16(rng.standard_normal(shape) * scale)
+
+
+def _rand_signs(rng, B, H, d):
+    return (1 - 2 * rng.integers(0, 2, size=(B, H, d))).astype(np.int8)
+
+
+# --------------------------------------------------------------------------
+# IEEE half conversions (the oracle's own, written from the format).
+# --------------------------------------------------------------------------
+
+def test_f16_to_f64_all_bit_patterns():
+    bits = np.arange(1 << 16, dtype=np.uint16)
+    ours = oracle.f16_to_f64(bits)
+    ref = bits.view(np.float16).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+
+
+def test_f64_to_f16_round_to_nearest_even():
+    rng = np.random.default_rng(1)
+    parts = [
+        rng.standard_normal(200000) * 10.0 ** rng.integers(-9, 6, 200000),
+        # exact halfway points between adjacent halves (ties)
+        (np.arange(1 << 16, dtype=np.uint16).view(np.float16).astype(np.float64)),
+    ]
+    h = np.arange(0x0000, 0x7bff, dtype=np.uint16).view(np.float16).astype(np.float64)
+    mid = (h[:-1] + np.diff(h) / 2.0)
+    parts.append(mid)
+    parts.append(-mid)
+    v = np.concatenate(parts)
+    v = v[np.isfinite(v)]
+    ours = oracle.f64_to_f16(v)
+    with np.errstate(over="ignore"):
+        ref = v.astype(np.float16).view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+@pytest.mark.parametrize("v,expect", [
+    (2049.0, 2048.0),            # tie -> even significand
+    (2051.0, 2052.0),
+    (65519.0, 65504.0),
+    (65520.0, np.inf),           # halfway to 2^16 rounds to even = overflow
+    (2.0 ** -25, 0.0),           # tie between 0 and the smallest subnormal
+    (3 * 2.0 ** -25, 2.0 ** -23),
+    (1.0 + 2.0 ** -11, 1.0),
+    (1.0 + 3 * 2.0 ** -11, 1.0 + 2.0 ** -9),
+])
+def test_f64_to_f16_hand_cases(v, expect):
+    got = oracle.f16_to_f64(oracle.f64_to_f16(np.array([v])))[0]
+    assert got == expect
+
+
+# --------------------------------------------------------------------------
+# SRFT rotation.
+# --------------------------------------------------------------------------
+
+def _pack_rfft(x_signed):
+    """Pack numpy's orthonormal rfft into the d-real layout (reading of the
+    Hermitian unpack): [Re X0, sqrt2 Re X1..X_{N-1}, Re X_N, sqrt2 Im X1..]."""
+    d = x_signed.shape[-1]
+    N = d // 2
+    X = np.fft.rfft(x_signed, norm="ortho")
+    y = np.empty(x_signed.shape, dtype=np.float64)
+    y[..., 0] = X[..., 0].real
+    y[..., 1:N] = math.sqrt(2.0) * X[..., 1:N].real
+    y[..., N] = X[..., N].real
+    y[..., N + 1:] = math.sqrt(2.0) * X[..., 1:N].imag
+    return y
+
+
+@pytest.mark.parametrize("d", [8, 16, 64, 128, 256])
+def test_srft_matches_numpy_rfft(d):
+    rng = np.random.default_rng(d)
+    B, T, H = 2, 5, 3
+    x = _rand_x(rng, (B, T, H, d))
+    s = _rand_signs(rng, B, H, d)
+    y = oracle.rotate(x, s, "srft")
+    xs = x.astype(np.float64) * s[:, None, :, :]
+    ref = _pack_rfft(xs)
+    assert np.max(np.abs(y - ref)) <= 1e-12 * max(1.0, np.max(np.abs(ref)))
+
+
+def test_srft_brute_force_d8():
+    d, N = 8, 4
+    rng = np.random.default_rng(8)
+    x = _rand_x(rng, (1, 7, 1, d))
+    s = _rand_signs(rng, 1, 1, d)
+    y = oracle.rotate(x, s, "srft")
+    F = np.array([[np.exp(-2j * np.pi * j * k / d) for j in range(d)] for k in range(d)]) / np.sqrt(d)
+    for t in range(7):
+        X = F @ (x[0, t, 0].astype(np.float64) * s[0, 0])
+        r2 = np.sqrt(2.0)
+        ref = np.array([X[0].real, r2 * X[1].real, r2 * X[2].real, r2 * X[3].real,
+                        X[4].real, r2 * X[1].imag, r2 * X[2].imag, r2 * X[3].imag])
+        assert np.allclose(y[0, t, 0], ref, atol=1e-13, rtol=0)
+
+
+@pytest.mark.parametrize("rot", ["srft", "srht"])
+@pytest.mark.parametrize("d", [8, 32, 128, 256])
+def test_rotation_is_orthogonal(rot, d):
+    eye = np.eye(d).astype(np.float16).reshape(d, 1, d)          # d basis vectors
+    M = oracle.rotate(eye, None, rot).reshape(d, d).T              # columns = M e_j
+    assert np.max(np.abs(M.T @ M - np.eye(d))) < 1e-13
+    assert np.max(np.abs(M @ M.T - np.eye(d))) < 1e-13
+
+
+@pytest.mark.parametrize("rot", ["srft", "srht", "none"])
+@pytest.mark.parametrize("d", [16, 64, 128, 256])
+def test_parseval_and_inverse(rot, d):
+    rng = np.random.default_rng(d + 7)
+    x = _rand_x(rng, (2, 9, 2, d), scale=3.0)
+    s = _rand_signs(rng, 2, 2, d)
+    y = oracle.rotate(x, s, rot)
+    xf = x.astype(np.float64)
+    assert np.allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(xf, axis=-1), rtol=1e-13, atol=0)
+    back = oracle.unrotate(y, s, rot)
+    assert np.max(np.abs(back - xf)) < 1e-12 * np.max(np.abs(xf))
+
+
+@pytest.mark.parametrize("d", [8, 64, 128])
+def test_srft_delta_closed_form(d):
+    N = d // 2
+    rng = np.random.default_rng(3 * d)
+    s = _rand_signs(rng, 1, 1, d)
+    for j0 in [0, 1, 5 % d, N - 1, N, d - 1]:
+        x = np.zeros((1, 1, 1, d), dtype=np.float16)
+        x[..., j0] = 1.0
+        y = oracle.rotate(x, s, "srft")[0, 0, 0]
+        k = np.arange(1, N)
+        ref = np.concatenate([[1.0], np.sqrt(2) * np.cos(2 * np.pi * j0 * k / d),
+                              [(-1.0) ** j0], -np.sqrt(2) * np.sin(2 * np.pi * j0 * k / d)])
+        ref *= s[0, 0, j0] / np.sqrt(d)
+        assert np.allclose(y, ref, atol=1e-14, rtol=0)
+
+
+@pytest.mark.parametrize("d", [8, 64, 256])
+def test_srft_constant_and_alternating(d):
+    N = d // 2
+    c = 1.5
+    x = np.full((1, 1, 1, d), c, dtype=np.float16)
+    y = oracle.rotate(x, None, "srft")[0, 0, 0]
+    e = np.zeros(d)
+    e[0] = c * np.sqrt(d)
+    assert np.allclose(y, e, atol=1e-13, rtol=0)
+    xa = (c * (-1.0) ** np.arange(d)).astype(np.float16).reshape(1, 1, 1, d)
+    ya = oracle.rotate(xa, None, "srft")[0, 0, 0]
+    e = np.zeros(d)
+    e[N] = c * np.sqrt(d)
+    assert np.allclose(ya, e, atol=1e-13, rtol=0)
+
+
+# --------------------------------------------------------------------------
+# SRHT rotation.
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d", [2, 8, 64, 128, 256])
+def test_srht_matches_scipy_hadamard(d):
+    rng = np.random.default_rng(d + 11)
+    x = _rand_x(rng, (1, 6, 2, d))
+    s = _rand_signs(rng, 1, 2, d)
+    y = oracle.rotate(x, s, "srht")
+    H = scipy.linalg.hadamard(d).astype(np.float64) / np.sqrt(d)
+    ref = (x.astype(np.float64) * s[:, None]) @ H.T
+    assert np.max(np.abs(y - ref)) < 1e-13 * max(1.0, np.max(np.abs(ref)))
+
+
+def test_srht_d2_explicit():
+    x = np.array([3.0, 1.0], dtype=np.float16).reshape(1, 1, 1, 2)
+    y = oracle.rotate(x, None, "srht")[0, 0, 0]
+    assert np.allclose(y, [4.0 / np.sqrt(2), 2.0 / np.sqrt(2)], atol=1e-15)
+
+
+def test_none_is_sign_only():
+    rng = np.random.default_rng(5)
+    x = _rand_x(rng, (1, 4, 3, 32))
+    s = _rand_signs(rng, 1, 3, 32)
+    y = oracle.rotate(x, s, "none")
+    assert np.array_equal(y, x.astype(np.float64) * s[:, None])
+
+
+# --------------------------------------------------------------------------
+# Quantizer.
+# --------------------------------------------------------------------------
+
+def decode_codes(codes, bits, d):
+    """Independent decoder of the documented layout: int8 bytes, or two's
+    complement nibbles with the even coordinate in the low nibble."""
+    c = np.asarray(codes, dtype=np.uint8)
+    if bits == 8:
+        return c.view(np.int8).astype(np.int64)
+    lo = (c & 0xF).astype(np.int64)
+    hi = (c >> 4).astype(np.int64)
+    q = np.empty(c.shape[:-1] + (d,), dtype=np.int64)
+    q[..., 0::2] = lo
+    q[..., 1::2] = hi
+    return np.where(q >= 8, q - 16, q)
+
+
+def _groups(a, g):
+    return a.reshape(a.shape[:-1] + (a.shape[-1] // g, g))
+
+
+@pytest.mark.parametrize("rot", ["srft", "srht", "none"])
+@pytest.mark.parametrize("bits,group", [(4, 16), (4, 32), (8, 32), (4, 8), (8, 128)])
+def test_quantizer_invariants(rot, bits, group):
+    d = 128
+    qmax = 7 if bits == 4 else 127
+    rng = np.random.default_rng(bits * 100 + group)
+    x = _rand_x(rng, (2, 33, 2, d), scale=2.0)
+    x[..., 3] *= 20
+    s = _rand_signs(rng, 2, 2, d)
+    lam = rng.uniform(0.5, 2.0, size=(2, 2, d)).astype(np.float32)
+    codes, scales, z = oracle.quantize(x, s, lam, group, bits, rot, return_z=True)
+    q = decode_codes(codes, bits, d)
+    sig = scales.view(np.float16).astype(np.float64)
+    assert np.all(np.abs(q) <= qmax)
+    # z is the fp32 rounding of lambda * y (the decision input)
+    y = oracle.rotate(x, s, rot)
+    zref = (lam[:, None].astype(np.float64) * y).astype(np.float32)
+    assert np.array_equal(z, zref)
+    zg = _groups(z.astype(np.float64), group)
+    qg = _groups(q, group)
+    a = np.max(np.abs(zg), axis=-1)
+    # sigma within fp16 + fp32 rounding of a / qmax
+    rel = np.abs(sig - a / qmax) / (a / qmax)
+    assert np.all(rel <= 2.0 ** -11 + 2.0 ** -22)
+    # every group reaches the end of the code range
+    assert np.all(np.max(np.abs(qg), axis=-1) == qmax)
+    # nearest code: |z - q sigma| <= sigma / 2
+    err = np.abs(zg - qg * sig[..., None])
+    assert np.all(err <= sig[..., None] * (0.5 + 2.0 ** -20))
+    # brute force over every code value: oracle agrees except at exact ties
+    cand = np.arange(-qmax, qmax + 1, dtype=np.float64)
+    dist = np.abs(zg[..., None] - cand * sig[..., None, None])
+    best = cand[np.argmin(dist, axis=-1)]
+    dmin = np.min(dist, axis=-1)
+    dour = np.abs(zg - qg * sig[..., None])
+    mism = best != qg
+    assert np.all(np.isclose(dour[mism], dmin[mism], rtol=1e-6, atol=0))
+
+
+def test_quantizer_ties_round_half_even():
+    d, g = 16, 16
+    # rot none, lambda 1, s = +1: z = x exactly; absmax 7 gives sigma = 1
+    vals = np.array([7.0, 2.5, 3.5, -2.5, -3.5, 0.5, 1.5, 6.5, -0.5, -1.5, 4.5, 5.5, 0.0, 1.0, -7.0, -6.5])
+    x = vals.astype(np.float16).reshape(1, 1, 1, d)
+    codes, scales = oracle.quantize(x, None, None, g, 4, "none")
+    assert scales.view(np.float16)[0, 0, 0, 0] == 1.0
+    q = decode_codes(codes, 4, d)[0, 0, 0]
+    expect = [7, 2, 4, -2, -4, 0, 2, 6, 0, -2, 4, 6, 0, 1, -7, -6]
+    assert list(q) == expect
+
+
+def test_quantizer_zero_group_and_subnormal_clamp():
+    d, g = 32, 16
+    x = np.zeros((1, 1, 1, d), dtype=np.float16)
+    # group 1: absmax 7 * 1.4 * 2^-24 -> a/7 rounds to the smallest subnormal,
+    # so a / sigma = 9.8 and the code clamps to 7
+    x[..., 16] = np.float16(7 * 1.4 * 2.0 ** -24)
+    codes, scales = oracle.quantize(x, None, None, g, 4, "none")
+    sc = scales.view(np.float16)[0, 0, 0]
+    assert sc[0] == 0.0
+    q = decode_codes(codes, 4, d)[0, 0, 0]
+    assert np.all(q[:16] == 0)
+    xv = float(x[0, 0, 0, 16])
+    assert sc[1] == np.float16(2.0 ** -24)
+    assert xv / float(sc[1]) > 7.5 and q[16] == 7 and np.all(q[17:] == 0)
+
+
+def test_quantizer_overflowing_scale_clamps():
+    d, g = 16, 16
+    x = np.zeros((1, 1, 1, d), dtype=np.float16)
+    x[..., 0] = 60000.0
+    x[..., 1] = -30000.0
+    x[..., 2] = 1000.0
+    # a / qmax = 6e7 / 127 exceeds the largest half: sigma clamps to 65504
+    lam = np.full((1, 1, d), 1000.0, dtype=np.float32)
+    codes, scales = oracle.quantize(x, None, lam, g, 8, "none")
+    assert scales.view(np.float16)[0, 0, 0, 0] == np.float16(65504.0)
+    q = decode_codes(codes, 8, d)[0, 0, 0]
+    # 6e7/65504 and -3e7/65504 clamp; 1e6/65504 = 15.27 rounds to 15
+    assert q[0] == 127 and q[1] == -127 and q[2] == 15
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_dequantize_rot_none_closed_form(bits):
+    """rot none: x_hat = s * q * sigma / lambda, rounded once to fp16."""
+    d, g = 64, 16
+    rng = np.random.default_rng(bits)
+    x = _rand_x(rng, (1, 20, 3, d), scale=4.0)
+    s = _rand_signs(rng, 1, 3, d)
+    codes, scales = oracle.quantize(x, s, None, g, bits, "none")
+    out = oracle.dequantize(codes, scales, s, None, g, bits, "none", d=d)
+    q = decode_codes(codes, bits, d).astype(np.float64)
+    sig = np.repeat(scales.view(np.float16).astype(np.float64), g, axis=-1)
+    ref = (s[:, None] * q * sig).astype(np.float16).view(np.uint16)
+    assert np.array_equal(out, ref)
+
+
+@pytest.mark.parametrize("rot", ["srft", "srht"])
+def test_roundtrip_error_identity_and_bound(rot):
+    """Orthogonality: ||x_hat - x|| = ||y_hat - y|| before fp16 output rounding,
+    and the per-vector error is bounded by half a quantization step."""
+    d, g, bits = 128, 16, 4
+    rng = np.random.default_rng(17)
+    x = _rand_x(rng, (1, 40, 2, d))
+    s = _rand_signs(rng, 1, 2, d)
+    lam = rng.uniform(0.5, 2.0, size=(1, 2, d)).astype(np.float32)
+    codes, scales = oracle.quantize(x, s, lam, g, bits, rot)
+    _, x64 = oracle.dequantize(codes, scales, s, lam, g, bits, rot, d=d, return_f64=True)
+    q = decode_codes(codes, bits, d).astype(np.float64)
+    sig = np.repeat(scales.view(np.float16).astype(np.float64), g, axis=-1)
+    yhat = q * sig / lam[:, None]
+    y = oracle.rotate(x, s, rot)
+    e_x = np.linalg.norm(x64 - x.astype(np.float64), axis=-1)
+    e_y = np.linalg.norm(yhat - y, axis=-1)
+    assert np.allclose(e_x, e_y, rtol=1e-9, atol=1e-12)
+    bound = np.sqrt(np.sum((sig / (2 * lam[:, None])) ** 2, axis=-1))
+    assert np.all(e_x <= bound * (1 + 1e-5))
+
+
+def test_calibrated_lambda_gives_unit_rms():
+    d = 64
+    rng = np.random.default_rng(23)
+    x = _rand_x(rng, (2, 50, 2, d)) * np.float16(3.0)
+    x[0, :, 1, :] = 0                       # a silent head: lambda stays 1
+    s = _rand_signs(rng, 2, 2, d)
+    for rot in ("srft", "srht"):
+        lam = oracle.calibrate_lambda(x, s, rot)
+        y = oracle.rotate(x, s, rot)
+        rms = np.sqrt(np.mean((lam[:, None].astype(np.float64) * y) ** 2, axis=1))
+        live = np.ones((2, 2), dtype=bool)
+        live[0, 1] = False
+        assert np.allclose(rms[live], 1.0, rtol=1e-6)
+        assert np.all(lam[0, 1] == 1.0)
+
+
+def test_pages_quality_claims_on_synthetic_outliers():
+    """The pages' two qualitative claims, on outlier-channel data: per-group
+    scaling beats per-token scaling, and SRFT and SRHT are on a par."""
+    d = 128
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((1, 256, 4, d))
+    for h in range(4):
+        x[0, :, h, rng.choice(d, 4, replace=False)] *= 20
+    x = _f16(x)
+    s = _rand_signs(rng, 1, 4, d)
+
+    def err(rot, g):
+        c, sc = oracle.quantize(x, s, None, g, 4, rot)
+        xh = oracle.dequantize(c, sc, s, None, g, 4, rot, d=d).view(np.float16)
+        xf = x.astype(np.float64)
+        return np.linalg.norm(xh.astype(np.float64) - xf) / np.linalg.norm(xf)
+
+    e16, etok, enone = err("srft", 16), err("srft", d), err("none", d)
+    assert e16 < etok < enone
+    assert abs(err("srht", 16) - e16) / e16 < 0.1
+
+
+def test_byte_accounting_reproduces_pages_figures():
+    """The packed format (bits per code + one fp16 scale per group) reproduces
+    the compression figures the pages print: 3.56x and 41 GB -> 10.9 GB."""
+    import json
+    import os
+    gold = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                       "compression_figures.json")))
+    d = 128
+    x = np.ones((1, 4, 1, d), dtype=np.float16)
+
+    def ratio(g):
+        codes, scales = oracle.quantize(x, None, None, g, 4, "none")
+        return x.nbytes / (codes.nbytes + scales.nbytes)
+
+    assert round(ratio(32), 2) == gold["compression_upper"]
+    assert round(gold["llama3_70b_128k_fp16_GB"] / ratio(64), 1) == gold["llama3_70b_128k_int4_GB"]
