@@ -1,0 +1,202 @@
+"""Benchmark of the SRFT rotate-then-quantize hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload outlier]
+
+One step = the whole hot path over one batch of synthetic KV tensors:
+srftq_quantize (sign, SRFT, lambda, group absmax, int4 rounding and packing)
+then srftq_dequantize (unpack, inverse SRFT, sign, fp16) of every vector,
+one launch each.  The default workload is the 28-layer K+V outlier case:
+56 tensors of fp16 [T=32768, H=2, d=128], lambda calibrated per rotated
+coordinate, group 16, int4.
+
+Prints one JSON line: throughput in KV vectors per second (each vector
+quantized and dequantized), the per-kernel HBM roofline of the dominant
+kernel (algorithmic bytes / measured kernel time vs 8 TB/s), and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+KERNEL_SOURCES = ["dev_common.h", "xform.h", "quant.h", "kernels.h", "dispatch.inc"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "kv_cache_quantization_srft_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes_per_vector(d: int, group: int, bits: int) -> int:
+    """fp16 vector + packed codes + fp16 group scales (one direction)."""
+    return 2 * d + d * bits // 8 + 2 * (d // group)
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when missing or taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except OSError:
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, x, s, lam, target_s: float = 15.0):
+    """The oracle, as it stands, on the first tokens of every tensor."""
+    import numpy as np
+    from oracle import oracle
+
+    # pilot on a small slice to size the sample to ~target_s of CPU work
+    tp = 64
+    xs = np.ascontiguousarray(x[:, :tp])
+    t0 = time.perf_counter()
+    c, sc = oracle.quantize(xs, s, lam, w.group, w.bits, "srft")
+    oracle.dequantize(c, sc, s, lam, w.group, w.bits, "srft", d=w.d)
+    pilot = time.perf_counter() - t0
+    tn = int(min(w.T, max(tp, tp * target_s / max(pilot, 1e-6))))
+    xs = np.ascontiguousarray(x[:, :tn])
+    t0 = time.perf_counter()
+    c, sc = oracle.quantize(xs, s, lam, w.group, w.bits, "srft")
+    oracle.dequantize(c, sc, s, lam, w.group, w.bits, "srft", d=w.d)
+    dt = time.perf_counter() - t0
+    nv = w.B * tn * w.H
+    return {"value": nv / dt, "unit": "KV vectors/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"first {tn} tokens of each of the {w.B} tensors ({nv} vectors), "
+                      f"quantize + dequantize, fp64 direct DFT, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="outlier")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(every KV vector is independent; see the sharding notes in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from kv_cache_quantization_srft_amd import srftq as S
+    from kv_cache_quantization_srft_amd import workloads as W
+
+    w = W.WORKLOADS[args.workload]
+    t0 = time.perf_counter()
+    x, s = W.generate(w)
+    gen_s = time.perf_counter() - t0
+    dev = torch.device("cuda:0")
+    xd = torch.from_numpy(x).to(dev)
+    sd = torch.from_numpy(s).to(dev)
+    lam = S.calibrate_lambda(xd, sd) if w.calibrated_lambda else None
+    torch.cuda.synchronize()
+    lam_h = lam.cpu().numpy() if lam is not None else None
+
+    codes = torch.empty(x.shape[:-1] + (w.d * w.bits // 8,), dtype=torch.uint8, device=dev)
+    scales = torch.empty(x.shape[:-1] + (w.d // w.group,), dtype=torch.float16, device=dev)
+    xhat = torch.empty_like(xd)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        S.quantize(xd, sd, lam, w.group, w.bits, codes=codes, scales=scales)
+        if ev is not None:
+            ev[1].record()
+        S.dequantize(codes, scales, sd, lam, w.group, w.bits, out=xhat)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    q_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    dq_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    ms_step = total_ms / args.steps
+
+    nvec = w.nvec
+    bpv = algorithmic_bytes_per_vector(w.d, w.group, w.bits)
+    per_kernel = {
+        "quantize": {"ms": q_ms, "vectors_per_s": nvec / (q_ms * 1e-3),
+                     "fp16_GBps": 2 * w.d * nvec / (q_ms * 1e-3) / 1e9,
+                     "algo_GBps": bpv * nvec / (q_ms * 1e-3) / 1e9},
+        "dequantize": {"ms": dq_ms, "vectors_per_s": nvec / (dq_ms * 1e-3),
+                       "fp16_GBps": 2 * w.d * nvec / (dq_ms * 1e-3) / 1e9,
+                       "algo_GBps": bpv * nvec / (dq_ms * 1e-3) / 1e9},
+    }
+    for k in per_kernel.values():
+        k["hbm_frac"] = k["algo_GBps"] / HBM_PEAK_GBPS
+    dom = "quantize" if q_ms >= dq_ms else "dequantize"
+    traffic = load_traffic(dom, w.name)
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": per_kernel[dom]["algo_GBps"],
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": per_kernel[dom]["algo_GBps"] / HBM_PEAK_GBPS,
+                "traffic": traffic,
+                "bytes_per_vector": bpv, "vectors_per_launch": nvec}
+
+    # sanity: reconstruction error of the round trip
+    rel = (torch.linalg.vector_norm(xhat.float() - xd.float()) / torch.linalg.vector_norm(xd.float())).item()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, x, s, lam_h)
+
+    out = {
+        "metric": "KV vectors/s (quantize + dequantize), SRFT->int4 pack, d=128",
+        "value": nvec / (ms_step * 1e-3),
+        "unit": "KV vectors/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded numpy; stands in for LLM KV caches)",
+        "config": {"workload": f"{w.name}: {w.B} x fp16 [T={w.T}, H={w.H}, d={w.d}], "
+                               f"SRFT, lambda {'calibrated' if w.calibrated_lambda else '1'}, "
+                               f"group {w.group}, int{w.bits}",
+                   "B": w.B, "T": w.T, "H": w.H, "d": w.d, "group": w.group, "bits": w.bits,
+                   "rot": "srft", "parallelism": "none (1 GPU)"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "per_kernel": per_kernel,
+        "fp16_in_GBps_quantize": per_kernel["quantize"]["fp16_GBps"],
+        "reconstruction_rel_l2": rel,
+        "device": torch.cuda.get_device_name(0),
+        "input_generation_s": gen_s,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

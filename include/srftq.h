@@ -1,0 +1,165 @@
+/*
+ * srftq.h -- C ABI of libsrftq: fused sign-randomized Fourier (SRFT) or
+ * Walsh-Hadamard (SRHT) rotation + int4/int8 quantization of KV-cache
+ * vectors, and the inverse, on AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the one described in "When Quantization Is Free: an int4
+ * KV cache that outruns fp16 on Apple Silicon" (gist.science technical
+ * summary), section "Metodologia":
+ *   1. SRFT(x) = pack(F diag(s) x): F the unitary DFT, s a fixed random +-1
+ *      vector; the Hadamard variant (SRHT) replaces F by the normalized
+ *      Walsh-Hadamard matrix (also the per-tile RHT = H D x of the HyperQuant
+ *      summary, "Metodologia" 1).
+ *   2. The fused pipeline: sign multiply; FFT; Hermitian unpack to reals;
+ *      per-channel lambda rescale, per-group absmax and rounding to signed
+ *      int4/int8; two int4 per byte.
+ *   3. Per-channel + per-group scaling (groups of 16 in the pages).
+ *
+ * Conventions fixed by this library (the pages are silent on them):
+ *   - F uses e^{-2 pi i jk/d} and 1/sqrt(d).  The d/2+1 Hermitian bins are
+ *     packed into d orthonormal reals
+ *       y = [Re X_0, sqrt2 Re X_1 .. sqrt2 Re X_{N-1}, Re X_N,
+ *            sqrt2 Im X_1 .. sqrt2 Im X_{N-1}],  N = d/2.
+ *     SRHT: y = H_d (s . x) / sqrt(d), H_d in Sylvester (natural) order.
+ *   - z_j = lambda_j * y_j.  Per group G of `group` consecutive coordinates:
+ *       a = max |z_j|, sigma = fp16_rne(min(a * fp32(1/qmax), 65504)),
+ *       q_j = 0 if sigma == 0 else clamp(rne(z_j / sigma), -qmax, qmax),
+ *     qmax = 7 (bits 4) or 127 (bits 8); the decision is taken in fp32 and
+ *     against the stored fp16 sigma.
+ *   - int4 codes: two's-complement nibbles, coordinate 2i in the low nibble
+ *     of byte i.  int8 codes: one two's-complement byte per coordinate.
+ *   - Dequantize: yhat_j = q_j * sigma_G / lambda_j, x = s . (M^T yhat),
+ *     stored as fp16 round-to-nearest-even.
+ *
+ * Memory layout (row-major, contiguous, element = fp16 / int8 / byte):
+ *   x, x_out   fp16   [B, T, H, d]        (B tensors, e.g. layers x {K,V})
+ *   signs      int8   [B, H, d]  values +1 / -1   (NULL: all +1)
+ *   lambda     fp32   [B, H, d]  finite, > 0      (NULL: all 1)
+ *   codes      uint8  [B, T, H, d*bits/8]
+ *   scales     fp16   [B, T, H, d/group]
+ *   y          fp32   [B, T, H, d]   (rotate / unrotate only)
+ *
+ * Ownership and threading: every buffer belongs to the caller; the library
+ * allocates nothing on the device, keeps no per-call state and may be called
+ * from several host threads.  All data pointers are device pointers
+ * (hipMalloc'ed or torch CUDA tensors).  `stream` is a hipStream_t passed as
+ * void* (NULL = the default stream); calls are asynchronous on it.
+ *
+ * Errors: argument errors (NULL pointer, bad shape, unsupported
+ * combination, misalignment) are returned before anything is launched and
+ * leave every buffer untouched.  SRFTQ_ERR_HIP reports a failed launch or a
+ * missing device; faults inside a kernel surface at the caller's next
+ * synchronization.  lambda > 0 and finite inputs are preconditions that are
+ * not checked on the device.
+ */
+#ifndef SRFTQ_H
+#define SRFTQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SRFTQ_OK = 0,
+    SRFTQ_ERR_NULL = 1,        /* a required pointer is NULL */
+    SRFTQ_ERR_SHAPE = 2,       /* negative or inconsistent sizes */
+    SRFTQ_ERR_UNSUPPORTED = 3, /* (rot, d, group, bits) combination not built */
+    SRFTQ_ERR_ALIGN = 4,       /* a data pointer is not 16-byte aligned */
+    SRFTQ_ERR_HIP = 5          /* HIP runtime error (launch failure, no device) */
+} srftq_status;
+
+typedef enum {
+    SRFTQ_ROT_SRFT = 0, /* sign-randomized unitary DFT, packed to d reals */
+    SRFTQ_ROT_SRHT = 1, /* sign-randomized Walsh-Hadamard (Sylvester order) */
+    SRFTQ_ROT_NONE = 2  /* sign multiply only: isolates the quantizer */
+} srftq_rot;
+
+/*
+ * Problem description.  Supported: d in {64, 128, 256}; bits in {4, 8};
+ * group a power of two with 8 <= group <= d; rot one of srftq_rot; B, T >= 0,
+ * H >= 1 (B*T*H == 0 is a no-op).  `variant` selects the SRFT kernel
+ * organisation: 0 = default (fastest), 1 = real-input radix-2 transform,
+ * 2 = complex pairing + d/2-point complex FFT + Hermitian unpack; it is
+ * ignored for SRHT and NONE.  Every variant computes the same result.
+ */
+typedef struct {
+    int64_t B;
+    int64_t T;
+    int32_t H;
+    int32_t d;
+    int32_t group;
+    int32_t bits;
+    int32_t rot;
+    int32_t variant;
+} srftq_shape;
+
+/* Host-only check of a shape (no device needed). */
+srftq_status srftq_validate(const srftq_shape* shape);
+
+/* Bytes of the codes tensor: B*T*H*d*bits/8.  0 for an invalid shape. */
+size_t srftq_codes_bytes(const srftq_shape* shape);
+
+/* Number of fp16 scales: B*T*H*d/group.  0 for an invalid shape. */
+size_t srftq_scales_count(const srftq_shape* shape);
+
+/*
+ * Rotate-then-quantize (pipeline steps 1-5 above).
+ *   x       in   fp16 [B,T,H,d], 16-B aligned
+ *   signs   in   int8 [B,H,d] or NULL
+ *   lambda  in   fp32 [B,H,d] or NULL
+ *   codes   out  uint8 [B,T,H,d*bits/8], 16-B aligned
+ *   scales  out  fp16 [B,T,H,d/group], 16-B aligned
+ */
+srftq_status srftq_quantize(const srftq_shape* shape, const uint16_t* x,
+                            const int8_t* signs, const float* lambda,
+                            uint8_t* codes, uint16_t* scales, void* stream);
+
+/*
+ * Dequantize + unrotate (the inverse read path, "rotation and de-rotation"
+ * in the pages' problem statement).
+ *   codes, scales  in   as written by srftq_quantize (16-B aligned)
+ *   signs, lambda  in   the same ones used to quantize (or NULL)
+ *   x_out          out  fp16 [B,T,H,d], 16-B aligned
+ */
+srftq_status srftq_dequantize(const srftq_shape* shape, const uint8_t* codes,
+                              const uint16_t* scales, const int8_t* signs,
+                              const float* lambda, uint16_t* x_out, void* stream);
+
+/*
+ * The rotation alone (steps 1-3): y = M (s . x) in fp32, no lambda.
+ *   x  in  fp16 [B,T,H,d];  y  out  fp32 [B,T,H,d]; both 16-B aligned.
+ */
+srftq_status srftq_rotate(const srftq_shape* shape, const uint16_t* x,
+                          const int8_t* signs, float* y, void* stream);
+
+/*
+ * The inverse rotation alone: x_out = fp16_rne(s . (M^T y)).
+ *   y  in  fp32 [B,T,H,d];  x_out  out  fp16 [B,T,H,d]; both 16-B aligned.
+ */
+srftq_status srftq_unrotate(const srftq_shape* shape, const float* y,
+                            const int8_t* signs, uint16_t* x_out, void* stream);
+
+/*
+ * Per-channel lambda calibration (the pages' "learned or calibrated" lambda,
+ * read as the inverse RMS over tokens of each rotated coordinate):
+ *   lambda[b,h,j] = 1 / sqrt(mean_t y[b,t,h,j]^2), or 1 where that is 0.
+ *   x  in  fp16 [B,T,H,d];  lambda  out  fp32 [B,H,d] (also used as the
+ *   accumulator, so it must not alias x).  `group`, `bits` are ignored.
+ */
+srftq_status srftq_calibrate_lambda(const srftq_shape* shape, const uint16_t* x,
+                                    const int8_t* signs, float* lambda, void* stream);
+
+/* Static description of a status code. */
+const char* srftq_status_string(srftq_status status);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int srftq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SRFTQ_H */

@@ -1,0 +1,222 @@
+// api.cpp -- the C ABI of libsrftq (include/srftq.h): argument validation on
+// the host, then dispatch to the per-head-size kernel translation units.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <unordered_map>
+
+#include "launch.h"
+#include "srftq.h"
+
+namespace srftq {
+
+int device_cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
+  if (cache[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 1;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+const int8_t* plus_ones_ptr();   // defined with the device array in ones.hip
+
+int blocks_per_cu(const void* kernel, int block) {
+  static std::mutex mu;
+  static std::unordered_map<const void*, int> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(kernel);
+  if (it != cache.end()) return it->second;
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, block, 0) != hipSuccess || nb <= 0) nb = 1;
+  cache.emplace(kernel, nb);
+  return nb;
+}
+
+}  // namespace srftq
+
+namespace {
+
+bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+srftq_status validate(const srftq_shape* s) {
+  if (!s) return SRFTQ_ERR_NULL;
+  if (s->B < 0 || s->T < 0 || s->H < 1) return SRFTQ_ERR_SHAPE;
+  if (s->d != 64 && s->d != 128) return SRFTQ_ERR_UNSUPPORTED;
+  if (s->bits != 4 && s->bits != 8) return SRFTQ_ERR_UNSUPPORTED;
+  if (!is_pow2(s->group) || s->group < 8 || s->group > s->d) return SRFTQ_ERR_UNSUPPORTED;
+  if (s->rot != SRFTQ_ROT_SRFT && s->rot != SRFTQ_ROT_SRHT && s->rot != SRFTQ_ROT_NONE)
+    return SRFTQ_ERR_UNSUPPORTED;
+  if (s->variant < 0 || s->variant > 2) return SRFTQ_ERR_UNSUPPORTED;
+  // 32-bit tile counters and per-lane byte offsets
+  if (s->H > 65535) return SRFTQ_ERR_SHAPE;
+  const int64_t tiles_t = (s->T + 63) / 64;
+  if (s->B > 0 && tiles_t > 0 && (s->B * (int64_t)s->H) > (int64_t)0x7fffffff / tiles_t) return SRFTQ_ERR_SHAPE;
+  if (s->B > 0 && s->T > (int64_t)0x7fffffffffffLL / (s->B * (int64_t)s->H * s->d)) return SRFTQ_ERR_SHAPE;
+  return SRFTQ_OK;
+}
+
+int64_t nvec(const srftq_shape* s) { return s->B * s->T * (int64_t)s->H; }
+
+srftq_status from_hip(hipError_t e) { return e == hipSuccess ? SRFTQ_OK : SRFTQ_ERR_HIP; }
+
+const srftq::RunFn kQuantize[2][4] = {
+    {srftq::run_quantize_d64_r0, srftq::run_quantize_d64_r1, srftq::run_quantize_d64_r2,
+     srftq::run_quantize_d64_r3},
+    {srftq::run_quantize_d128_r0, srftq::run_quantize_d128_r1, srftq::run_quantize_d128_r2,
+     srftq::run_quantize_d128_r3}};
+const srftq::RunFn kDequantize[2][4] = {
+    {srftq::run_dequantize_d64_r0, srftq::run_dequantize_d64_r1, srftq::run_dequantize_d64_r2,
+     srftq::run_dequantize_d64_r3},
+    {srftq::run_dequantize_d128_r0, srftq::run_dequantize_d128_r1, srftq::run_dequantize_d128_r2,
+     srftq::run_dequantize_d128_r3}};
+
+srftq::RunFn pick(const srftq::RunFn (&table)[2][4], const srftq_shape* s) {
+  const int di = s->d == 64 ? 0 : s->d == 128 ? 1 : -1;
+  if (di < 0) return nullptr;
+  return table[di][srftq::rot_selector(*s)];
+}
+
+srftq_status check_side(const int8_t* signs, const float* lambda) {
+  if (signs && !aligned4(signs)) return SRFTQ_ERR_ALIGN;
+  if (lambda && !aligned4(lambda)) return SRFTQ_ERR_ALIGN;
+  return SRFTQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+srftq_status srftq_validate(const srftq_shape* shape) { return validate(shape); }
+
+size_t srftq_codes_bytes(const srftq_shape* s) {
+  if (validate(s) != SRFTQ_OK) return 0;
+  return (size_t)nvec(s) * (size_t)s->d * (size_t)s->bits / 8;
+}
+
+size_t srftq_scales_count(const srftq_shape* s) {
+  if (validate(s) != SRFTQ_OK) return 0;
+  return (size_t)nvec(s) * (size_t)(s->d / s->group);
+}
+
+srftq_status srftq_quantize(const srftq_shape* s, const uint16_t* x, const int8_t* signs,
+                            const float* lambda, uint8_t* codes, uint16_t* scales, void* stream) {
+  srftq_status st = validate(s);
+  if (st != SRFTQ_OK) return st;
+  if (nvec(s) == 0) return SRFTQ_OK;
+  if (!x || !codes || !scales) return SRFTQ_ERR_NULL;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return SRFTQ_ERR_ALIGN;
+  if ((st = check_side(signs, lambda)) != SRFTQ_OK) return st;
+  srftq::Ptrs p = {};
+  p.x = x;
+  p.signs = signs ? signs : srftq::plus_ones_ptr();
+  p.signs_shared = (signs == nullptr);
+  if (!p.signs) return SRFTQ_ERR_HIP;
+  p.lambda = lambda;
+  p.codes_out = codes;
+  p.scales_out = scales;
+  const srftq::RunFn fn = pick(kQuantize, s);
+  return fn ? from_hip(fn(*s, p, (hipStream_t)stream)) : SRFTQ_ERR_UNSUPPORTED;
+}
+
+srftq_status srftq_dequantize(const srftq_shape* s, const uint8_t* codes, const uint16_t* scales,
+                              const int8_t* signs, const float* lambda, uint16_t* x_out, void* stream) {
+  srftq_status st = validate(s);
+  if (st != SRFTQ_OK) return st;
+  if (nvec(s) == 0) return SRFTQ_OK;
+  if (!codes || !scales || !x_out) return SRFTQ_ERR_NULL;
+  if (!aligned16(codes) || !aligned16(scales) || !aligned16(x_out)) return SRFTQ_ERR_ALIGN;
+  if ((st = check_side(signs, lambda)) != SRFTQ_OK) return st;
+  srftq::Ptrs p = {};
+  p.codes_in = codes;
+  p.scales_in = scales;
+  p.signs = signs ? signs : srftq::plus_ones_ptr();
+  p.signs_shared = (signs == nullptr);
+  if (!p.signs) return SRFTQ_ERR_HIP;
+  p.lambda = lambda;
+  p.x_out = x_out;
+  const srftq::RunFn fn = pick(kDequantize, s);
+  return fn ? from_hip(fn(*s, p, (hipStream_t)stream)) : SRFTQ_ERR_UNSUPPORTED;
+}
+
+static srftq_status run_misc(srftq::Op op, const srftq_shape* s, const srftq::Ptrs& p, void* stream) {
+  hipStream_t hs = (hipStream_t)stream;
+  switch (s->d) {
+    case 64: return from_hip(srftq::run_misc_d64(op, *s, p, hs));
+    case 128: return from_hip(srftq::run_misc_d128(op, *s, p, hs));
+    default: return SRFTQ_ERR_UNSUPPORTED;
+  }
+}
+
+srftq_status srftq_rotate(const srftq_shape* s, const uint16_t* x, const int8_t* signs, float* y,
+                          void* stream) {
+  srftq_status st = validate(s);
+  if (st != SRFTQ_OK) return st;
+  if (nvec(s) == 0) return SRFTQ_OK;
+  if (!x || !y) return SRFTQ_ERR_NULL;
+  if (!aligned16(x) || !aligned16(y)) return SRFTQ_ERR_ALIGN;
+  if ((st = check_side(signs, nullptr)) != SRFTQ_OK) return st;
+  srftq::Ptrs p = {};
+  p.x = x;
+  p.signs = signs ? signs : srftq::plus_ones_ptr();
+  p.signs_shared = (signs == nullptr);
+  if (!p.signs) return SRFTQ_ERR_HIP;
+  p.y_out = y;
+  return run_misc(srftq::Op::Rotate, s, p, stream);
+}
+
+srftq_status srftq_unrotate(const srftq_shape* s, const float* y, const int8_t* signs, uint16_t* x_out,
+                            void* stream) {
+  srftq_status st = validate(s);
+  if (st != SRFTQ_OK) return st;
+  if (nvec(s) == 0) return SRFTQ_OK;
+  if (!y || !x_out) return SRFTQ_ERR_NULL;
+  if (!aligned16(y) || !aligned16(x_out)) return SRFTQ_ERR_ALIGN;
+  if ((st = check_side(signs, nullptr)) != SRFTQ_OK) return st;
+  srftq::Ptrs p = {};
+  p.y_in = y;
+  p.signs = signs ? signs : srftq::plus_ones_ptr();
+  p.signs_shared = (signs == nullptr);
+  if (!p.signs) return SRFTQ_ERR_HIP;
+  p.x_out = x_out;
+  return run_misc(srftq::Op::Unrotate, s, p, stream);
+}
+
+srftq_status srftq_calibrate_lambda(const srftq_shape* s, const uint16_t* x, const int8_t* signs,
+                                    float* lambda, void* stream) {
+  srftq_status st = validate(s);
+  if (st != SRFTQ_OK) return st;
+  if (s->B * (int64_t)s->H == 0) return SRFTQ_OK;
+  if (!lambda || (s->T > 0 && !x)) return SRFTQ_ERR_NULL;
+  if ((x && !aligned16(x)) || !aligned4(lambda)) return SRFTQ_ERR_ALIGN;
+  if ((st = check_side(signs, nullptr)) != SRFTQ_OK) return st;
+  srftq::Ptrs p = {};
+  p.x = x;
+  p.signs = signs ? signs : srftq::plus_ones_ptr();
+  p.signs_shared = (signs == nullptr);
+  if (!p.signs) return SRFTQ_ERR_HIP;
+  p.lambda_out = lambda;
+  return run_misc(srftq::Op::Calibrate, s, p, stream);
+}
+
+const char* srftq_status_string(srftq_status status) {
+  switch (status) {
+    case SRFTQ_OK: return "ok";
+    case SRFTQ_ERR_NULL: return "null pointer";
+    case SRFTQ_ERR_SHAPE: return "invalid shape";
+    case SRFTQ_ERR_UNSUPPORTED: return "unsupported (d, group, bits, rot, variant) combination";
+    case SRFTQ_ERR_ALIGN: return "misaligned pointer";
+    case SRFTQ_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int srftq_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,111 @@
+// dev_common.h -- gfx950 device helpers shared by the libsrftq kernels.
+//
+// Compile-time twiddles, fp16 half extraction, LDS direct loads
+// (global_load_lds_dwordx4, gfx950), wait counters and a static loop.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+#include <utility>
+
+namespace srftq {
+
+// ----------------------------------------------------------------------------
+// Compile-time trigonometry (Taylor series in double; |x| <= pi).
+// ----------------------------------------------------------------------------
+constexpr double kPi = 3.14159265358979323846264338327950288;
+
+constexpr double csin(double x) {
+  double term = x, sum = x;
+  for (int n = 1; n < 32; ++n) {
+    term *= -x * x / double((2 * n) * (2 * n + 1));
+    sum += term;
+  }
+  return sum;
+}
+
+constexpr double ccos(double x) {
+  double term = 1.0, sum = 1.0;
+  for (int n = 1; n < 32; ++n) {
+    term *= -x * x / double((2 * n - 1) * (2 * n));
+    sum += term;
+  }
+  return sum;
+}
+
+constexpr double csqrt(double x) {
+  double r = x > 1.0 ? x : 1.0;
+  for (int i = 0; i < 64; ++i) r = 0.5 * (r + x / r);
+  return r;
+}
+
+// ----------------------------------------------------------------------------
+// Static loop: f(std::integral_constant<int, I>) for I in [0, N).
+// ----------------------------------------------------------------------------
+template <class F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (N > 0) static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// ----------------------------------------------------------------------------
+// fp16 halves of a dword as fp32 (folds into v_fma_mix_f32 / SDWA cvt).
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ float hlo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+__device__ __forceinline__ float hhi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed fp16 pair, round to nearest even (v_cvt_pk_f16_f32).
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  float2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, half2_t));
+}
+
+__device__ __forceinline__ uint32_t as_u32(float f) { return __builtin_bit_cast(uint32_t, f); }
+__device__ __forceinline__ float as_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
+
+// ----------------------------------------------------------------------------
+// Wait counters (gfx9 s_waitcnt encoding: vmcnt[3:0] | expcnt[6:4] |
+// lgkmcnt[11:8] | vmcnt_hi[15:14]).
+// ----------------------------------------------------------------------------
+template <int VM>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 0xf) | (0x7 << 4) | (0xf << 8) | ((VM >> 4) << 14));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(0xf | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// One 16-byte-per-lane direct load into LDS: lane l's 16 bytes land at
+// lds_base + 16*l (lds_base must be wave-uniform).
+__device__ __forceinline__ void lds_dma16(const void* gptr, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(gptr, (lds_void_t*)lds_base, 16, 0, 0);
+}
+
+// Read-only data addressed through the constant address space: loads with a
+// wave-uniform address become scalar (s_load) loads even across barriers.
+template <class T>
+using const_ptr = const __attribute__((address_space(4))) T*;
+template <class T>
+__device__ __forceinline__ const_ptr<T> as_const(const T* p) {
+  return (const_ptr<T>)(p);
+}
+
+// Uniform value -> scalar register.
+__device__ __forceinline__ int uniform_i32(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+}  // namespace srftq

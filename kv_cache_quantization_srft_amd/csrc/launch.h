@@ -1,0 +1,78 @@
+// launch.h -- host-side dispatch from a runtime srftq_shape to the compiled
+// kernel instance, and persistent-grid sizing.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "srftq.h"
+
+namespace srftq {
+
+enum class Op : int { Quantize = 0, Dequantize = 1, Rotate = 2, Unrotate = 3, Calibrate = 4 };
+
+struct Ptrs {
+  const void* x;         // quantize / rotate / calibrate input (fp16)
+  const float* y_in;     // unrotate input (fp32)
+  const uint8_t* codes_in;
+  const uint16_t* scales_in;
+  const int8_t* signs;   // never null: a shared +1 row when the caller passes none
+  bool signs_shared;     // true: one row for every head (stride 0)
+  const float* lambda;
+  uint8_t* codes_out;
+  uint16_t* scales_out;
+  uint16_t* x_out;
+  float* y_out;
+  float* lambda_out;
+};
+
+// Per-d entry points (one translation unit per d, direction and rotation
+// selector r: 0 = SRFT real-input, 1 = SRFT paired, 2 = SRHT, 3 = none).
+using RunFn = hipError_t (*)(const srftq_shape&, const Ptrs&, hipStream_t);
+#define SRFTQ_DECL_RUN(d)                                                         \
+  hipError_t run_quantize_d##d##_r0(const srftq_shape&, const Ptrs&, hipStream_t);   \
+  hipError_t run_quantize_d##d##_r1(const srftq_shape&, const Ptrs&, hipStream_t);   \
+  hipError_t run_quantize_d##d##_r2(const srftq_shape&, const Ptrs&, hipStream_t);   \
+  hipError_t run_quantize_d##d##_r3(const srftq_shape&, const Ptrs&, hipStream_t);   \
+  hipError_t run_dequantize_d##d##_r0(const srftq_shape&, const Ptrs&, hipStream_t); \
+  hipError_t run_dequantize_d##d##_r1(const srftq_shape&, const Ptrs&, hipStream_t); \
+  hipError_t run_dequantize_d##d##_r2(const srftq_shape&, const Ptrs&, hipStream_t); \
+  hipError_t run_dequantize_d##d##_r3(const srftq_shape&, const Ptrs&, hipStream_t); \
+  hipError_t run_misc_d##d(Op op, const srftq_shape&, const Ptrs&, hipStream_t);
+SRFTQ_DECL_RUN(64)
+SRFTQ_DECL_RUN(128)
+#undef SRFTQ_DECL_RUN
+
+inline int rot_selector(const srftq_shape& s) {
+  if (s.rot == SRFTQ_ROT_SRFT) return s.variant == 2 ? 1 : 0;
+  return s.rot == SRFTQ_ROT_SRHT ? 2 : 3;
+}
+
+// Number of compute units of the current device (cached per device).
+int device_cu_count();
+
+// Resident blocks per CU of a kernel at a block size (cached per kernel).
+int blocks_per_cu(const void* kernel, int block);
+
+// Persistent grid: at most (resident blocks per CU) x CUs, at least 1.
+inline int persistent_grid(const void* kernel, int n_tiles, int block) {
+  long g = (long)blocks_per_cu(kernel, block) * (long)device_cu_count();
+  if (g > n_tiles) g = n_tiles;
+  return g < 1 ? 1 : (int)g;
+}
+
+// Launch sizes derived from a validated shape.
+struct GeoH {
+  int64_t T;
+  int32_t H, BH, tiles_t, n_tiles;
+};
+inline GeoH make_geo(const srftq_shape& s) {
+  GeoH g;
+  g.T = s.T;
+  g.H = s.H;
+  g.BH = (int32_t)(s.B * s.H);
+  g.tiles_t = (int32_t)((s.T + 63) / 64);
+  g.n_tiles = g.tiles_t * g.BH;
+  return g;
+}
+
+}  // namespace srftq

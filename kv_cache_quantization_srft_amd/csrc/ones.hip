@@ -1,0 +1,31 @@
+// ones.hip -- a device-resident row of +1 signs, used when the caller passes
+// no sign vector (signs == NULL means s = +1), so kernels always read signs
+// through one scalar-loaded pointer.  Static device memory: nothing is
+// allocated at run time.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace srftq {
+
+__device__ int8_t g_plus_ones[256] = {
+#define SRFTQ_ONE8 1, 1, 1, 1, 1, 1, 1, 1
+#define SRFTQ_ONE64 SRFTQ_ONE8, SRFTQ_ONE8, SRFTQ_ONE8, SRFTQ_ONE8, SRFTQ_ONE8, SRFTQ_ONE8, SRFTQ_ONE8, SRFTQ_ONE8
+    SRFTQ_ONE64, SRFTQ_ONE64, SRFTQ_ONE64, SRFTQ_ONE64
+#undef SRFTQ_ONE64
+#undef SRFTQ_ONE8
+};
+
+// Address of g_plus_ones on the current device (cached per device).
+const int8_t* plus_ones_ptr() {
+  static void* cache[64] = {nullptr};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  if (!cache[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_plus_ones)) != hipSuccess) return nullptr;
+    cache[dev] = p;
+  }
+  return (const int8_t*)cache[dev];
+}
+
+}  // namespace srftq

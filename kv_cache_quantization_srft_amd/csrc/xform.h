@@ -1,0 +1,414 @@
+// xform.h -- register-resident rotations of one KV vector per lane.
+//
+// The rotation is SRFT(x) = pack(F diag(s) x) ("When Quantization Is Free",
+// gist.science summary, "Metodologia" 1; fused pipeline steps 1-3 in
+// "Metodologia" 2), or the normalized Walsh-Hadamard transform for the SRHT
+// variant.  Every lane owns one whole d-vector, so all butterflies are
+// in-register with compile-time indices and compile-time twiddles: no
+// cross-lane traffic and no twiddle loads.
+//
+// Two SRFT organisations compute the same orthonormal map:
+//   VAR_REAL   real-input radix-2 decimation in time.  Its first log2(d/2)
+//              passes compute the d/2-point DFTs of the even and odd samples
+//              (the real and imaginary parts of the paired sequence
+//              z_m = x_2m + i x_2m+1); its last pass is the Hermitian unpack
+//              X_k = E_k + W_d^k O_k.  Each pass keeps only the
+//              non-redundant half of every Hermitian sub-spectrum, which
+//              saves a quarter of the arithmetic of VAR_PAIRED.
+//   VAR_PAIRED the pages' organisation: pair z_m = x_2m + i x_2m+1, run a
+//              d/2-point complex radix-2 FFT, unpack the Hermitian symmetry.
+//
+// Spectra are held "halfcomplex": for a real sequence of length L,
+// h[k] = Re X_k (0 <= k <= L/2) and h[L-k] = Im X_k (0 < k < L/2).
+// The packed output order is y = [h[0..N], h[d-1], h[d-2], ..., h[N+1]], i.e.
+// [Re X_0..Re X_N, Im X_1..Im X_{N-1}] with N = d/2, before the per-coordinate
+// scale (1/sqrt(d) for X_0, X_N and sqrt(2/d) for the rest).
+#pragma once
+
+#include "dev_common.h"
+
+namespace srftq {
+
+enum : int { ROT_SRFT = 0, ROT_SRHT = 1, ROT_NONE = 2 };
+enum : int { VAR_REAL = 1, VAR_PAIRED = 2 };
+
+// Per-coordinate scale of the unscaled transform outputs (forward) and of
+// the inputs of the unscaled inverse.  Coordinates 0 and d/2 of the SRFT
+// ("edges") carry a different scale from the rest ("bulk").
+template <int D, int ROT, int VAR>
+struct Scales {
+  static constexpr bool kEdges = (ROT == ROT_SRFT);
+  static constexpr double kFwdBulk = ROT == ROT_NONE ? 1.0
+                                   : ROT == ROT_SRHT ? 1.0 / csqrt(D)
+                                   : VAR == VAR_REAL ? csqrt(2.0 / D)
+                                                     : 1.0 / csqrt(2.0 * D);
+  static constexpr double kFwdEdge = ROT == ROT_SRFT ? 1.0 / csqrt(D) : kFwdBulk;
+  static constexpr double kInvBulk = ROT == ROT_NONE ? 1.0
+                                   : ROT == ROT_SRHT ? 1.0 / csqrt(D)
+                                                     : 1.0 / csqrt(2.0 * D);
+  static constexpr double kInvEdge = ROT == ROT_SRFT ? 1.0 / csqrt(D) : kInvBulk;
+  static constexpr bool is_edge(int j) { return kEdges && (j == 0 || j == D / 2); }
+};
+
+// Signs of one head: int8 +-1, read as 4-byte words through scalar loads
+// (the row pointer is wave-uniform and 4-byte aligned).
+struct HeadSigns {
+  const_ptr<uint32_t> p;
+  __device__ __forceinline__ explicit HeadSigns(const int8_t* row)
+      : p(as_const((const uint32_t*)row)) {}
+  // bit 7 of sign byte j
+  __device__ __forceinline__ uint32_t sbit(int j) const { return (p[j >> 2] >> (8 * (j & 3) + 7)) & 1u; }
+  // XOR mask flipping the fp16 sign bits of elements 2m, 2m+1.
+  __device__ __forceinline__ uint32_t mask(int m) const {
+    uint32_t v = (sbit(2 * m) << 15) | (sbit(2 * m + 1) << 31);
+    asm("" : "+s"(v));   // keep the mask whole in an SGPR: one v_xor per use
+    return v;
+  }
+  // +-1.0f for element j.
+  __device__ __forceinline__ float f(int j) const { return as_f32(0x3f800000u | (sbit(j) << 31)); }
+};
+
+// ----------------------------------------------------------------------------
+// Pass 1 from fp16: s (.) x, converted, and the pair sums of elements r and
+// r + d/2:  p0[r] = x'_r + x'_{r+d/2},  p1[r] = x'_r - x'_{r+d/2}.
+// Every rotation starts with exactly these (radix-2 split on the top index
+// bit); each is one v_fma_mix_f32 from the packed halves.
+// ----------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ void pair_sums(const uint32_t (&w)[D / 2], const HeadSigns& sg,
+                                          float (&p0)[D / 2], float (&p1)[D / 2]) {
+  static_for<D / 4>([&](auto mm) {
+    constexpr int m = decltype(mm)::value;
+    const uint32_t wa = w[m] ^ sg.mask(m);       // elements 2m, 2m+1 (signed)
+    const uint32_t wb = w[D / 4 + m];            // elements d/2+2m, d/2+2m+1
+    const float s0 = sg.f(D / 2 + 2 * m), s1 = sg.f(D / 2 + 2 * m + 1);
+    p0[2 * m] = __builtin_fmaf(hlo(wb), s0, hlo(wa));
+    p1[2 * m] = __builtin_fmaf(hlo(wb), -s0, hlo(wa));
+    p0[2 * m + 1] = __builtin_fmaf(hhi(wb), s1, hhi(wa));
+    p1[2 * m + 1] = __builtin_fmaf(hhi(wb), -s1, hhi(wa));
+  });
+}
+
+// ----------------------------------------------------------------------------
+// VAR_REAL forward: halfcomplex combine of two length-L spectra E, O (of the
+// even / odd subsequences) into the length-2L spectrum:
+//   X_k = E_k + W^k O_k,  X_{L-k} = conj(E_k - W^k O_k),  W = e^{-i pi/L}.
+// Six FMAs per k (the second output reuses the first: 2E - (E + WO)).
+// ----------------------------------------------------------------------------
+template <int L>
+__device__ __forceinline__ void hc_combine(const float (&E)[L], const float (&O)[L], float (&X)[2 * L]) {
+  X[0] = E[0] + O[0];
+  X[L] = E[0] - O[0];
+  if constexpr (L >= 2) {
+    X[L / 2] = E[L / 2];
+    X[2 * L - L / 2] = -O[L / 2];
+  }
+  static_for<(L >= 4 ? L / 2 - 1 : 0)>([&](auto kk) {
+    constexpr int k = decltype(kk)::value + 1;
+    constexpr float c = (float)ccos(kPi * k / L);
+    constexpr float s = (float)csin(kPi * k / L);
+    const float Er = E[k], Ei = E[L - k], Or = O[k], Oi = O[L - k];
+    const float xr = __builtin_fmaf(s, Oi, __builtin_fmaf(c, Or, Er));
+    const float xi = __builtin_fmaf(-s, Or, __builtin_fmaf(c, Oi, Ei));
+    X[k] = xr;
+    X[2 * L - k] = xi;
+    X[L - k] = __builtin_fmaf(2.0f, Er, -xr);
+    X[L + k] = __builtin_fmaf(-2.0f, Ei, xi);
+  });
+}
+
+// Halfcomplex DFT of the subsequence x[OFF + m*S], m < L (L*S = D).
+template <int L, int S, int OFF, int D>
+__device__ __forceinline__ void rdft(const float (&p0)[D / 2], const float (&p1)[D / 2], float (&X)[L]) {
+  if constexpr (L == 2) {
+    X[0] = p0[OFF];
+    X[1] = p1[OFF];
+  } else {
+    float E[L / 2], O[L / 2];
+    rdft<L / 2, 2 * S, OFF, D>(p0, p1, E);
+    rdft<L / 2, 2 * S, OFF + S, D>(p0, p1, O);
+    hc_combine<L / 2>(E, O, X);
+  }
+}
+
+// ----------------------------------------------------------------------------
+// VAR_PAIRED forward: complex radix-2 DIT FFT of z_m = x'_2m + i x'_2m+1.
+// Butterfly X_k = E_k + W O_k, X_{k+L/2} = E_k - W O_k in six FMAs.
+// ----------------------------------------------------------------------------
+template <int L, int S, int OFF, int D, bool INV>
+__device__ __forceinline__ void cfft(const float (&p0)[D / 2], const float (&p1)[D / 2],
+                                     float (&Xr)[L], float (&Xi)[L]);
+
+template <int L, bool INV>
+__device__ __forceinline__ void c_butterflies(const float (&Er)[L / 2], const float (&Ei)[L / 2],
+                                              const float (&Or)[L / 2], const float (&Oi)[L / 2],
+                                              float (&Xr)[L], float (&Xi)[L]) {
+  static_for<L / 2>([&](auto kk) {
+    constexpr int k = decltype(kk)::value;
+    if constexpr (k == 0) {
+      Xr[0] = Er[0] + Or[0];
+      Xi[0] = Ei[0] + Oi[0];
+      Xr[L / 2] = Er[0] - Or[0];
+      Xi[L / 2] = Ei[0] - Oi[0];
+    } else if constexpr (4 * k == L) {
+      // W = -i (forward) or +i (inverse)
+      const float wr = INV ? -Oi[k] : Oi[k];
+      const float wi = INV ? Or[k] : -Or[k];
+      Xr[k] = Er[k] + wr;
+      Xi[k] = Ei[k] + wi;
+      Xr[k + L / 2] = Er[k] - wr;
+      Xi[k + L / 2] = Ei[k] - wi;
+    } else {
+      constexpr float c = (float)ccos(2.0 * kPi * k / L);
+      constexpr float s = INV ? -(float)csin(2.0 * kPi * k / L) : (float)csin(2.0 * kPi * k / L);
+      // W = c - i s:  W O = (c Or + s Oi) + i (c Oi - s Or)
+      const float xr = __builtin_fmaf(s, Oi[k], __builtin_fmaf(c, Or[k], Er[k]));
+      const float xi = __builtin_fmaf(-s, Or[k], __builtin_fmaf(c, Oi[k], Ei[k]));
+      Xr[k] = xr;
+      Xi[k] = xi;
+      Xr[k + L / 2] = __builtin_fmaf(2.0f, Er[k], -xr);
+      Xi[k + L / 2] = __builtin_fmaf(2.0f, Ei[k], -xi);
+    }
+  });
+}
+
+template <int L, int S, int OFF, int D, bool INV>
+__device__ __forceinline__ void cfft(const float (&p0)[D / 2], const float (&p1)[D / 2],
+                                     float (&Xr)[L], float (&Xi)[L]) {
+  if constexpr (L == 2) {
+    Xr[0] = p0[2 * OFF];
+    Xi[0] = p0[2 * OFF + 1];
+    Xr[1] = p1[2 * OFF];
+    Xi[1] = p1[2 * OFF + 1];
+  } else {
+    float Er[L / 2], Ei[L / 2], Or[L / 2], Oi[L / 2];
+    cfft<L / 2, 2 * S, OFF, D, INV>(p0, p1, Er, Ei);
+    cfft<L / 2, 2 * S, OFF + S, D, INV>(p0, p1, Or, Oi);
+    c_butterflies<L, INV>(Er, Ei, Or, Oi, Xr, Xi);
+  }
+}
+
+// Hermitian unpack of Z (d/2-point spectrum of z) into the halfcomplex
+// spectrum of x, bins 1..N-1 doubled (their scale absorbs the 1/2):
+//   2E_k = Z_k + conj Z_{N-k},  2O_k = (Z_k - conj Z_{N-k}) / i,
+//   2X_k = 2E_k + W_d^k 2O_k,  2X_{N-k} = conj(2E_k - W_d^k 2O_k).
+template <int D>
+__device__ __forceinline__ void hermitian_unpack(const float (&Zr)[D / 2], const float (&Zi)[D / 2],
+                                                 float (&h)[D]) {
+  constexpr int N = D / 2;
+  h[0] = Zr[0] + Zi[0];
+  h[N] = Zr[0] - Zi[0];
+  h[N / 2] = 2.0f * Zr[N / 2];
+  h[D - N / 2] = -2.0f * Zi[N / 2];
+  static_for<N / 2 - 1>([&](auto kk) {
+    constexpr int k = decltype(kk)::value + 1;
+    constexpr float c = (float)ccos(2.0 * kPi * k / D);
+    constexpr float s = (float)csin(2.0 * kPi * k / D);
+    const float A = Zr[k] + Zr[N - k];
+    const float B = Zi[k] - Zi[N - k];
+    const float C = Zi[k] + Zi[N - k];
+    const float Dm = Zr[N - k] - Zr[k];
+    const float xr = __builtin_fmaf(s, Dm, __builtin_fmaf(c, C, A));
+    const float xi = __builtin_fmaf(-s, C, __builtin_fmaf(c, Dm, B));
+    h[k] = xr;
+    h[D - k] = xi;
+    h[N - k] = __builtin_fmaf(2.0f, A, -xr);
+    h[N + k] = __builtin_fmaf(-2.0f, B, xi);
+  });
+}
+
+// In-place natural-order Walsh-Hadamard transform of length M (unnormalized).
+template <int M>
+__device__ __forceinline__ void wht(float (&v)[M]) {
+  static_for<(M > 1 ? __builtin_ctz(M) : 0)>([&](auto ss) {
+    constexpr int h = 1 << decltype(ss)::value;
+    static_for<M / 2>([&](auto ii) {
+      constexpr int i = decltype(ii)::value;
+      constexpr int lo = (i / h) * 2 * h + (i % h);
+      const float a = v[lo], b = v[lo + h];
+      v[lo] = a + b;
+      v[lo + h] = a - b;
+    });
+  });
+}
+
+// ----------------------------------------------------------------------------
+// Forward rotation of one vector given as D/2 packed fp16 dwords.  Output y
+// is in packed order and unscaled (multiply by Scales<>::kFwd*).
+// ----------------------------------------------------------------------------
+template <int D, int ROT, int VAR>
+__device__ __forceinline__ void forward(const uint32_t (&w)[D / 2], const HeadSigns& sg, float (&y)[D]) {
+  if constexpr (ROT == ROT_NONE) {
+    static_for<D / 2>([&](auto mm) {
+      constexpr int m = decltype(mm)::value;
+      const uint32_t v = w[m] ^ sg.mask(m);
+      y[2 * m] = hlo(v);
+      y[2 * m + 1] = hhi(v);
+    });
+  } else {
+    float p0[D / 2], p1[D / 2];
+    pair_sums<D>(w, sg, p0, p1);
+    if constexpr (ROT == ROT_SRHT) {
+      wht<D / 2>(p0);
+      wht<D / 2>(p1);
+      static_for<D / 2>([&](auto kk) {
+        constexpr int k = decltype(kk)::value;
+        y[k] = p0[k];
+        y[D / 2 + k] = p1[k];
+      });
+    } else {
+      constexpr int N = D / 2;
+      float h[D];
+      if constexpr (VAR == VAR_PAIRED) {
+        float Zr[N], Zi[N];
+        cfft<N, 1, 0, D, false>(p0, p1, Zr, Zi);
+        hermitian_unpack<D>(Zr, Zi, h);
+      } else {
+        rdft<D, 1, 0, D>(p0, p1, h);
+      }
+      static_for<N + 1>([&](auto jj) {
+        constexpr int j = decltype(jj)::value;
+        y[j] = h[j];
+      });
+      static_for<N - 1>([&](auto kk) {
+        constexpr int k = decltype(kk)::value + 1;
+        y[N + k] = h[D - k];
+      });
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Inverse rotation.  Input: packed coordinates already multiplied by
+// Scales<>::kInv* (and by the dequantization scale).  Output: x' = M^T y,
+// natural order, before the sign multiply.
+// ----------------------------------------------------------------------------
+
+// Split a halfcomplex length-2M spectrum X (whose Nyquist entry X[M] carries a
+// pending factor NYQ) into the spectra of its even / odd samples:
+//   E_k = X_k + conj X_{M-k},  O_k = conj(W^k) (X_k - conj X_{M-k}),
+//   W = e^{-i pi/M}.
+// The Nyquist entries of E and O come out with pending factors 2 and -2.
+template <int M, int NYQ>
+__device__ __forceinline__ void hc_split(const float (&X)[2 * M], float (&E)[M], float (&O)[M]) {
+  constexpr float f = (float)NYQ;
+  E[0] = __builtin_fmaf(f, X[M], X[0]);
+  O[0] = __builtin_fmaf(-f, X[M], X[0]);
+  if constexpr (M >= 2) {
+    E[M / 2] = X[M / 2];
+    O[M / 2] = X[2 * M - M / 2];
+  }
+  static_for<(M >= 4 ? M / 2 - 1 : 0)>([&](auto kk) {
+    constexpr int k = decltype(kk)::value + 1;
+    constexpr float c = (float)ccos(kPi * k / M);
+    constexpr float s = (float)csin(kPi * k / M);
+    const float Pr = X[k], Pi = X[2 * M - k];
+    const float Qr = X[M - k], Qi = -X[M + k];
+    const float Er = Pr + Qr, Ei = Pi + Qi;
+    const float Dr = Pr - Qr, Di = Pi - Qi;
+    // conj(W) D = (c + i s)(Dr + i Di)
+    E[k] = Er;
+    E[M - k] = Ei;
+    O[k] = __builtin_fmaf(c, Dr, -s * Di);
+    O[M - k] = __builtin_fmaf(c, Di, s * Dr);
+  });
+}
+
+// Inverse of rdft: the subsequence x[OFF + m*S] from its halfcomplex spectrum.
+template <int L, int S, int OFF, int D, int NYQ>
+__device__ __forceinline__ void irdft(const float (&X)[L], float (&x)[D]) {
+  if constexpr (L == 2) {
+    constexpr float f = (float)NYQ;
+    x[OFF] = __builtin_fmaf(f, X[1], X[0]);
+    x[OFF + S] = __builtin_fmaf(-f, X[1], X[0]);
+  } else {
+    float E[L / 2], O[L / 2];
+    hc_split<L / 2, NYQ>(X, E, O);
+    irdft<L / 2, 2 * S, OFF, D, 2>(E, x);
+    irdft<L / 2, 2 * S, OFF + S, D, -2>(O, x);
+  }
+}
+
+// Inverse complex DIT FFT (e^{+}) of Z[OFF + k*S], natural-order output.
+template <int L, int S, int OFF, int NN>
+__device__ __forceinline__ void icfft(const float (&Zr)[NN], const float (&Zi)[NN], float (&zr)[L], float (&zi)[L]) {
+  if constexpr (L == 2) {
+    zr[0] = Zr[OFF] + Zr[OFF + S];
+    zi[0] = Zi[OFF] + Zi[OFF + S];
+    zr[1] = Zr[OFF] - Zr[OFF + S];
+    zi[1] = Zi[OFF] - Zi[OFF + S];
+  } else {
+    float Er[L / 2], Ei[L / 2], Or[L / 2], Oi[L / 2];
+    icfft<L / 2, 2 * S, OFF, NN>(Zr, Zi, Er, Ei);
+    icfft<L / 2, 2 * S, OFF + S, NN>(Zr, Zi, Or, Oi);
+    c_butterflies<L, true>(Er, Ei, Or, Oi, zr, zi);
+  }
+}
+
+template <int D, int ROT, int VAR>
+__device__ __forceinline__ void inverse(const float (&y)[D], float (&x)[D]) {
+  constexpr int N = D / 2;
+  if constexpr (ROT == ROT_NONE) {
+    static_for<D>([&](auto jj) {
+      constexpr int j = decltype(jj)::value;
+      x[j] = y[j];
+    });
+  } else if constexpr (ROT == ROT_SRHT) {
+    float u[N], v[N];
+    static_for<N>([&](auto kk) {
+      constexpr int k = decltype(kk)::value;
+      u[k] = y[k];
+      v[k] = y[N + k];
+    });
+    wht<N>(u);
+    wht<N>(v);
+    static_for<N>([&](auto rr) {
+      constexpr int r = decltype(rr)::value;
+      x[r] = u[r] + v[r];
+      x[r + N] = u[r] - v[r];
+    });
+  } else if constexpr (VAR == VAR_PAIRED) {
+    // Re-pair: Z_k = E_k + i O_k with 2E_k = X_k + conj X_{N-k},
+    // 2O_k = (X_k - conj X_{N-k}) conj(W_d^k); then z = IDFT_N(Z).
+    float Zr[N], Zi[N];
+    Zr[0] = y[0] + y[N];
+    Zi[0] = y[0] - y[N];
+    Zr[N / 2] = 2.0f * y[N / 2];
+    Zi[N / 2] = -2.0f * y[N + N / 2];
+    static_for<N / 2 - 1>([&](auto kk) {
+      constexpr int k = decltype(kk)::value + 1;
+      constexpr float c = (float)ccos(2.0 * kPi * k / D);
+      constexpr float s = (float)csin(2.0 * kPi * k / D);
+      const float Pr = y[k], Pi = y[N + k];           // X_k
+      const float Qr = y[N - k], Qi = -y[D - k];      // conj X_{N-k}
+      const float Er = Pr + Qr, Ei = Pi + Qi;
+      const float Dr = Pr - Qr, Di = Pi - Qi;
+      const float Or = __builtin_fmaf(c, Dr, -s * Di);
+      const float Oi = __builtin_fmaf(c, Di, s * Dr);
+      Zr[k] = Er - Oi;
+      Zi[k] = Ei + Or;
+      Zr[N - k] = Er + Oi;
+      Zi[N - k] = Or - Ei;
+    });
+    float zr[N], zi[N];
+    icfft<N, 1, 0, N>(Zr, Zi, zr, zi);
+    static_for<N>([&](auto mm) {
+      constexpr int m = decltype(mm)::value;
+      x[2 * m] = zr[m];
+      x[2 * m + 1] = zi[m];
+    });
+  } else {
+    float h[D];
+    static_for<N + 1>([&](auto jj) {
+      constexpr int j = decltype(jj)::value;
+      h[j] = y[j];
+    });
+    static_for<N - 1>([&](auto kk) {
+      constexpr int k = decltype(kk)::value + 1;
+      h[D - k] = y[N + k];
+    });
+    irdft<D, 1, 0, D, 1>(h, x);
+  }
+}
+
+}  // namespace srftq

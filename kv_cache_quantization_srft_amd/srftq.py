@@ -1,0 +1,248 @@
+"""Thin Python binding of libsrftq (include/srftq.h) over ctypes.
+
+Argument marshalling only: every step of the quantize / dequantize path runs
+in the library's HIP kernels.  Tensors are torch CUDA tensors (device memory
+and the current stream come from torch); there is no CPU fallback, and a
+missing library raises.
+
+The C functions keep their names here (``srftq_quantize`` ...) and take the
+same arguments, with a ``Shape`` in place of ``const srftq_shape*``.  The
+convenience wrappers ``quantize`` / ``dequantize`` / ``rotate`` /
+``unrotate`` / ``calibrate_lambda`` allocate outputs with torch.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsrftq.so")
+
+SRFTQ_OK, SRFTQ_ERR_NULL, SRFTQ_ERR_SHAPE, SRFTQ_ERR_UNSUPPORTED, SRFTQ_ERR_ALIGN, SRFTQ_ERR_HIP = range(6)
+ROT = {"srft": 0, "srht": 1, "none": 2}
+VARIANT = {"default": 0, "real": 1, "paired": 2}
+
+
+class SrftqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("H", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("group", ctypes.c_int32), ("bits", ctypes.c_int32),
+                ("rot", ctypes.c_int32), ("variant", ctypes.c_int32)]
+
+    def __repr__(self):
+        return (f"Shape(B={self.B}, T={self.T}, H={self.H}, d={self.d}, group={self.group}, "
+                f"bits={self.bits}, rot={self.rot}, variant={self.variant})")
+
+
+def make_shape(B, T, H, d, group=16, bits=4, rot="srft", variant="default") -> Shape:
+    r = ROT[rot] if isinstance(rot, str) else int(rot)
+    v = VARIANT[variant] if isinstance(variant, str) else int(variant)
+    return Shape(int(B), int(T), int(H), int(d), int(group), int(bits), r, v)
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m kv_cache_quantization_srft_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        sp = ctypes.POINTER(Shape)
+        vp = ctypes.c_void_p
+        L.srftq_validate.argtypes = [sp]
+        L.srftq_codes_bytes.argtypes = [sp]
+        L.srftq_codes_bytes.restype = ctypes.c_size_t
+        L.srftq_scales_count.argtypes = [sp]
+        L.srftq_scales_count.restype = ctypes.c_size_t
+        L.srftq_quantize.argtypes = [sp, vp, vp, vp, vp, vp, vp]
+        L.srftq_dequantize.argtypes = [sp, vp, vp, vp, vp, vp, vp]
+        L.srftq_rotate.argtypes = [sp, vp, vp, vp, vp]
+        L.srftq_unrotate.argtypes = [sp, vp, vp, vp, vp]
+        L.srftq_calibrate_lambda.argtypes = [sp, vp, vp, vp, vp]
+        L.srftq_status_string.argtypes = [ctypes.c_int]
+        L.srftq_status_string.restype = ctypes.c_char_p
+        L.srftq_version.argtypes = []
+        for f in ("srftq_validate", "srftq_quantize", "srftq_dequantize", "srftq_rotate",
+                  "srftq_unrotate", "srftq_calibrate_lambda", "srftq_version"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().srftq_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != SRFTQ_OK:
+        raise SrftqError(status, where)
+
+
+# ---------------------------------------------------------------------------
+# The C functions, same names and arguments.
+# ---------------------------------------------------------------------------
+
+def srftq_validate(shape: Shape) -> int:
+    return lib().srftq_validate(ctypes.byref(shape))
+
+
+def srftq_codes_bytes(shape: Shape) -> int:
+    return int(lib().srftq_codes_bytes(ctypes.byref(shape)))
+
+
+def srftq_scales_count(shape: Shape) -> int:
+    return int(lib().srftq_scales_count(ctypes.byref(shape)))
+
+
+def srftq_version() -> int:
+    return int(lib().srftq_version())
+
+
+def _dp(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(int(stream))
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def srftq_quantize(shape, x, signs, lam, codes, scales, stream=None) -> int:
+    return lib().srftq_quantize(ctypes.byref(shape), _dp(x), _dp(signs), _dp(lam), _dp(codes),
+                                _dp(scales), _stream(stream))
+
+
+def srftq_dequantize(shape, codes, scales, signs, lam, x_out, stream=None) -> int:
+    return lib().srftq_dequantize(ctypes.byref(shape), _dp(codes), _dp(scales), _dp(signs), _dp(lam),
+                                  _dp(x_out), _stream(stream))
+
+
+def srftq_rotate(shape, x, signs, y, stream=None) -> int:
+    return lib().srftq_rotate(ctypes.byref(shape), _dp(x), _dp(signs), _dp(y), _stream(stream))
+
+
+def srftq_unrotate(shape, y, signs, x_out, stream=None) -> int:
+    return lib().srftq_unrotate(ctypes.byref(shape), _dp(y), _dp(signs), _dp(x_out), _stream(stream))
+
+
+def srftq_calibrate_lambda(shape, x, signs, lam_out, stream=None) -> int:
+    return lib().srftq_calibrate_lambda(ctypes.byref(shape), _dp(x), _dp(signs), _dp(lam_out),
+                                        _stream(stream))
+
+
+# ---------------------------------------------------------------------------
+# torch conveniences.
+# ---------------------------------------------------------------------------
+
+def _dims(x):
+    if x.dim() == 3:
+        T, H, d = x.shape
+        return 1, T, H, d
+    if x.dim() == 4:
+        return tuple(x.shape)
+    raise ValueError("expected [T,H,d] or [B,T,H,d]")
+
+
+def _req(t, dtype, name):
+    import torch
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def quantize(x, signs=None, lam=None, group=16, bits=4, rot="srft", variant="default",
+             codes=None, scales=None, stream=None):
+    """x fp16 [B,T,H,d] or [T,H,d] -> (codes uint8 [...,d*bits/8], scales fp16 [...,d/group])."""
+    import torch
+    B, T, H, d = _dims(x)
+    _req(x, torch.float16, "x")
+    _req(signs, torch.int8, "signs")
+    _req(lam, torch.float32, "lambda")
+    lead = tuple(x.shape[:-1])
+    if codes is None:
+        codes = torch.empty(lead + (d * bits // 8,), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(lead + (d // group,), dtype=torch.float16, device=x.device)
+    sh = make_shape(B, T, H, d, group, bits, rot, variant)
+    _check(srftq_quantize(sh, x, signs, lam, codes, scales, stream), "srftq_quantize")
+    return codes, scales
+
+
+def dequantize(codes, scales, signs=None, lam=None, group=16, bits=4, rot="srft", variant="default",
+               d=None, out=None, stream=None):
+    """codes + scales -> fp16 [...,d]."""
+    import torch
+    _req(codes, torch.uint8, "codes")
+    _req(scales, torch.float16, "scales")
+    _req(signs, torch.int8, "signs")
+    _req(lam, torch.float32, "lambda")
+    if d is None:
+        d = codes.shape[-1] * 8 // bits
+    lead = tuple(codes.shape[:-1])
+    if codes.dim() == 3:
+        B, T, H = (1,) + lead
+    elif codes.dim() == 4:
+        B, T, H = lead
+    else:
+        raise ValueError("codes must be [T,H,*] or [B,T,H,*]")
+    if out is None:
+        out = torch.empty(lead + (d,), dtype=torch.float16, device=codes.device)
+    sh = make_shape(B, T, H, d, group, bits, rot, variant)
+    _check(srftq_dequantize(sh, codes, scales, signs, lam, out, stream), "srftq_dequantize")
+    return out
+
+
+def rotate(x, signs=None, rot="srft", variant="default", out=None, stream=None):
+    """Rotated coordinates y = M (s . x), fp32, same shape as x."""
+    import torch
+    B, T, H, d = _dims(x)
+    _req(x, torch.float16, "x")
+    _req(signs, torch.int8, "signs")
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+    sh = make_shape(B, T, H, d, 8, 4, rot, variant)
+    _check(srftq_rotate(sh, x, signs, out, stream), "srftq_rotate")
+    return out
+
+
+def unrotate(y, signs=None, rot="srft", variant="default", out=None, stream=None):
+    """fp16 s . (M^T y), same shape as y."""
+    import torch
+    B, T, H, d = _dims(y)
+    _req(y, torch.float32, "y")
+    _req(signs, torch.int8, "signs")
+    if out is None:
+        out = torch.empty(y.shape, dtype=torch.float16, device=y.device)
+    sh = make_shape(B, T, H, d, 8, 4, rot, variant)
+    _check(srftq_unrotate(sh, y, signs, out, stream), "srftq_unrotate")
+    return out
+
+
+def calibrate_lambda(x, signs=None, rot="srft", variant="default", out=None, stream=None):
+    """lambda [B,H,d] (or [H,d] for 3-D x) = 1/RMS over tokens of the rotated coordinates."""
+    import torch
+    B, T, H, d = _dims(x)
+    _req(x, torch.float16, "x")
+    _req(signs, torch.int8, "signs")
+    if out is None:
+        out = torch.empty((B, H, d), dtype=torch.float32, device=x.device)
+    sh = make_shape(B, T, H, d, 8, 4, rot, variant)
+    _check(srftq_calibrate_lambda(sh, x, signs, out, stream), "srftq_calibrate_lambda")
+    return out if x.dim() == 4 else out[0]

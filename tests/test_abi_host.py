@@ -1,0 +1,137 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/srftq.h declares, and rejects bad arguments before
+anything is launched."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from kv_cache_quantization_srft_amd import srftq as S
+from oracle import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    hdr = open(os.path.join(ROOT, "include", "srftq.h")).read()
+    return sorted(set(re.findall(r"\b(srftq_[a-z_]+)\s*\(", hdr)))
+
+
+def test_library_exports_every_declared_function():
+    L = S.lib()
+    names = _declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings():
+    assert S.srftq_version() >= 100
+    for st in range(6):
+        assert isinstance(S.status_string(st), str) and S.status_string(st)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(B=1, T=10, H=8, d=128, group=16, bits=4), S.SRFTQ_OK),
+    (dict(B=56, T=32768, H=2, d=128, group=16, bits=4), S.SRFTQ_OK),
+    (dict(B=1, T=256, H=8, d=64, group=32, bits=8), S.SRFTQ_OK),
+    (dict(B=1, T=0, H=8, d=128, group=16, bits=4), S.SRFTQ_OK),
+    (dict(B=0, T=5, H=8, d=128, group=16, bits=4), S.SRFTQ_OK),
+    (dict(B=1, T=10, H=8, d=128, group=128, bits=8), S.SRFTQ_OK),
+    (dict(B=1, T=10, H=8, d=96, group=16, bits=4), S.SRFTQ_ERR_UNSUPPORTED),
+    (dict(B=1, T=10, H=8, d=128, group=16, bits=3), S.SRFTQ_ERR_UNSUPPORTED),
+    (dict(B=1, T=10, H=8, d=128, group=12, bits=4), S.SRFTQ_ERR_UNSUPPORTED),
+    (dict(B=1, T=10, H=8, d=128, group=4, bits=4), S.SRFTQ_ERR_UNSUPPORTED),
+    (dict(B=1, T=10, H=8, d=64, group=128, bits=4), S.SRFTQ_ERR_UNSUPPORTED),
+    (dict(B=-1, T=10, H=8, d=128, group=16, bits=4), S.SRFTQ_ERR_SHAPE),
+    (dict(B=1, T=-1, H=8, d=128, group=16, bits=4), S.SRFTQ_ERR_SHAPE),
+    (dict(B=1, T=10, H=0, d=128, group=16, bits=4), S.SRFTQ_ERR_SHAPE),
+    (dict(B=1 << 20, T=1 << 30, H=8, d=128, group=16, bits=4), S.SRFTQ_ERR_SHAPE),
+])
+def test_validate(kw, expect):
+    assert S.srftq_validate(S.make_shape(**kw)) == expect
+
+
+def test_validate_rot_and_variant_range():
+    assert S.srftq_validate(S.make_shape(1, 1, 1, 128, rot=5)) == S.SRFTQ_ERR_UNSUPPORTED
+    assert S.srftq_validate(S.make_shape(1, 1, 1, 128, variant=3)) == S.SRFTQ_ERR_UNSUPPORTED
+    for r in ("srft", "srht", "none"):
+        for v in ("default", "real", "paired"):
+            assert S.srftq_validate(S.make_shape(1, 1, 1, 128, rot=r, variant=v)) == S.SRFTQ_OK
+
+
+def test_null_shape_pointer():
+    assert S.lib().srftq_validate(None) == S.SRFTQ_ERR_NULL
+
+
+@pytest.mark.parametrize("d,group,bits", [(128, 16, 4), (64, 32, 8), (128, 128, 8), (64, 8, 4)])
+def test_sizes_match_oracle_layout(d, group, bits):
+    B, T, H = 2, 7, 3
+    sh = S.make_shape(B, T, H, d, group, bits)
+    x = np.zeros((B, T, H, d), dtype=np.float16)
+    codes, scales = oracle.quantize(x, None, None, group, bits, "none")
+    assert S.srftq_codes_bytes(sh) == codes.nbytes
+    assert S.srftq_scales_count(sh) == scales.size
+
+
+def test_sizes_zero_for_invalid_shape():
+    sh = S.make_shape(1, 10, 8, 96, 16, 4)
+    assert S.srftq_codes_bytes(sh) == 0 and S.srftq_scales_count(sh) == 0
+
+
+class _Fake:
+    """Stands in for a tensor: only data_ptr() is read by the raw bindings."""
+
+    def __init__(self, addr):
+        self.addr = addr
+
+    def data_ptr(self):
+        return self.addr
+
+
+def test_argument_errors_return_before_launch():
+    sh = S.make_shape(1, 64, 8, 128, 16, 4)
+    a = _Fake(0x10000)
+    mis = _Fake(0x10008)
+    # NULL required pointers
+    assert S.srftq_quantize(sh, None, None, None, a, a, stream=0) == S.SRFTQ_ERR_NULL
+    assert S.srftq_quantize(sh, a, None, None, None, a, stream=0) == S.SRFTQ_ERR_NULL
+    assert S.srftq_dequantize(sh, a, None, None, None, a, stream=0) == S.SRFTQ_ERR_NULL
+    assert S.srftq_rotate(sh, a, None, None, stream=0) == S.SRFTQ_ERR_NULL
+    assert S.srftq_unrotate(sh, None, None, a, stream=0) == S.SRFTQ_ERR_NULL
+    assert S.srftq_calibrate_lambda(sh, a, None, None, stream=0) == S.SRFTQ_ERR_NULL
+    # misaligned data pointers
+    assert S.srftq_quantize(sh, mis, None, None, a, a, stream=0) == S.SRFTQ_ERR_ALIGN
+    assert S.srftq_quantize(sh, a, None, None, mis, a, stream=0) == S.SRFTQ_ERR_ALIGN
+    assert S.srftq_dequantize(sh, a, mis, None, None, a, stream=0) == S.SRFTQ_ERR_ALIGN
+    assert S.srftq_quantize(sh, a, _Fake(0x10001), None, a, a, stream=0) == S.SRFTQ_ERR_ALIGN
+    assert S.srftq_quantize(sh, a, None, _Fake(0x10002), a, a, stream=0) == S.SRFTQ_ERR_ALIGN
+    # bad shape wins over everything
+    bad = S.make_shape(1, 64, 8, 100, 16, 4)
+    assert S.srftq_quantize(bad, a, None, None, a, a, stream=0) == S.SRFTQ_ERR_UNSUPPORTED
+
+
+def test_empty_problem_is_a_no_op():
+    sh = S.make_shape(1, 0, 8, 128, 16, 4)
+    assert S.srftq_quantize(sh, None, None, None, None, None, stream=0) == S.SRFTQ_OK
+    assert S.srftq_dequantize(sh, None, None, None, None, None, stream=0) == S.SRFTQ_OK
+    assert S.srftq_rotate(sh, None, None, None, stream=0) == S.SRFTQ_OK
+    assert S.srftq_unrotate(sh, None, None, None, stream=0) == S.SRFTQ_OK
+
+
+def test_device_calls_without_a_device_report_hip_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a device is present; this checks the GPU-less failure path only")
+    sh = S.make_shape(1, 64, 8, 128, 16, 4)
+    a = _Fake(0x10000)
+    assert S.srftq_quantize(sh, a, None, None, a, a, stream=0) == S.SRFTQ_ERR_HIP
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(S, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(S, "_lib", None)
+    with pytest.raises(RuntimeError):
+        S.lib()
