@@ -5,7 +5,9 @@
 // int4/int8) and step 5 (two int4 per byte), with "Metodologia" 3
 // (per-channel + per-group scaling).  Decision rule (fp32):
 //   z = lambda * y;  a = max_G |z|;  sigma = fp16(min(a * fp32(1/qmax), 65504));
-//   q = clamp(rne(z / sigma), -qmax, qmax)  (q = 0 when sigma == 0).
+//   r = fp32(1/sigma) correctly rounded;
+//   q = clamp(rne(z * r), -qmax, qmax) with the product exact  (q = 0 when
+//   sigma == 0).
 //
 // Implementation notes (gfx950):
 //   - The transform leaves y unscaled; the per-coordinate scale c_j is
@@ -41,6 +43,17 @@ struct QConst {
   static constexpr uint32_t kLo = kMagicBits - (uint32_t)kQmax;   // bits of q = -qmax
   static constexpr uint32_t kHi = kMagicBits + (uint32_t)kQmax;   // bits of q = +qmax
 };
+
+// fp32(1/sigma), correctly rounded, for sigma an fp16 value.  1/sigma =
+// 2^-e / m with an integer m < 2^11 is never within 2^-36 (relative) of an
+// fp32 rounding midpoint, so an fp64 reciprocal (plus one Newton step) rounded
+// to fp32 is the correctly rounded fp32 reciprocal.  One per group.
+__device__ __forceinline__ float recip_f16_value(float sigma) {
+  const double s = (double)sigma;
+  double r = __builtin_amdgcn_rcp(s);
+  r = __builtin_fma(r, __builtin_fma(-s, r, 1.0), r);
+  return (float)r;
+}
 
 // Codes of one vector: int4 -> D/8 dwords, int8 -> D/4 dwords.
 template <int D, int BITS>
@@ -129,7 +142,7 @@ __device__ __forceinline__ void quantize_tail(float (&y)[D], const float* __rest
       const float sg = ii == 0 ? hlo(sw) : hhi(sw);
       // sigma subnormal (and nonzero): rounding alone may leave the range
       need_clamp |= (sg != 0.0f && sg < 6.103515625e-05f) ? 1u : 0u;
-      const float r = sg == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(sg);
+      const float r = sg == 0.0f ? 0.0f : recip_f16_value(sg);
       rB[g] = r * cB;
       rE[g] = r * cE;
     });

@@ -35,8 +35,10 @@
  *     kernel: z = fp32(lambda * y); a = max |z| over the group;
  *     t = min(a * fp32(1/qmax), 65504) (fp32 multiply);
  *     sigma = fp16 round-to-nearest-even(t), stored;
- *     q = 0 if sigma == 0 else clamp(rne(z / sigma), -qmax, qmax), with the
- *     division in fp32 and the codes taken against the stored fp16 sigma.
+ *     r = fp32(1 / sigma), correctly rounded;
+ *     q = 0 if sigma == 0 else clamp(rne(z * r), -qmax, qmax), with the
+ *     product z * r taken exactly, and the codes taken against the stored
+ *     fp16 sigma.
  *   - int4 nibbles are two's complement, even coordinate in the low nibble.
  *   - signs == NULL means s = +1; lambda == NULL means lambda = 1.
  *
@@ -359,16 +361,21 @@ int oracle_quantize(int64_t B, int64_t T, int H, int d, int group, int bits,
                 uint16_t sh = oracle_f64_to_f16((double)t);
                 float sg = (float)oracle_f16_to_f64(sh);
                 scales[(size_t)v * ng + g] = sh;
+                /* fp32 reciprocal of the stored scale, correctly rounded:
+                 * the double quotient is exact to 2^-53 and 1/sigma never
+                 * sits within 2^-36 of an fp32 midpoint, so one rounding
+                 * of it to float is the correct rounding. */
+                float r = sg == 0.0f ? 0.0f : (float)(1.0 / (double)sg);
                 for (int j = g * group; j < (g + 1) * group; ++j) {
                     if (sg == 0.0f) {
                         q[j] = 0;
                     } else {
-                        float r = z[j] / sg;           /* fp32 division */
-                        float n = nearbyintf(r);       /* ties to even */
-                        if (n > (float)qmax)
-                            n = (float)qmax;
-                        if (n < (float)-qmax)
-                            n = (float)-qmax;
+                        /* 24-bit x 24-bit product: exact in double */
+                        double n = nearbyint((double)z[j] * (double)r);   /* ties to even */
+                        if (n > (double)qmax)
+                            n = (double)qmax;
+                        if (n < (double)-qmax)
+                            n = (double)-qmax;
                         q[j] = (int)n;
                     }
                 }

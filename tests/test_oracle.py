@@ -399,3 +399,20 @@ def test_byte_accounting_reproduces_pages_figures():
 
     assert round(ratio(32), 2) == gold["compression_upper"]
     assert round(gold["llama3_70b_128k_fp16_GB"] / ratio(64), 1) == gold["llama3_70b_128k_int4_GB"]
+
+
+def test_fp32_reciprocal_of_every_fp16_is_correctly_rounded():
+    """The decision uses fp32(1/sigma) taken as one rounding of the double
+    quotient; check it is the correctly rounded fp32 reciprocal for every
+    positive finite fp16 sigma, with exact rational arithmetic."""
+    from fractions import Fraction
+    sig = np.arange(1, 0x7c00, dtype=np.uint16).view(np.float16).astype(np.float64)
+    r = (1.0 / sig).astype(np.float32)
+    up = np.nextafter(r, np.float32(np.inf))
+    dn = np.nextafter(r, np.float32(0))
+    for s_, r_, u_, d_ in zip(sig.tolist(), r.astype(np.float64).tolist(),
+                              up.astype(np.float64).tolist(), dn.astype(np.float64).tolist()):
+        exact = 1 / Fraction(s_)
+        e = abs(Fraction(r_) - exact)
+        assert e <= abs(Fraction(u_) - exact) and e <= abs(Fraction(d_) - exact)
+        assert e != abs(Fraction(u_) - exact) and e != abs(Fraction(d_) - exact)   # never a tie
