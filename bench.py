@@ -162,6 +162,25 @@ def main():
                 "traffic": traffic,
                 "bytes_per_vector": bpv, "vectors_per_launch": nvec}
 
+    # plain copy kernel of the quantize input's size (fp16 negate: reads and
+    # writes 2*d bytes per vector): achievable-bandwidth reference, and the
+    # known-size kernel the HBM byte counters are scaled against
+    src = xd.view(-1)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        torch.neg(src, out=dst)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    c0.record()
+    for _ in range(args.steps):
+        torch.neg(src, out=dst)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_ms = c0.elapsed_time(c1) / args.steps
+    copy_probe = {"bytes_read": src.numel() * 2, "bytes_written": dst.numel() * 2, "ms": copy_ms,
+                  "GBps": 2 * src.numel() * 2 / (copy_ms * 1e-3) / 1e9}
+    del dst
+
     # sanity: reconstruction error of the round trip
     rel = (torch.linalg.vector_norm(xhat.float() - xd.float()) / torch.linalg.vector_norm(xd.float())).item()
 
@@ -190,6 +209,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "per_kernel": per_kernel,
+        "copy_probe": copy_probe,
         "fp16_in_GBps_quantize": per_kernel["quantize"]["fp16_GBps"],
         "reconstruction_rel_l2": rel,
         "device": torch.cuda.get_device_name(0),

@@ -90,11 +90,45 @@ __device__ __forceinline__ void wait_lgkmcnt0() {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// One 16-byte-per-lane direct load into LDS: lane l's 16 bytes land at
-// lds_base + 16*l (lds_base must be wave-uniform).
-__device__ __forceinline__ void lds_dma16(const void* gptr, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(gptr, (lds_void_t*)lds_base, 16, 0, 0);
+// LDS offset of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
+
+// Direct global -> LDS load (LDS-DMA) of SIZE bytes per lane: lane l reads
+// sbase + voff(l) and its data lands at LDS byte lds + SIZE*l.  sbase and
+// lds are wave-uniform.  Issued from inline asm so the compiler neither
+// tracks it nor inserts its blanket vmcnt(0) before later LDS reads; the
+// kernels order it themselves with wait_vm<>() / wait_lgkm0(), and they
+// issue no other vector-memory loads whose results the compiler tracks.
+// "s_nop 0" is the one wait state required between writing M0 and an LDS-DMA.
+template <int SIZE>
+__device__ __forceinline__ void dma_to_lds(const void* sbase, uint32_t voff, uint32_t lds) {
+  static_assert(SIZE == 16 || SIZE == 4 || SIZE == 2, "LDS-DMA size");
+  if constexpr (SIZE == 16)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(voff), "s"(sbase), "s"(lds) : "memory", "m0");
+  else if constexpr (SIZE == 4)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+                 :: "v"(voff), "s"(sbase), "s"(lds) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_ushort %0, %1"
+                 :: "v"(voff), "s"(sbase), "s"(lds) : "memory", "m0");
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight
+// (loads and stores complete in issue order on this counter).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Compiler-only ordering point for LDS traffic inside one wave (the LDS
+// executes one wave's instructions in order, so no hardware barrier is needed
+// when a block is a single wave).
+__device__ __forceinline__ void wave_fence() { asm volatile("" ::: "memory"); }
 
 // Read-only data addressed through the constant address space: loads with a
 // wave-uniform address become scalar (s_load) loads even across barriers.

@@ -68,77 +68,117 @@ __device__ __forceinline__ int64_t row_index(const Geo& a, int bh, int64_t t) {
 }
 
 // ----------------------------------------------------------------------------
-// fp16 row tile geometry: 64 rows of 2*D bytes, CPR 16-byte chunks per row.
-// Chunk c of row v sits at LDS slot position c ^ sw(v).
+// A tile of 64 rows of ROWB bytes in LDS, filled by LDS-DMA.  Row v starts at
+// v*ROWB; for ROWB >= 16 its 16-byte chunk c sits at position c ^ swz(v),
+// an XOR swizzle that keeps ds_read_b128 of "chunk c of my own row" free of
+// bank conflicts in every 8-lane and 16-lane phase.  Sub-16-byte rows are
+// stored unswizzled (lanes then read consecutive addresses).
+//
+// DMA: instruction i writes LDS bytes [1 KiB * i, 1 KiB * (i+1)) (16 B per
+// lane) or, for ROWB < 16, E = min(ROWB, 4) bytes per lane.  Lane l of
+// instruction i fetches chunk (l % CPR) ^ swz(v) of row v = i*RPI + l/CPR:
+// every instruction reads whole rows, i.e. full cache lines.  The per-lane
+// source offsets depend on i only through i mod kPat and are computed once.
 // ----------------------------------------------------------------------------
-template <int D>
-struct F16Tile {
-  static constexpr int kRowBytes = 2 * D;
-  static constexpr int kCpr = kRowBytes / 16;        // chunks per row
-  static constexpr int kInst = kCpr;                 // 64*kCpr chunks / 64 lanes
-  static constexpr int kRpi = 64 / kCpr;             // rows per instruction
-  static constexpr int kBytes = 64 * kRowBytes;
-  static_assert(kCpr == 8 || kCpr == 16, "tile geometry");
-  // sw depends on the instruction index only through (i mod kPat)
-  static constexpr int kPat = kCpr == 16 ? 4 : 2;
-  __device__ static __forceinline__ int sw(int v) {
-    return kCpr == 16 ? (v & 15) : ((v & 7) ^ ((v >> 3) & 1));
+template <int ROWB>
+struct RowTile {
+  static_assert(ROWB == 2 || ROWB == 4 || ROWB == 8 || ROWB == 16 || ROWB == 32 || ROWB == 64 ||
+                    ROWB == 128 || ROWB == 256 || ROWB == 512,
+                "row size");
+  static constexpr bool kWide = ROWB >= 16;
+  static constexpr int kElem = kWide ? 16 : (ROWB < 4 ? ROWB : 4);   // DMA bytes per lane
+  // LDS-DMA writes at least a dword per lane: a 2-byte row occupies a
+  // 4-byte LDS slot
+  static constexpr int kSlot = kElem < 4 ? 4 : kElem;
+  static constexpr int kEpr = ROWB / kElem;                          // DMA elements per row
+  static constexpr int kRpi = 64 / kEpr;                             // rows per instruction
+  static constexpr int kInst = kEpr;                                 // instructions per tile
+  static constexpr int kRowLds = kEpr * kSlot;                       // LDS bytes per row
+  static constexpr int kBytes = 64 * kRowLds;
+  static constexpr int kCpr = kWide ? ROWB / 16 : 1;
+  static constexpr int kPat = !kWide ? 1 : kCpr <= 4 ? 1 : kCpr == 8 ? 2 : kCpr == 16 ? 4 : 8;
+
+  __device__ static __forceinline__ int swz(int v) {
+    if constexpr (!kWide || kCpr == 1) return 0;
+    else if constexpr (kCpr == 2) return ((v >> 2) ^ (v >> 3)) & 1;
+    else if constexpr (kCpr == 4) return ((v >> 1) & 3) ^ ((v >> 3) & 1);
+    else if constexpr (kCpr == 8) return (v & 7) ^ ((v >> 3) & 1);
+    else return v & 15;
   }
-};
 
-// Per-lane byte offsets (relative to the tile's first row) of the DMA
-// source for instruction pattern m, rows spaced rsb bytes apart.
-template <int D>
-__device__ __forceinline__ uint32_t dma_offset(int lane, int i, uint32_t rsb, int nv) {
-  using TL = F16Tile<D>;
-  int v = i * TL::kRpi + lane / TL::kCpr;
-  const int p = lane % TL::kCpr;
-  const int c = p ^ TL::sw(v);
-  if (v > nv - 1) v = nv - 1;
-  return (uint32_t)v * rsb + 16u * (uint32_t)c;
-}
-
-template <int D>
-struct DmaPlan {
-  using TL = F16Tile<D>;
-  uint32_t off[TL::kPat];
-  __device__ __forceinline__ void init(int lane, uint32_t rsb) {
-#pragma unroll
-    for (int m = 0; m < TL::kPat; ++m) off[m] = dma_offset<D>(lane, m, rsb, 64);
+  // Source byte offset (relative to row 0) of lane `lane` in instruction i;
+  // rows beyond nv-1 are clamped to the last valid row.
+  __device__ static __forceinline__ uint32_t src_offset(int lane, int i, uint32_t rsb, int nv) {
+    int v = i * kRpi + lane / kEpr;
+    const int e = lane % kEpr;
+    const int c = kWide ? (e ^ swz(v)) : e;
+    if (v > nv - 1) v = nv - 1;
+    return (uint32_t)v * rsb + (uint32_t)(c * kElem);
   }
-};
 
-// Issue the 64-row fp16 tile starting at `base` into LDS.
-template <int D>
-__device__ __forceinline__ void issue_tile(const uint8_t* base, uint32_t rsb, int nv, int lane,
-                                           const DmaPlan<D>& plan, uint8_t* lds) {
-  using TL = F16Tile<D>;
-  if (nv == 64) {
+  struct Plan {
+    uint32_t off[kPat];
+    __device__ __forceinline__ void init(int lane, uint32_t rsb) {
 #pragma unroll
-    for (int i = 0; i < TL::kInst; ++i) {
-      const uint8_t* g = base + (size_t)(i / TL::kPat) * (size_t)(TL::kPat * TL::kRpi) * rsb;
-      lds_dma16(g + plan.off[i % TL::kPat], lds + i * 1024);
+      for (int m = 0; m < kPat; ++m) off[m] = src_offset(lane, m, rsb, 64);
     }
-  } else {
+  };
+
+  // Issue the whole tile (rows 0..nv-1 of the tile starting at `base`,
+  // wave-uniform) into LDS at `lds`.
+  __device__ static __forceinline__ void issue(const uint8_t* base, uint32_t rsb, int nv, int lane,
+                                               const Plan& plan, uint8_t* lds) {
+    const uint32_t l0 = lds_addr(lds);
+    if (nv == 64) {
 #pragma unroll
-    for (int i = 0; i < TL::kInst; ++i) lds_dma16(base + dma_offset<D>(lane, i, rsb, nv), lds + i * 1024);
+      for (int i = 0; i < kInst; ++i) {
+        const uint8_t* g = base + (size_t)(i / kPat) * (size_t)(kPat * kRpi) * rsb;
+        dma_to_lds<kElem>(g, plan.off[i % kPat], l0 + i * 64 * kSlot);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kInst; ++i) dma_to_lds<kElem>(base, src_offset(lane, i, rsb, nv), l0 + i * 64 * kSlot);
+    }
   }
+
+  // Lane v's own row as ROWB/4 dwords (ROWB >= 4) or one half-dword.
+  template <int NW>
+  __device__ static __forceinline__ void read_row(const uint8_t* lds, int v, uint32_t (&w)[NW]) {
+    const uint8_t* row = lds + v * kRowLds;
+    if constexpr (kWide) {
+      static_assert(NW == ROWB / 4, "row words");
+      int s = swz(v);
+      asm("" : "+v"(s));   // keep per-chunk addresses short-lived (not hoisted)
+      static_for<kCpr>([&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        const uint4 q = *(const uint4*)(row + 16 * (c ^ s));
+        w[4 * c + 0] = q.x;
+        w[4 * c + 1] = q.y;
+        w[4 * c + 2] = q.z;
+        w[4 * c + 3] = q.w;
+      });
+    } else if constexpr (ROWB == 8) {
+      const uint2 q = *(const uint2*)row;
+      w[0] = q.x;
+      w[1] = q.y;
+    } else if constexpr (ROWB == 4) {
+      w[0] = *(const uint32_t*)row;
+    } else {
+      w[0] = *(const uint16_t*)row;
+    }
+  }
+};
+
+// A D-float row (lambda) fetched by LDS-DMA: lanes 0..D/4-1 move 16 B each.
+template <int D>
+__device__ __forceinline__ void issue_row_f32(const float* src, int lane, uint8_t* lds) {
+  if (lane < D / 4) dma_to_lds<16>(src, 16u * (uint32_t)lane, lds_addr(lds));
 }
 
-// Read lane `v`'s own row (D/2 dwords) from the staged tile.
-template <int D>
-__device__ __forceinline__ void read_row(const uint8_t* lds, int v, uint32_t (&w)[D / 2]) {
-  using TL = F16Tile<D>;
-  const uint8_t* row = lds + v * TL::kRowBytes;
-  const int s = TL::sw(v);
-  static_for<TL::kCpr>([&](auto cc) {
-    constexpr int c = decltype(cc)::value;
-    const uint4 q = *(const uint4*)(row + 16 * (c ^ s));
-    w[4 * c + 0] = q.x;
-    w[4 * c + 1] = q.y;
-    w[4 * c + 2] = q.z;
-    w[4 * c + 3] = q.w;
-  });
+// Number of global store instructions store_words<N> / store_scales issue.
+template <int N>
+constexpr int store_count() {
+  return N % 4 == 0 ? N / 4 : 1;
 }
 
 template <int N>
@@ -197,23 +237,33 @@ __device__ __forceinline__ void load_scales(const uint8_t* src, uint32_t (&s)[Sc
 
 // ----------------------------------------------------------------------------
 // Quantize: fp16 [B,T,H,D] -> codes + fp16 scales.
+//
+// Loop per tile: wait for the tile's LDS-DMA (not for the previous tile's
+// stores), read the own row from LDS, issue the next tile's DMA, transform +
+// quantize in registers, store.  lambda rows arrive by DMA too, into a
+// double-buffered LDS row read with broadcast ds_reads.
 // ----------------------------------------------------------------------------
 template <int D, int G, int BITS, int ROT, int VAR, bool LAM>
 __global__ __launch_bounds__(64) SRFTQ_QUANT_OCC void quantize_kernel(const uint16_t* __restrict__ x,
-                                                      const int8_t* __restrict__ signs,
-                                                      const float* __restrict__ lambda,
-                                                      uint8_t* __restrict__ codes_out,
-                                                      uint16_t* __restrict__ scales_out, Geo a) {
-  using TL = F16Tile<D>;
+                                                                      const int8_t* __restrict__ signs,
+                                                                      const float* __restrict__ lambda,
+                                                                      uint8_t* __restrict__ codes_out,
+                                                                      uint16_t* __restrict__ scales_out,
+                                                                      Geo a) {
+  using XT = RowTile<2 * D>;
   constexpr int CB = D * BITS / 8;        // code bytes per vector
   constexpr int SB = 2 * D / G;           // scale bytes per vector
-  __shared__ __attribute__((aligned(16))) uint8_t lds[TL::kBytes];
+  constexpr int NCW = CodeWords<D, BITS>::kWords;
+  constexpr int NSW = ScaleWords<D, G>::kWords;
+  constexpr int NST = store_count<NCW>() + 1;   // global stores per tile
+  __shared__ __attribute__((aligned(16))) uint8_t lds[XT::kBytes];
+  __shared__ __attribute__((aligned(16))) float lam_lds[LAM ? 2 * D : 4];
 
   const int lane = threadIdx.x;
   const int stride = gridDim.x;
   if ((int)blockIdx.x >= a.n_tiles) return;
-  const uint32_t rsb = (uint32_t)a.H * (uint32_t)TL::kRowBytes;   // x row stride, bytes
-  DmaPlan<D> plan;
+  const uint32_t rsb = (uint32_t)a.H * (uint32_t)(2 * D);   // x row stride, bytes
+  typename XT::Plan plan;
   plan.init(lane, rsb);
   const int dk = stride / a.BH, dbh = stride - dk * a.BH;
 
@@ -221,118 +271,155 @@ __global__ __launch_bounds__(64) SRFTQ_QUANT_OCC void quantize_kernel(const uint
   cur.init(blockIdx.x, a.BH);
   int remaining = (a.n_tiles - 1 - (int)blockIdx.x) / stride;     // tiles after this one
 
-  auto tile_base = [&](const Cursor& c, int& nv) {
+  auto issue = [&](const Cursor& c, int& nv, int buf) {
     const int64_t t0 = (int64_t)c.k * 64;
     const int64_t left = a.T - t0;
     nv = left < 64 ? (int)left : 64;
-    return (const uint8_t*)x + row_index(a, c.bh, t0) * (int64_t)TL::kRowBytes;
+    XT::issue((const uint8_t*)x + row_index(a, c.bh, t0) * (int64_t)(2 * D), rsb, nv, lane, plan, lds);
+    if constexpr (LAM) issue_row_f32<D>(lambda + (int64_t)c.bh * D, lane, (uint8_t*)(lam_lds + buf * D));
   };
 
-  int nv;
-  issue_tile<D>(tile_base(cur, nv), rsb, nv, lane, plan, lds);
+  int nv, buf = 0;
+  issue(cur, nv, 0);
 
-  for (;;) {
-    wait_vmcnt<0>();
-    __syncthreads();
+  // One tile: read it from LDS, start the next tile's DMA, compute, store.
+  auto body = [&]() {
+    wave_fence();
     uint32_t w[D / 2];
-    read_row<D>(lds, lane, w);
-    wait_lgkmcnt0();
-    __syncthreads();
+    XT::read_row(lds, lane, w);
+    wait_lgkm0();   // the reads are done before the next DMA reuses the tile
 
     const Cursor now = cur;
-    const int nv_now = nv;
+    const int nv_now = nv, cb = buf;
     if (remaining > 0) {
       cur.advance(dk, dbh, a.BH);
-      issue_tile<D>(tile_base(cur, nv), rsb, nv, lane, plan, lds);
+      buf ^= 1;
+      issue(cur, nv, buf);
     }
 
     const HeadSigns sg(signs + (int64_t)now.bh * a.sign_stride);
     float y[D];
     forward<D, ROT, VAR>(w, sg, y);
-    uint32_t codes[CodeWords<D, BITS>::kWords];
-    uint32_t scales[ScaleWords<D, G>::kWords];
-    const float* lam = LAM ? lambda + (int64_t)now.bh * D : nullptr;
-    quantize_tail<D, G, BITS, ROT, VAR, LAM>(y, lam, codes, scales);
+    uint32_t codes[NCW];
+    uint32_t scales[NSW];
+    quantize_tail<D, G, BITS, ROT, VAR, LAM>(y, lam_lds + cb * D, codes, scales);
 
     if (lane < nv_now) {
       const int64_t r0 = row_index(a, now.bh, (int64_t)now.k * 64);   // uniform
       const uint32_t dr = (uint32_t)lane * (uint32_t)a.H;
-      store_words<CodeWords<D, BITS>::kWords>(codes_out + r0 * CB + dr * CB, codes);
+      store_words<NCW>(codes_out + r0 * CB + dr * CB, codes);
       store_scales<D, G>((uint8_t*)scales_out + r0 * SB + dr * SB, scales);
     }
-    if (remaining == 0) break;
+    return nv_now == 64;
+  };
+
+  // The first tile is peeled so that every entry into the loop has this
+  // tile's stores issued after the next tile's DMA: the wait at the top of
+  // the loop then covers the DMA only.
+  wait_vm<0>();
+  bool full = body();
+  while (remaining > 0) {
     --remaining;
+    // A full tile issued exactly NST stores after the DMA; after a ragged
+    // one some stores may have been skipped, so wait for everything.
+    if (full)
+      wait_vm<NST>();
+    else
+      wait_vm<0>();
+    full = body();
   }
 }
 
 // ----------------------------------------------------------------------------
-// Dequantize: codes + scales -> fp16 [B,T,H,D]; rows leave through LDS as
-// coalesced 1 KiB stores.  The next tile's codes are prefetched into
-// registers while the current one computes.
+// Dequantize: codes + scales -> fp16 [B,T,H,D].  Codes, scales and lambda
+// arrive by coalesced LDS-DMA (prefetched one tile ahead); output rows are
+// staged through LDS half a row at a time and leave as 1 KiB coalesced
+// stores.
 // ----------------------------------------------------------------------------
 template <int D, int G, int BITS, int ROT, int VAR, bool LAM>
 __global__ __launch_bounds__(64) SRFTQ_DEQUANT_OCC void dequantize_kernel(const uint8_t* __restrict__ codes_in,
-                                                        const uint16_t* __restrict__ scales_in,
-                                                        const int8_t* __restrict__ signs,
-                                                        const float* __restrict__ lambda,
-                                                        uint16_t* __restrict__ x_out, Geo a) {
-  using TL = F16Tile<D>;
+                                                                          const uint16_t* __restrict__ scales_in,
+                                                                          const int8_t* __restrict__ signs,
+                                                                          const float* __restrict__ lambda,
+                                                                          uint16_t* __restrict__ x_out, Geo a) {
   using Sc = Scales<D, ROT, VAR>;
   constexpr int CB = D * BITS / 8;
   constexpr int SB = 2 * D / G;
   constexpr int NCW = CodeWords<D, BITS>::kWords;
   constexpr int NSW = ScaleWords<D, G>::kWords;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[TL::kBytes];
-  __shared__ __attribute__((aligned(16))) float lam_tab[LAM ? D : 4];
+  using CT = RowTile<CB>;
+  using ST = RowTile<SB>;
+  using OT = RowTile<D>;                  // half an fp16 output row (D bytes)
+  constexpr int NST = 2 * OT::kInst;      // global stores per tile
+  __shared__ __attribute__((aligned(16))) uint8_t ctile[CT::kBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t stile[ST::kBytes < 16 ? 16 : ST::kBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t otile[OT::kBytes];
+  __shared__ __attribute__((aligned(16))) float lam_lds[LAM ? 2 * D : 4];
 
   const int lane = threadIdx.x;
   const int stride = gridDim.x;
   if ((int)blockIdx.x >= a.n_tiles) return;
-  const uint32_t rsb = (uint32_t)a.H * (uint32_t)TL::kRowBytes;
+  const uint32_t rsb_c = (uint32_t)a.H * CB, rsb_s = (uint32_t)a.H * SB;
+  const uint32_t rsb_x = (uint32_t)a.H * (uint32_t)(2 * D);
+  typename CT::Plan cplan;
+  cplan.init(lane, rsb_c);
+  typename ST::Plan splan;
+  splan.init(lane, rsb_s);
+  // output staging: per-lane LDS and global offsets for each store pattern
+  uint32_t o_lds[OT::kPat], o_glb[OT::kPat];
+#pragma unroll
+  for (int m = 0; m < OT::kPat; ++m) {
+    const int v = m * OT::kRpi + lane / OT::kCpr;
+    const int p = lane % OT::kCpr;
+    o_lds[m] = (uint32_t)(v * D + 16 * (p ^ OT::swz(v)));
+    o_glb[m] = (uint32_t)v * rsb_x + 16u * (uint32_t)p;
+  }
   const int dk = stride / a.BH, dbh = stride - dk * a.BH;
 
   Cursor cur;
   cur.init(blockIdx.x, a.BH);
   int remaining = (a.n_tiles - 1 - (int)blockIdx.x) / stride;
 
-  auto fetch = [&](const Cursor& c, uint32_t (&cw)[NCW], uint32_t (&sw)[NSW], int& nv) {
+  auto issue = [&](const Cursor& c, int& nv, int buf) {
     const int64_t t0 = (int64_t)c.k * 64;
     const int64_t left = a.T - t0;
     nv = left < 64 ? (int)left : 64;
-    const int v = lane < nv ? lane : nv - 1;
-    const int64_t r0 = row_index(a, c.bh, t0);                         // uniform
-    const uint32_t dr = (uint32_t)v * (uint32_t)a.H;
-    load_words<NCW>(codes_in + r0 * CB + dr * CB, cw);
-    load_scales<D, G>((const uint8_t*)scales_in + r0 * SB + dr * SB, sw);
+    const int64_t r0 = row_index(a, c.bh, t0);
+    CT::issue(codes_in + r0 * CB, rsb_c, nv, lane, cplan, ctile);
+    ST::issue((const uint8_t*)scales_in + r0 * SB, rsb_s, nv, lane, splan, stile);
+    if constexpr (LAM) issue_row_f32<D>(lambda + (int64_t)c.bh * D, lane, (uint8_t*)(lam_lds + buf * D));
   };
 
-  uint32_t cw[NCW], sw[NSW];
-  int nv;
-  fetch(cur, cw, sw, nv);
+  int nv, buf = 0;
+  issue(cur, nv, 0);
 
-  for (;;) {
+  auto body = [&]() {
+    wave_fence();
+    uint32_t cw[NCW], sw[NSW];
+    CT::read_row(ctile, lane, cw);
+    ST::read_row(stile, lane, sw);
+    const int cb = buf;
+    if constexpr (LAM) {
+      // e_j / lambda_j, computed lane-parallel in place, read back broadcast
+      float* lt = lam_lds + cb * D;
+      for (int j = lane; j < D; j += 64) {
+        const bool edge = Sc::kEdges && (j == 0 || j == D / 2);
+        lt[j] = (edge ? (float)Sc::kInvEdge : (float)Sc::kInvBulk) * __builtin_amdgcn_rcpf(lt[j]);
+      }
+    }
+    wait_lgkm0();   // the reads are done before the next DMA reuses the tiles
+    wave_fence();
+
     const Cursor now = cur;
     const int nv_now = nv;
-    uint32_t ccw[NCW], csw[NSW];
-#pragma unroll
-    for (int i = 0; i < NCW; ++i) ccw[i] = cw[i];
-#pragma unroll
-    for (int i = 0; i < NSW; ++i) csw[i] = sw[i];
     if (remaining > 0) {
       cur.advance(dk, dbh, a.BH);
-      fetch(cur, cw, sw, nv);
+      buf ^= 1;
+      issue(cur, nv, buf);
     }
 
-    if constexpr (LAM) {
-      // e_j / lambda_j is uniform per head: computed lane-parallel once per
-      // tile and broadcast from LDS.
-      const float* lrow = lambda + (int64_t)now.bh * D;
-      for (int j = lane; j < D; j += 64)
-        lam_tab[j] = (float)(Sc::is_edge(j) ? Sc::kInvEdge : Sc::kInvBulk) * __builtin_amdgcn_rcpf(lrow[j]);
-      __syncthreads();
-    }
     float y[D];
-    dequantize_head<D, G, BITS, ROT, VAR, LAM>(ccw, csw, lam_tab, y);
+    dequantize_head<D, G, BITS, ROT, VAR, LAM>(cw, sw, lam_lds + cb * D, y);
     float xr[D];
     inverse<D, ROT, VAR>(y, xr);
 
@@ -344,30 +431,45 @@ __global__ __launch_bounds__(64) SRFTQ_DEQUANT_OCC void dequantize_kernel(const 
       o[m] = pack_f16x2(xr[2 * m], xr[2 * m + 1]) ^ sg.mask(m);
     });
 
-    // stage the row in LDS (swizzled), then write 64 rows out coalesced
-    {
-      uint8_t* row = lds + lane * TL::kRowBytes;
-      const int s = TL::sw(lane);
-      static_for<TL::kCpr>([&](auto cc) {
-        constexpr int c = decltype(cc)::value;
-        *(uint4*)(row + 16 * (c ^ s)) = make_uint4(o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]);
-      });
-    }
-    __syncthreads();
-    {
-      const int64_t t0 = (int64_t)now.k * 64;
-      uint8_t* obase = (uint8_t*)x_out + row_index(a, now.bh, t0) * (int64_t)TL::kRowBytes;
-      static_for<TL::kInst>([&](auto ii) {
+    uint8_t* obase = (uint8_t*)x_out + row_index(a, now.bh, (int64_t)now.k * 64) * (int64_t)(2 * D);
+    static_for<2>([&](auto hh) {
+      constexpr int h = decltype(hh)::value;
+      {
+        uint8_t* row = otile + lane * D;
+        int s = OT::swz(lane);
+        asm("" : "+v"(s));
+        static_for<OT::kCpr>([&](auto cc) {
+          constexpr int c = decltype(cc)::value;
+          constexpr int k = h * OT::kCpr + c;       // chunk of the full row
+          *(uint4*)(row + 16 * (c ^ s)) = make_uint4(o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]);
+        });
+      }
+      wave_fence();
+      static_for<OT::kInst>([&](auto ii) {
         constexpr int i = decltype(ii)::value;
-        const int v = i * TL::kRpi + lane / TL::kCpr;
-        const int p = lane % TL::kCpr;
-        const uint4 q = *(const uint4*)(lds + v * TL::kRowBytes + 16 * (p ^ TL::sw(v)));
-        if (v < nv_now) *(uint4*)(obase + (size_t)v * rsb + 16 * p) = q;
+        constexpr int m = i % OT::kPat;
+        // o_lds[m] already holds the rows of pattern m; add whole periods only
+        const uint4 q = *(const uint4*)(otile + (i / OT::kPat) * (OT::kPat * OT::kRpi * D) + o_lds[m]);
+        uint8_t* dst = obase + (size_t)(i / OT::kPat) * (size_t)(OT::kPat * OT::kRpi) * rsb_x + h * D + o_glb[m];
+        if (nv_now == 64 || i * OT::kRpi + lane / OT::kCpr < nv_now) *(uint4*)dst = q;
       });
-    }
-    __syncthreads();
-    if (remaining == 0) break;
+      wave_fence();
+    });
+    return nv_now == 64;
+  };
+
+  // First tile peeled: inside the loop the wait covers the next tile's DMA
+  // only, while this tile's stores drain.
+  wait_vm<0>();
+  bool full = body();
+  while (remaining > 0) {
     --remaining;
+    // see quantize_kernel: exact store count only after a full tile
+    if (full)
+      wait_vm<NST>();
+    else
+      wait_vm<0>();
+    full = body();
   }
 }
 

@@ -89,7 +89,7 @@ __device__ __forceinline__ uint32_t pack_codes(const uint32_t* t) {
 }
 
 // Quantize one vector.  y: unscaled transform output (packed order).
-// lam: the head's lambda row (wave-uniform pointer) or unused.
+// lam: the head's lambda row in LDS (read broadcast) or unused.
 template <int D, int G, int BITS, int ROT, int VAR, bool LAM>
 __device__ __forceinline__ void quantize_tail(float (&y)[D], const float* __restrict__ lam,
                                               uint32_t (&codes)[CodeWords<D, BITS>::kWords],
@@ -101,10 +101,9 @@ __device__ __forceinline__ void quantize_tail(float (&y)[D], const float* __rest
   constexpr float cE = (float)Sc::kFwdEdge;
 
   if constexpr (LAM) {
-    const_ptr<float> lc = as_const(lam);
     static_for<D>([&](auto jj) {
       constexpr int j = decltype(jj)::value;
-      y[j] = y[j] * lc[j];
+      y[j] = y[j] * lam[j];
     });
   }
 
