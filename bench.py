@@ -112,8 +112,9 @@ def main():
     torch.cuda.synchronize()
     lam_h = lam.cpu().numpy() if lam is not None else None
 
-    codes = torch.empty(x.shape[:-1] + (w.d * w.bits // 8,), dtype=torch.uint8, device=dev)
-    scales = torch.empty(x.shape[:-1] + (w.d // w.group,), dtype=torch.float16, device=dev)
+    # head-major quantized cache [B, H, T, .]
+    codes = torch.empty((w.B, w.H, w.T, w.d * w.bits // 8), dtype=torch.uint8, device=dev)
+    scales = torch.empty((w.B, w.H, w.T, w.d // w.group), dtype=torch.float16, device=dev)
     xhat = torch.empty_like(xd)
 
     def step(ev=None):

@@ -35,9 +35,13 @@
  *   x, x_out   fp16   [B, T, H, d]        (B tensors, e.g. layers x {K,V})
  *   signs      int8   [B, H, d]  values +1 / -1   (NULL: all +1)
  *   lambda     fp32   [B, H, d]  finite, > 0      (NULL: all 1)
- *   codes      uint8  [B, T, H, d*bits/8]
- *   scales     fp16   [B, T, H, d/group]
+ *   codes      uint8  [B, H, T, d*bits/8]   head-major quantized cache
+ *   scales     fp16   [B, H, T, d/group]   head-major quantized cache
  *   y          fp32   [B, T, H, d]   (rotate / unrotate only)
+ * The quantized cache is head-major: vector (b, t, h) of x is row
+ * (b*H + h)*T + t of codes and scales, so each head's tokens are one
+ * contiguous run (the order in which attention reads a per-head cache; the
+ * pages fix no layout).
  *
  * Ownership and threading: every buffer belongs to the caller; the library
  * allocates nothing on the device, keeps no per-call state and may be called
@@ -110,8 +114,8 @@ size_t srftq_scales_count(const srftq_shape* shape);
  *   x       in   fp16 [B,T,H,d], 16-B aligned
  *   signs   in   int8 [B,H,d] or NULL
  *   lambda  in   fp32 [B,H,d] or NULL
- *   codes   out  uint8 [B,T,H,d*bits/8], 16-B aligned
- *   scales  out  fp16 [B,T,H,d/group], 16-B aligned
+ *   codes   out  uint8 [B,H,T,d*bits/8], 16-B aligned
+ *   scales  out  fp16 [B,H,T,d/group], 16-B aligned
  */
 srftq_status srftq_quantize(const srftq_shape* shape, const uint16_t* x,
                             const int8_t* signs, const float* lambda,
@@ -120,7 +124,7 @@ srftq_status srftq_quantize(const srftq_shape* shape, const uint16_t* x,
 /*
  * Dequantize + unrotate (the inverse read path, "rotation and de-rotation"
  * in the pages' problem statement).
- *   codes, scales  in   as written by srftq_quantize (16-B aligned)
+ *   codes, scales  in   [B,H,T,.] as written by srftq_quantize (16-B aligned)
  *   signs, lambda  in   the same ones used to quantize (or NULL)
  *   x_out          out  fp16 [B,T,H,d], 16-B aligned
  */

@@ -61,10 +61,16 @@ struct Cursor {
   }
 };
 
-// Row offset (in elements of d) of token t of head bh: ((b*T + t)*H + h).
+// Row of token t of head bh in x [B,T,H,D]: ((b*T + t)*H + h).
 __device__ __forceinline__ int64_t row_index(const Geo& a, int bh, int64_t t) {
   const int b = bh / a.H, h = bh - b * a.H;
   return ((int64_t)b * a.T + t) * a.H + h;
+}
+
+// Row of token t of head bh in the head-major quantized cache [B,H,T,.]:
+// a tile's 64 code and scale rows are one contiguous run.
+__device__ __forceinline__ int64_t cache_row(const Geo& a, int bh, int64_t t) {
+  return (int64_t)bh * a.T + t;
 }
 
 // ----------------------------------------------------------------------------
@@ -236,7 +242,7 @@ __device__ __forceinline__ void load_scales(const uint8_t* src, uint32_t (&s)[Sc
 }
 
 // ----------------------------------------------------------------------------
-// Quantize: fp16 [B,T,H,D] -> codes + fp16 scales.
+// Quantize: fp16 [B,T,H,D] -> codes + fp16 scales, head-major [B,H,T,.].
 //
 // Loop per tile: wait for the tile's LDS-DMA (not for the previous tile's
 // stores), read the own row from LDS, issue the next tile's DMA, transform +
@@ -305,10 +311,9 @@ __global__ __launch_bounds__(64) SRFTQ_QUANT_OCC void quantize_kernel(const uint
     quantize_tail<D, G, BITS, ROT, VAR, LAM>(y, lam_lds + cb * D, codes, scales);
 
     if (lane < nv_now) {
-      const int64_t r0 = row_index(a, now.bh, (int64_t)now.k * 64);   // uniform
-      const uint32_t dr = (uint32_t)lane * (uint32_t)a.H;
-      store_words<NCW>(codes_out + r0 * CB + dr * CB, codes);
-      store_scales<D, G>((uint8_t*)scales_out + r0 * SB + dr * SB, scales);
+      const int64_t r0 = cache_row(a, now.bh, (int64_t)now.k * 64);   // uniform
+      store_words<NCW>(codes_out + r0 * CB + (uint32_t)lane * CB, codes);
+      store_scales<D, G>((uint8_t*)scales_out + r0 * SB + (uint32_t)lane * SB, scales);
     }
     return nv_now == 64;
   };
@@ -331,7 +336,7 @@ __global__ __launch_bounds__(64) SRFTQ_QUANT_OCC void quantize_kernel(const uint
 }
 
 // ----------------------------------------------------------------------------
-// Dequantize: codes + scales -> fp16 [B,T,H,D].  Codes, scales and lambda
+// Dequantize: codes + scales [B,H,T,.] -> fp16 [B,T,H,D].  Codes, scales and lambda
 // arrive by coalesced LDS-DMA (prefetched one tile ahead); output rows are
 // staged through LDS half a row at a time and leave as 1 KiB coalesced
 // stores.
@@ -359,7 +364,7 @@ __global__ __launch_bounds__(64) SRFTQ_DEQUANT_OCC void dequantize_kernel(const 
   const int lane = threadIdx.x;
   const int stride = gridDim.x;
   if ((int)blockIdx.x >= a.n_tiles) return;
-  const uint32_t rsb_c = (uint32_t)a.H * CB, rsb_s = (uint32_t)a.H * SB;
+  const uint32_t rsb_c = CB, rsb_s = SB;   // cache rows are contiguous
   const uint32_t rsb_x = (uint32_t)a.H * (uint32_t)(2 * D);
   typename CT::Plan cplan;
   cplan.init(lane, rsb_c);
@@ -384,7 +389,7 @@ __global__ __launch_bounds__(64) SRFTQ_DEQUANT_OCC void dequantize_kernel(const 
     const int64_t t0 = (int64_t)c.k * 64;
     const int64_t left = a.T - t0;
     nv = left < 64 ? (int)left : 64;
-    const int64_t r0 = row_index(a, c.bh, t0);
+    const int64_t r0 = cache_row(a, c.bh, t0);
     CT::issue(codes_in + r0 * CB, rsb_c, nv, lane, cplan, ctile);
     ST::issue((const uint8_t*)scales_in + r0 * SB, rsb_s, nv, lane, splan, stile);
     if constexpr (LAM) issue_row_f32<D>(lambda + (int64_t)c.bh * D, lane, (uint8_t*)(lam_lds + buf * D));

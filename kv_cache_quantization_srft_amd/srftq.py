@@ -167,19 +167,38 @@ def _req(t, dtype, name):
     return t
 
 
+def _cache_lead(x):
+    """Leading dims of the head-major cache for x [B,T,H,d] / [T,H,d]."""
+    if x.dim() == 4:
+        B, T, H, _ = x.shape
+        return (B, H, T)
+    T, H, _ = x.shape
+    return (H, T)
+
+
+def _out(t, shape, dtype, device, name):
+    import torch
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    _req(t, dtype, name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
 def quantize(x, signs=None, lam=None, group=16, bits=4, rot="srft", variant="default",
              codes=None, scales=None, stream=None):
-    """x fp16 [B,T,H,d] or [T,H,d] -> (codes uint8 [...,d*bits/8], scales fp16 [...,d/group])."""
+    """x fp16 [B,T,H,d] (or [T,H,d]) -> (codes uint8 [B,H,T,d*bits/8],
+    scales fp16 [B,H,T,d/group]) in the head-major cache layout ([H,T,.]
+    for 3-D x)."""
     import torch
     B, T, H, d = _dims(x)
     _req(x, torch.float16, "x")
     _req(signs, torch.int8, "signs")
     _req(lam, torch.float32, "lambda")
-    lead = tuple(x.shape[:-1])
-    if codes is None:
-        codes = torch.empty(lead + (d * bits // 8,), dtype=torch.uint8, device=x.device)
-    if scales is None:
-        scales = torch.empty(lead + (d // group,), dtype=torch.float16, device=x.device)
+    lead = _cache_lead(x)
+    codes = _out(codes, lead + (d * bits // 8,), torch.uint8, x.device, "codes")
+    scales = _out(scales, lead + (max(d // max(group, 1), 1),), torch.float16, x.device, "scales")
     sh = make_shape(B, T, H, d, group, bits, rot, variant)
     _check(srftq_quantize(sh, x, signs, lam, codes, scales, stream), "srftq_quantize")
     return codes, scales
@@ -187,7 +206,8 @@ def quantize(x, signs=None, lam=None, group=16, bits=4, rot="srft", variant="def
 
 def dequantize(codes, scales, signs=None, lam=None, group=16, bits=4, rot="srft", variant="default",
                d=None, out=None, stream=None):
-    """codes + scales -> fp16 [...,d]."""
+    """codes + scales, head-major [B,H,T,.] (or [H,T,.]) -> fp16 [B,T,H,d]
+    (or [T,H,d])."""
     import torch
     _req(codes, torch.uint8, "codes")
     _req(scales, torch.float16, "scales")
@@ -195,15 +215,15 @@ def dequantize(codes, scales, signs=None, lam=None, group=16, bits=4, rot="srft"
     _req(lam, torch.float32, "lambda")
     if d is None:
         d = codes.shape[-1] * 8 // bits
-    lead = tuple(codes.shape[:-1])
     if codes.dim() == 3:
-        B, T, H = (1,) + lead
+        H, T = codes.shape[:2]
+        B, oshape = 1, (T, H, d)
     elif codes.dim() == 4:
-        B, T, H = lead
+        B, H, T = codes.shape[:3]
+        oshape = (B, T, H, d)
     else:
-        raise ValueError("codes must be [T,H,*] or [B,T,H,*]")
-    if out is None:
-        out = torch.empty(lead + (d,), dtype=torch.float16, device=codes.device)
+        raise ValueError("codes must be [H,T,*] or [B,H,T,*]")
+    out = _out(out, oshape, torch.float16, codes.device, "out")
     sh = make_shape(B, T, H, d, group, bits, rot, variant)
     _check(srftq_dequantize(sh, codes, scales, signs, lam, out, stream), "srftq_dequantize")
     return out

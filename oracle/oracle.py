@@ -119,31 +119,33 @@ def unrotate(y, signs=None, rot="srft") -> np.ndarray:
 
 
 def quantize(x16, signs=None, lam=None, group=16, bits=4, rot="srft", return_z=False):
-    """Return (codes uint8, scales fp16-bits uint16[, z fp32])."""
+    """Return (codes uint8, scales fp16-bits uint16[, z fp32]) in the
+    head-major cache layout: [B, H, T, .] for x [B, T, H, d] ([H, T, .] for
+    3-D x [T, H, d])."""
     x, B, T, H, d = _as4(_bits(x16))
     s = _signs(signs, B, H, d)
     l = _lam(lam, B, H, d)
-    codes = np.empty((B, T, H, d * bits // 8), dtype=np.uint8)
-    scales = np.empty((B, T, H, d // group), dtype=np.uint16)
-    z = np.empty((B, T, H, d), dtype=np.float32) if return_z else None
+    codes = np.empty((B, H, T, d * bits // 8), dtype=np.uint8)
+    scales = np.empty((B, H, T, d // group), dtype=np.uint16)
+    z = np.empty((B, H, T, d), dtype=np.float32) if return_z else None
     _check(lib().oracle_quantize(B, T, H, d, group, bits, ROT[rot], _ptr(x), _ptr(s), _ptr(l),
                                  _ptr(codes), _ptr(scales), _ptr(z)), "quantize")
-    lead = x16.shape[:-1]
-    out = (codes.reshape(*lead, -1), scales.reshape(*lead, -1))
-    if return_z:
-        out = out + (z.reshape(x16.shape),)
+    out = (codes, scales) + ((z,) if return_z else ())
+    if x16.ndim == 3:
+        out = tuple(a[0] for a in out)
     return out
 
 
 def dequantize(codes, scales, signs=None, lam=None, group=16, bits=4, rot="srft", d=None,
                return_f64=False):
-    """Return fp16 bits (uint16) of the reconstruction (and fp64 values)."""
+    """codes [B, H, T, .] (or [H, T, .]) -> fp16 bits (uint16) of the
+    reconstruction [B, T, H, d] (or [T, H, d]), and its fp64 values."""
     codes = np.ascontiguousarray(codes, dtype=np.uint8)
     scales = np.ascontiguousarray(scales, dtype=np.uint16)
     if d is None:
         d = codes.shape[-1] * 8 // bits
     c4 = codes if codes.ndim == 4 else codes[None]
-    B, T, H = c4.shape[:3]
+    B, H, T = c4.shape[:3]
     s = _signs(signs, B, H, d)
     l = _lam(lam, B, H, d)
     x = np.empty((B, T, H, d), dtype=np.uint16)
@@ -151,10 +153,10 @@ def dequantize(codes, scales, signs=None, lam=None, group=16, bits=4, rot="srft"
     _check(lib().oracle_dequantize(B, T, H, d, group, bits, ROT[rot], _ptr(c4),
                                    _ptr(scales), _ptr(s), _ptr(l), _ptr(x), _ptr(x64)),
            "dequantize")
-    lead = codes.shape[:-1]
-    if return_f64:
-        return x.reshape(*lead, d), x64.reshape(*lead, d)
-    return x.reshape(*lead, d)
+    if codes.ndim == 3:
+        x = x[0]
+        x64 = None if x64 is None else x64[0]
+    return (x, x64) if return_f64 else x
 
 
 def calibrate_lambda(x16, signs=None, rot="srft") -> np.ndarray:

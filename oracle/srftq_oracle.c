@@ -42,13 +42,16 @@
  *   - int4 nibbles are two's complement, even coordinate in the low nibble.
  *   - signs == NULL means s = +1; lambda == NULL means lambda = 1.
  *
- * Layouts (all row-major, contiguous):
+ * Layouts (all row-major, contiguous).  The quantized cache is stored
+ * head-major (the pages fix no layout): vector (b, t, h) of x is row
+ * (b*H + h)*T + t of codes and scales.
  *   x, x_out   fp16 bits  [B, T, H, d]
  *   y          fp64       [B, T, H, d]
  *   signs      int8 +-1   [B, H, d]
  *   lambda     fp32       [B, H, d]
- *   codes      uint8      [B, T, H, d*bits/8]
- *   scales     fp16 bits  [B, T, H, d/group]
+ *   codes      uint8      [B, H, T, d*bits/8]
+ *   scales     fp16 bits  [B, H, T, d/group]
+ *   z_out      fp32       [B, H, T, d]   (rows aligned with codes)
  */
 #include <math.h>
 #include <stdint.h>
@@ -308,8 +311,14 @@ static int check_quant(int d, int group, int bits)
     return 0;
 }
 
+/* Row of vector (b, t, h) in the head-major quantized cache. */
+static size_t cache_row(int64_t b, int64_t t, int h, int64_t T, int H)
+{
+    return ((size_t)b * (size_t)H + (size_t)h) * (size_t)T + (size_t)t;
+}
+
 /*
- * Quantize every vector.  z_out (optional, fp32 [B,T,H,d]) receives the fp32
+ * Quantize every vector.  z_out (optional, fp32 [B,H,T,d]) receives the fp32
  * values the decision was taken on.
  */
 int oracle_quantize(int64_t B, int64_t T, int H, int d, int group, int bits,
@@ -340,6 +349,7 @@ int oracle_quantize(int64_t B, int64_t T, int H, int d, int group, int bits,
         for (int64_t v = 0; v < nvec; ++v) {
             int h = (int)(v % H);
             int64_t b = v / (T * H);
+            size_t c = cache_row(b, (v / H) % T, h, T, H);
             for (int j = 0; j < d; ++j)
                 xs[j] = sign_of(signs, b, H, h, d, j) *
                         oracle_f16_to_f64(x[(size_t)v * d + j]);
@@ -360,7 +370,7 @@ int oracle_quantize(int64_t B, int64_t T, int H, int d, int group, int bits,
                     t = 65504.0f;
                 uint16_t sh = oracle_f64_to_f16((double)t);
                 float sg = (float)oracle_f16_to_f64(sh);
-                scales[(size_t)v * ng + g] = sh;
+                scales[c * ng + g] = sh;
                 /* fp32 reciprocal of the stored scale, correctly rounded:
                  * the double quotient is exact to 2^-53 and 1/sigma never
                  * sits within 2^-36 of an fp32 midpoint, so one rounding
@@ -380,7 +390,7 @@ int oracle_quantize(int64_t B, int64_t T, int H, int d, int group, int bits,
                     }
                 }
             }
-            uint8_t *row = codes + (size_t)v * code_row;
+            uint8_t *row = codes + c * code_row;
             if (bits == 8) {
                 for (int j = 0; j < d; ++j)
                     row[j] = (uint8_t)(int8_t)q[j];
@@ -389,7 +399,7 @@ int oracle_quantize(int64_t B, int64_t T, int H, int d, int group, int bits,
                     row[i] = (uint8_t)((q[2 * i] & 0xF) | ((q[2 * i + 1] & 0xF) << 4));
             }
             if (z_out)
-                memcpy(z_out + (size_t)v * d, z, sizeof(float) * (size_t)d);
+                memcpy(z_out + c * d, z, sizeof(float) * (size_t)d);
         }
         free(xs);
         free(y);
@@ -430,7 +440,8 @@ int oracle_dequantize(int64_t B, int64_t T, int H, int d, int group, int bits,
         for (int64_t v = 0; v < nvec; ++v) {
             int h = (int)(v % H);
             int64_t b = v / (T * H);
-            const uint8_t *row = codes + (size_t)v * code_row;
+            size_t c = cache_row(b, (v / H) % T, h, T, H);
+            const uint8_t *row = codes + c * code_row;
             for (int j = 0; j < d; ++j) {
                 int qj;
                 if (bits == 8) {
@@ -439,7 +450,7 @@ int oracle_dequantize(int64_t B, int64_t T, int H, int d, int group, int bits,
                     int nib = (row[j / 2] >> (4 * (j % 2))) & 0xF;
                     qj = nib >= 8 ? nib - 16 : nib;    /* sign-extend */
                 }
-                double sg = oracle_f16_to_f64(scales[(size_t)v * ng + j / group]);
+                double sg = oracle_f16_to_f64(scales[c * ng + j / group]);
                 double lam = lambda ? (double)lambda[((size_t)b * H + h) * d + j] : 1.0;
                 yh[j] = (double)qj * sg / lam;
             }

@@ -91,7 +91,7 @@ def test_no_signs_means_plus_one():
 def test_empty_tokens_no_op():
     x = torch.zeros((0, 8, 128), dtype=torch.float16, device="cuda")
     codes, scales = S.quantize(x)
-    assert codes.shape == (0, 8, 64) and scales.shape == (0, 8, 8)
+    assert codes.shape == (8, 0, 64) and scales.shape == (8, 0, 8)     # head-major [H, T, .]
 
 
 def test_constructed_ties_exact():
@@ -197,8 +197,9 @@ def _check_sampled(x, s, lam, codes_g, scales_g, xhat_g, w, rot, n=1536):
     xs = x[b, t, h][None, None]                     # [1, 1, n, d]
     ss = s[b, h][None]                              # [1, n, d]
     ls = None if lam is None else lam[b, h][None]
-    cg = host(codes_g[b, t, h])[None, None]
-    sg = host(scales_g[b, t, h]).view(np.uint16)[None, None]
+    # the oracle's sample is B=1, H=n, T=1: its head-major cache is [1, n, 1, .]
+    cg = host(codes_g[b, h, t])[None, :, None]
+    sg = host(scales_g[b, h, t]).view(np.uint16)[None, :, None]
     co, so, zo = oracle.quantize(xs, ss, ls, w.group, w.bits, rot, return_z=True)
     st = compare.check_quantize(cg, sg, co, so, zo, w.bits, w.group, d)
     xo = oracle.dequantize(cg, sg, ss, ls, w.group, w.bits, rot, d=d)

@@ -243,7 +243,8 @@ def test_quantizer_invariants(rot, bits, group):
     # z is the fp32 rounding of lambda * y (the decision input)
     y = oracle.rotate(x, s, rot)
     zref = (lam[:, None].astype(np.float64) * y).astype(np.float32)
-    assert np.array_equal(z, zref)
+    # codes, scales and z are head-major [B, H, T, .]; y is [B, T, H, d]
+    assert np.array_equal(z, zref.transpose(0, 2, 1, 3))
     zg = _groups(z.astype(np.float64), group)
     qg = _groups(q, group)
     a = np.max(np.abs(zg), axis=-1)
@@ -317,10 +318,10 @@ def test_dequantize_rot_none_closed_form(bits):
     s = _rand_signs(rng, 1, 3, d)
     codes, scales = oracle.quantize(x, s, None, g, bits, "none")
     out = oracle.dequantize(codes, scales, s, None, g, bits, "none", d=d)
-    q = decode_codes(codes, bits, d).astype(np.float64)
+    q = decode_codes(codes, bits, d).astype(np.float64)                 # [B, H, T, d]
     sig = np.repeat(scales.view(np.float16).astype(np.float64), g, axis=-1)
-    ref = (s[:, None] * q * sig).astype(np.float16).view(np.uint16)
-    assert np.array_equal(out, ref)
+    ref = (s[:, :, None] * q * sig).transpose(0, 2, 1, 3)               # -> [B, T, H, d]
+    assert np.array_equal(out, ref.astype(np.float16).view(np.uint16))
 
 
 @pytest.mark.parametrize("rot", ["srft", "srht"])
@@ -336,7 +337,8 @@ def test_roundtrip_error_identity_and_bound(rot):
     _, x64 = oracle.dequantize(codes, scales, s, lam, g, bits, rot, d=d, return_f64=True)
     q = decode_codes(codes, bits, d).astype(np.float64)
     sig = np.repeat(scales.view(np.float16).astype(np.float64), g, axis=-1)
-    yhat = q * sig / lam[:, None]
+    yhat = (q * sig / lam[:, :, None]).transpose(0, 2, 1, 3)           # [B, T, H, d]
+    sig = sig.transpose(0, 2, 1, 3)
     y = oracle.rotate(x, s, rot)
     e_x = np.linalg.norm(x64 - x.astype(np.float64), axis=-1)
     e_y = np.linalg.norm(yhat - y, axis=-1)
