@@ -1,9 +1,11 @@
 // kernels.h -- libsrftq kernels for gfx950, one KV vector per lane.
 //
 // Work decomposition: a tile is 64 consecutive tokens of one (tensor, head)
-// pair, so the head's signs and lambda row are wave-uniform (scalar loads,
-// SGPR operands).  Tiles are numbered token-chunk-major, head-minor, so the
-// waves resident at any moment cover adjacent rows of the [B,T,H,d] tensors.
+// pair, so the head's signs and lambda row are wave-uniform: they arrive by
+// LDS-DMA with the tile, the signs are expanded lane-parallel into one XOR
+// mask per packed fp16 pair, and both are read back as LDS broadcasts.
+// Tiles are numbered token-chunk-major, head-minor, so the waves resident at
+// any moment cover adjacent rows of the [B,T,H,d] tensors.
 // Each block is one wave; the grid is persistent (about the number of
 // resident waves) and walks the tiles with a fixed stride.
 //
@@ -181,6 +183,14 @@ __device__ __forceinline__ void issue_row_f32(const float* src, int lane, uint8_
   if (lane < D / 4) dma_to_lds<16>(src, 16u * (uint32_t)lane, lds_addr(lds));
 }
 
+// A head's D int8 signs fetched by LDS-DMA: lane l < D/2 moves bytes 2l, 2l+1
+// into the low half of LDS dword l (a sub-dword DMA fills one 4-byte slot
+// per lane).  The kernel turns slot l into sign mask l in place.
+template <int D>
+__device__ __forceinline__ void issue_signs(const int8_t* row, int lane, uint32_t* lds) {
+  if (lane < D / 2) dma_to_lds<2>(row, 2u * (uint32_t)lane, lds_addr(lds));
+}
+
 // Number of global store instructions store_words<N> / store_scales issue.
 template <int N>
 constexpr int store_count() {
@@ -264,6 +274,7 @@ __global__ __launch_bounds__(64) SRFTQ_QUANT_OCC void quantize_kernel(const uint
   constexpr int NST = store_count<NCW>() + 1;   // global stores per tile
   __shared__ __attribute__((aligned(16))) uint8_t lds[XT::kBytes];
   __shared__ __attribute__((aligned(16))) float lam_lds[LAM ? 2 * D : 4];
+  __shared__ __attribute__((aligned(16))) uint32_t smask[2 * 64];   // sign masks, double-buffered
 
   const int lane = threadIdx.x;
   const int stride = gridDim.x;
@@ -283,6 +294,7 @@ __global__ __launch_bounds__(64) SRFTQ_QUANT_OCC void quantize_kernel(const uint
     nv = left < 64 ? (int)left : 64;
     XT::issue((const uint8_t*)x + row_index(a, c.bh, t0) * (int64_t)(2 * D), rsb, nv, lane, plan, lds);
     if constexpr (LAM) issue_row_f32<D>(lambda + (int64_t)c.bh * D, lane, (uint8_t*)(lam_lds + buf * D));
+    issue_signs<D>(signs + (int64_t)c.bh * a.sign_stride, lane, smask + buf * 64);
   };
 
   int nv, buf = 0;
@@ -293,19 +305,21 @@ __global__ __launch_bounds__(64) SRFTQ_QUANT_OCC void quantize_kernel(const uint
     wave_fence();
     uint32_t w[D / 2];
     XT::read_row(lds, lane, w);
+    const int cb = buf;
+    const uint32_t su = smask[cb * 64 + lane];
     wait_lgkm0();   // the reads are done before the next DMA reuses the tile
 
     const Cursor now = cur;
-    const int nv_now = nv, cb = buf;
+    const int nv_now = nv;
     if (remaining > 0) {
       cur.advance(dk, dbh, a.BH);
       buf ^= 1;
       issue(cur, nv, buf);
     }
 
-    const HeadSigns sg(signs + (int64_t)now.bh * a.sign_stride);
+    smask[cb * 64 + lane] = sign_mask_of(su);   // in order before the broadcast reads
     float y[D];
-    forward<D, ROT, VAR>(w, sg, y);
+    forward<D, ROT, VAR>(w, LdsSigns{smask + cb * 64}, y);
     uint32_t codes[NCW];
     uint32_t scales[NSW];
     quantize_tail<D, G, BITS, ROT, VAR, LAM>(y, lam_lds + cb * D, codes, scales);
@@ -360,6 +374,7 @@ __global__ __launch_bounds__(64) SRFTQ_DEQUANT_OCC void dequantize_kernel(const 
   __shared__ __attribute__((aligned(16))) uint8_t stile[ST::kBytes < 16 ? 16 : ST::kBytes];
   __shared__ __attribute__((aligned(16))) uint8_t otile[OT::kBytes];
   __shared__ __attribute__((aligned(16))) float lam_lds[LAM ? 2 * D : 4];
+  __shared__ __attribute__((aligned(16))) uint32_t smask[2 * 64];   // sign masks, double-buffered
 
   const int lane = threadIdx.x;
   const int stride = gridDim.x;
@@ -393,6 +408,7 @@ __global__ __launch_bounds__(64) SRFTQ_DEQUANT_OCC void dequantize_kernel(const 
     CT::issue(codes_in + r0 * CB, rsb_c, nv, lane, cplan, ctile);
     ST::issue((const uint8_t*)scales_in + r0 * SB, rsb_s, nv, lane, splan, stile);
     if constexpr (LAM) issue_row_f32<D>(lambda + (int64_t)c.bh * D, lane, (uint8_t*)(lam_lds + buf * D));
+    issue_signs<D>(signs + (int64_t)c.bh * a.sign_stride, lane, smask + buf * 64);
   };
 
   int nv, buf = 0;
@@ -404,6 +420,7 @@ __global__ __launch_bounds__(64) SRFTQ_DEQUANT_OCC void dequantize_kernel(const 
     CT::read_row(ctile, lane, cw);
     ST::read_row(stile, lane, sw);
     const int cb = buf;
+    smask[cb * 64 + lane] = sign_mask_of(smask[cb * 64 + lane]);
     if constexpr (LAM) {
       // e_j / lambda_j, computed lane-parallel in place, read back broadcast
       float* lt = lam_lds + cb * D;
@@ -429,11 +446,15 @@ __global__ __launch_bounds__(64) SRFTQ_DEQUANT_OCC void dequantize_kernel(const 
     inverse<D, ROT, VAR>(y, xr);
 
     // fp16 RNE, then the sign multiply as an XOR on the packed halves
-    const HeadSigns sg(signs + (int64_t)now.bh * a.sign_stride);
+    const LdsSigns sg{smask + cb * 64};
     uint32_t o[D / 2];
-    static_for<D / 2>([&](auto mm) {
-      constexpr int m = decltype(mm)::value;
-      o[m] = pack_f16x2(xr[2 * m], xr[2 * m + 1]) ^ sg.mask(m);
+    static_for<D / 8>([&](auto qq) {
+      constexpr int q = decltype(qq)::value;
+      const uint4 m4 = sg.mask4(q);
+      o[4 * q + 0] = pack_f16x2(xr[8 * q + 0], xr[8 * q + 1]) ^ m4.x;
+      o[4 * q + 1] = pack_f16x2(xr[8 * q + 2], xr[8 * q + 3]) ^ m4.y;
+      o[4 * q + 2] = pack_f16x2(xr[8 * q + 4], xr[8 * q + 5]) ^ m4.z;
+      o[4 * q + 3] = pack_f16x2(xr[8 * q + 6], xr[8 * q + 7]) ^ m4.w;
     });
 
     uint8_t* obase = (uint8_t*)x_out + row_index(a, now.bh, (int64_t)now.k * 64) * (int64_t)(2 * D);

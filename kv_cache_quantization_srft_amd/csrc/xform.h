@@ -50,42 +50,72 @@ struct Scales {
   static constexpr bool is_edge(int j) { return kEdges && (j == 0 || j == D / 2); }
 };
 
-// Signs of one head: int8 +-1, read as 4-byte words through scalar loads
-// (the row pointer is wave-uniform and 4-byte aligned).
+// Sign sources.  mask(m) is the XOR mask that flips the fp16 sign bits of
+// elements 2m and 2m+1 where s = -1 (bit 15 and bit 31); mask4(q) returns
+// masks 4q .. 4q+3.
+//
+// HeadSigns: the int8 +-1 row read as 4-byte words through scalar loads
+// (wave-uniform, 4-byte aligned row pointer); masks built on the scalar unit.
 struct HeadSigns {
   const_ptr<uint32_t> p;
   __device__ __forceinline__ explicit HeadSigns(const int8_t* row)
       : p(as_const((const uint32_t*)row)) {}
   // bit 7 of sign byte j
   __device__ __forceinline__ uint32_t sbit(int j) const { return (p[j >> 2] >> (8 * (j & 3) + 7)) & 1u; }
-  // XOR mask flipping the fp16 sign bits of elements 2m, 2m+1.
   __device__ __forceinline__ uint32_t mask(int m) const {
     uint32_t v = (sbit(2 * m) << 15) | (sbit(2 * m + 1) << 31);
     asm("" : "+s"(v));   // keep the mask whole in an SGPR: one v_xor per use
     return v;
   }
-  // +-1.0f for element j.
-  __device__ __forceinline__ float f(int j) const { return as_f32(0x3f800000u | (sbit(j) << 31)); }
+  __device__ __forceinline__ uint4 mask4(int q) const {
+    return make_uint4(mask(4 * q), mask(4 * q + 1), mask(4 * q + 2), mask(4 * q + 3));
+  }
 };
+
+// LdsSigns: the masks of one head already expanded in LDS (D/2 dwords,
+// built lane-parallel by the streaming kernels); every lane reads the same
+// address, so each ds_read_b128 is a broadcast.
+struct LdsSigns {
+  const uint32_t* row;
+  __device__ __forceinline__ uint32_t mask(int m) const { return row[m]; }
+  __device__ __forceinline__ uint4 mask4(int q) const { return *(const uint4*)(row + 4 * q); }
+};
+
+// Mask of elements 2m, 2m+1 from their two sign bytes (low 16 bits of u):
+// bit 7 of each byte is set exactly for -1.
+__device__ __forceinline__ uint32_t sign_mask_of(uint32_t u) {
+  return ((u & 0x80u) << 8) | ((u & 0x8000u) << 16);
+}
 
 // ----------------------------------------------------------------------------
 // Pass 1 from fp16: s (.) x, converted, and the pair sums of elements r and
 // r + d/2:  p0[r] = x'_r + x'_{r+d/2},  p1[r] = x'_r - x'_{r+d/2}.
 // Every rotation starts with exactly these (radix-2 split on the top index
-// bit); each is one v_fma_mix_f32 from the packed halves.
+// bit); the sign multiply is one XOR per packed pair and each sum one
+// v_fma_mix_f32 from the packed halves.
 // ----------------------------------------------------------------------------
-template <int D>
-__device__ __forceinline__ void pair_sums(const uint32_t (&w)[D / 2], const HeadSigns& sg,
+template <int D, class S>
+__device__ __forceinline__ void pair_sums(const uint32_t (&w)[D / 2], const S& sg,
                                           float (&p0)[D / 2], float (&p1)[D / 2]) {
-  static_for<D / 4>([&](auto mm) {
-    constexpr int m = decltype(mm)::value;
-    const uint32_t wa = w[m] ^ sg.mask(m);       // elements 2m, 2m+1 (signed)
-    const uint32_t wb = w[D / 4 + m];            // elements d/2+2m, d/2+2m+1
-    const float s0 = sg.f(D / 2 + 2 * m), s1 = sg.f(D / 2 + 2 * m + 1);
-    p0[2 * m] = __builtin_fmaf(hlo(wb), s0, hlo(wa));
-    p1[2 * m] = __builtin_fmaf(hlo(wb), -s0, hlo(wa));
-    p0[2 * m + 1] = __builtin_fmaf(hhi(wb), s1, hhi(wa));
-    p1[2 * m + 1] = __builtin_fmaf(hhi(wb), -s1, hhi(wa));
+  static_assert(D % 16 == 0, "pair_sums reads masks four at a time");
+  // an opaque 1.0 keeps the sums as fma_mix (fp16 sources, fp32 result)
+  float one = 1.0f;
+  asm("" : "+s"(one));
+  static_for<D / 16>([&](auto qq) {
+    constexpr int q = decltype(qq)::value;
+    const uint4 ma4 = sg.mask4(q), mb4 = sg.mask4(D / 16 + q);
+    const uint32_t ma[4] = {ma4.x, ma4.y, ma4.z, ma4.w};
+    const uint32_t mb[4] = {mb4.x, mb4.y, mb4.z, mb4.w};
+    static_for<4>([&](auto ii) {
+      constexpr int i = decltype(ii)::value;
+      constexpr int m = 4 * q + i;
+      const uint32_t wa = w[m] ^ ma[i];              // elements 2m, 2m+1
+      const uint32_t wb = w[D / 4 + m] ^ mb[i];      // elements d/2+2m, d/2+2m+1
+      p0[2 * m] = __builtin_fmaf(hlo(wb), one, hlo(wa));
+      p1[2 * m] = __builtin_fmaf(hlo(wb), -one, hlo(wa));
+      p0[2 * m + 1] = __builtin_fmaf(hhi(wb), one, hhi(wa));
+      p1[2 * m + 1] = __builtin_fmaf(hhi(wb), -one, hhi(wa));
+    });
   });
 }
 
@@ -236,8 +266,8 @@ __device__ __forceinline__ void wht(float (&v)[M]) {
 // Forward rotation of one vector given as D/2 packed fp16 dwords.  Output y
 // is in packed order and unscaled (multiply by Scales<>::kFwd*).
 // ----------------------------------------------------------------------------
-template <int D, int ROT, int VAR>
-__device__ __forceinline__ void forward(const uint32_t (&w)[D / 2], const HeadSigns& sg, float (&y)[D]) {
+template <int D, int ROT, int VAR, class S>
+__device__ __forceinline__ void forward(const uint32_t (&w)[D / 2], const S& sg, float (&y)[D]) {
   if constexpr (ROT == ROT_NONE) {
     static_for<D / 2>([&](auto mm) {
       constexpr int m = decltype(mm)::value;
