@@ -84,8 +84,11 @@ def cpu_baseline(w, x, s, lam, target_s: float = 15.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-s", type=float, default=1.0,
+                    help="untimed steps for this long before the warmup steps, so the timed "
+                         "steps run at the clocks a sustained load settles to")
     ap.add_argument("--workload", default="outlier")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -127,6 +130,15 @@ def main():
         if ev is not None:
             ev[2].record()
 
+    # the GPU's clocks need a sustained load to settle (the first ~100 calls of
+    # a kernel run up to 15 % slower): untimed steps for settle_s seconds
+    t_settle = time.perf_counter()
+    n_settle = 0
+    while time.perf_counter() - t_settle < args.settle_s:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+        n_settle += 10
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -196,6 +208,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_steps": n_settle,
         "ms_per_step": ms_step,
         "higher_is_better": True,
         "scaling": "weak",

@@ -29,10 +29,17 @@
 
 namespace srftq {
 
-// Byte k of a dword as fp32 (v_cvt_f32_ubyteK).
+// Byte K of a dword as fp32: one v_cvt_f32_ubyteK (register-only asm; the
+// compiler would otherwise extract the byte first when it knows the upper
+// bits of each byte are clear).
 template <int K>
 __device__ __forceinline__ float ubyte_f32(uint32_t v) {
-  return (float)((v >> (8 * K)) & 0xffu);
+  float r;
+  if constexpr (K == 0) asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(r) : "v"(v));
+  else if constexpr (K == 1) asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(r) : "v"(v));
+  else if constexpr (K == 2) asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(r) : "v"(v));
+  else asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(r) : "v"(v));
+  return r;
 }
 
 template <int BITS>
@@ -101,9 +108,32 @@ __device__ __forceinline__ void quantize_tail(float (&y)[D], const float* __rest
   constexpr float cE = (float)Sc::kFwdEdge;
 
   if constexpr (LAM) {
-    static_for<D>([&](auto jj) {
-      constexpr int j = decltype(jj)::value;
-      y[j] = y[j] * lam[j];
+    // z = lambda * y group by group; the next group's lambda (LDS
+    // broadcast) is requested before this group's multiplies, so the LDS
+    // latency overlaps them instead of stalling each read.
+    static_assert(G % 4 == 0, "lambda groups are read four floats at a time");
+    float lc[G], ln[G];
+    auto fetch = [&](float (&dst)[G], int g) {
+      static_for<G / 4>([&](auto qq) {
+        constexpr int q = decltype(qq)::value;
+        const float4 v = *(const float4*)(lam + g * G + 4 * q);
+        dst[4 * q + 0] = v.x;
+        dst[4 * q + 1] = v.y;
+        dst[4 * q + 2] = v.z;
+        dst[4 * q + 3] = v.w;
+      });
+    };
+    fetch(lc, 0);
+    static_for<NG>([&](auto gg) {
+      constexpr int g = decltype(gg)::value;
+      if constexpr (g + 1 < NG) fetch(ln, g + 1);
+      static_for<G>([&](auto kk) {
+        constexpr int k = decltype(kk)::value;
+        y[g * G + k] = y[g * G + k] * lc[k];
+      });
+      if constexpr (g + 1 < NG) {
+        static_for<G>([&](auto kk) { lc[decltype(kk)::value] = ln[decltype(kk)::value]; });
+      }
     });
   }
 
