@@ -57,6 +57,58 @@ def load_traffic(kernel: str, workload: str):
     return t.get("hbm_bytes_per_launch")
 
 
+def _counter_means(csv_path: str, counter: str) -> dict:
+    """Mean counter value per dispatch, by kernel family, from a rocprofv3
+    counter_collection.csv (values summed over the counter's instances)."""
+    import csv
+    per = {}
+    with open(csv_path) as f:
+        for row in csv.DictReader(f):
+            if row.get("Counter_Name") != counter:
+                continue
+            name = row.get("Kernel_Name", "")
+            fam = ("dequantize" if "dequantize_kernel" in name else
+                   "quantize" if "quantize_kernel" in name else
+                   "copy" if "neg" in name else None)
+            if fam is None:
+                continue
+            key = (fam, row.get("Dispatch_Id"))
+            per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
+    out = {}
+    for (fam, _), v in per.items():
+        out.setdefault(fam, []).append(v)
+    return {k: sum(v) / len(v) for k, v in out.items()}
+
+
+def write_traffic(fetch_csv: str, write_csv: str, workload: str) -> None:
+    """HBM bytes per launch of each streaming kernel from two rocprofv3 runs
+    of this benchmark (--pmc FETCH_SIZE, --pmc WRITE_SIZE).  Each counter is
+    scaled by what it reads for the copy kernel of known size (torch.neg over
+    the quantize input: reads and writes exactly 2*d bytes per vector)."""
+    from kv_cache_quantization_srft_amd import workloads as W
+    w = W.WORKLOADS[workload]
+    copy_bytes = 2 * w.d * w.nvec
+    fetch = _counter_means(fetch_csv, "FETCH_SIZE")
+    write = _counter_means(write_csv, "WRITE_SIZE")
+    f_scale = copy_bytes / (fetch["copy"] * 1024.0)
+    w_scale = copy_bytes / (write["copy"] * 1024.0)
+    bpv = algorithmic_bytes_per_vector(w.d, w.group, w.bits)
+    for k in ("quantize", "dequantize"):
+        rd = fetch[k] * 1024.0 * f_scale
+        wr = write[k] * 1024.0 * w_scale
+        rec = {"kernel": k, "workload": workload, "kernel_source_hash": kernel_source_hash(),
+               "fetch_kib_per_launch": fetch[k], "write_kib_per_launch": write[k],
+               "fetch_scale": f_scale, "write_scale": w_scale,
+               "hbm_read_bytes_per_launch": rd, "hbm_write_bytes_per_launch": wr,
+               "hbm_bytes_per_launch": rd + wr,
+               "algorithmic_bytes_per_launch": bpv * w.nvec,
+               "traffic_over_algorithmic": (rd + wr) / (bpv * w.nvec)}
+        path = os.path.join(ROOT, "profiles", f"traffic_{k}_{workload}.json")
+        with open(path, "w") as f:
+            json.dump(rec, f, indent=1)
+        print(json.dumps(rec))
+
+
 def cpu_baseline(w, x, s, lam, target_s: float = 15.0):
     """The oracle, as it stands, on the first tokens of every tensor."""
     import numpy as np
@@ -91,7 +143,13 @@ def main():
                          "steps run at the clocks a sustained load settles to")
     ap.add_argument("--workload", default="outlier")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic_<kernel>_<workload>.json from two rocprofv3 "
+                         "counter_collection.csv files of this benchmark, then exit")
     args = ap.parse_args()
+    if args.traffic:
+        write_traffic(args.traffic[0], args.traffic[1], args.workload)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
