@@ -260,7 +260,7 @@ def main():
         cpu = cpu_baseline(w, x, s, lam_h)
 
     out = {
-        "metric": "KV vectors/s (quantize + dequantize), SRFT->int4 pack, d=128",
+        "metric": "KV vectors/s + fp16-in GB/s (% of HBM peak), SRFT\u2192int4 pack, d=128",
         "value": nvec / (ms_step * 1e-3),
         "unit": "KV vectors/s",
         "n_gpus": 1,
@@ -283,6 +283,9 @@ def main():
         "per_kernel": per_kernel,
         "copy_probe": copy_probe,
         "fp16_in_GBps_quantize": per_kernel["quantize"]["fp16_GBps"],
+        "hbm_peak_frac_quantize": per_kernel["quantize"]["hbm_frac"],
+        "hbm_peak_frac_dequantize": per_kernel["dequantize"]["hbm_frac"],
+        "step": "srftq_quantize then srftq_dequantize of every vector (one launch each)",
         "reconstruction_rel_l2": rel,
         "device": torch.cuda.get_device_name(0),
         "input_generation_s": gen_s,
