@@ -33,8 +33,16 @@ def sources():
     return sorted(f for f in os.listdir(CSRC) if f.endswith(".hip") or f.endswith(".cpp"))
 
 
+# Development only: a comma-separated list of name fragments (e.g. "d256")
+# whose already-built objects are linked as they are instead of recompiled.
+# Unset (the default), every unit is compiled.
+_REUSE = [f for f in os.environ.get("SRFTQ_REUSE_OBJECTS", "").split(",") if f]
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, src + ".o")
+    if any(f in src for f in _REUSE) and os.path.exists(obj):
+        return obj
     path = os.path.join(CSRC, src)
     flags = DEVICE_FLAGS if src.endswith(".hip") else HOST_FLAGS
     cmd = [HIPCC] + flags + ["-c", path, "-o", obj]
@@ -46,7 +54,8 @@ def _compile(src: str) -> str:
 
 def build(jobs: int | None = None, verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
+    # the d = 256 units take several times longer: start them first
+    srcs = sorted(sources(), key=lambda f: (0 if "d256" in f else 1, f))
     jobs = jobs or min(len(srcs), os.cpu_count() or 4, 16)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(_compile, srcs))

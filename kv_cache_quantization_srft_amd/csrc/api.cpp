@@ -48,7 +48,7 @@ bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 srftq_status validate(const srftq_shape* s) {
   if (!s) return SRFTQ_ERR_NULL;
   if (s->B < 0 || s->T < 0 || s->H < 1) return SRFTQ_ERR_SHAPE;
-  if (s->d != 64 && s->d != 128) return SRFTQ_ERR_UNSUPPORTED;
+  if (s->d != 64 && s->d != 128 && s->d != 256) return SRFTQ_ERR_UNSUPPORTED;
   if (s->bits != 4 && s->bits != 8) return SRFTQ_ERR_UNSUPPORTED;
   if (!is_pow2(s->group) || s->group < 8 || s->group > s->d) return SRFTQ_ERR_UNSUPPORTED;
   if (s->rot != SRFTQ_ROT_SRFT && s->rot != SRFTQ_ROT_SRHT && s->rot != SRFTQ_ROT_NONE)
@@ -66,19 +66,23 @@ int64_t nvec(const srftq_shape* s) { return s->B * s->T * (int64_t)s->H; }
 
 srftq_status from_hip(hipError_t e) { return e == hipSuccess ? SRFTQ_OK : SRFTQ_ERR_HIP; }
 
-const srftq::RunFn kQuantize[2][4] = {
+const srftq::RunFn kQuantize[3][4] = {
     {srftq::run_quantize_d64_r0, srftq::run_quantize_d64_r1, srftq::run_quantize_d64_r2,
      srftq::run_quantize_d64_r3},
     {srftq::run_quantize_d128_r0, srftq::run_quantize_d128_r1, srftq::run_quantize_d128_r2,
-     srftq::run_quantize_d128_r3}};
-const srftq::RunFn kDequantize[2][4] = {
+     srftq::run_quantize_d128_r3},
+    {srftq::run_quantize_d256_r0, srftq::run_quantize_d256_r1, srftq::run_quantize_d256_r2,
+     srftq::run_quantize_d256_r3}};
+const srftq::RunFn kDequantize[3][4] = {
     {srftq::run_dequantize_d64_r0, srftq::run_dequantize_d64_r1, srftq::run_dequantize_d64_r2,
      srftq::run_dequantize_d64_r3},
     {srftq::run_dequantize_d128_r0, srftq::run_dequantize_d128_r1, srftq::run_dequantize_d128_r2,
-     srftq::run_dequantize_d128_r3}};
+     srftq::run_dequantize_d128_r3},
+    {srftq::run_dequantize_d256_r0, srftq::run_dequantize_d256_r1, srftq::run_dequantize_d256_r2,
+     srftq::run_dequantize_d256_r3}};
 
-srftq::RunFn pick(const srftq::RunFn (&table)[2][4], const srftq_shape* s) {
-  const int di = s->d == 64 ? 0 : s->d == 128 ? 1 : -1;
+srftq::RunFn pick(const srftq::RunFn (&table)[3][4], const srftq_shape* s) {
+  const int di = s->d == 64 ? 0 : s->d == 128 ? 1 : s->d == 256 ? 2 : -1;
   if (di < 0) return nullptr;
   return table[di][srftq::rot_selector(*s)];
 }
@@ -150,6 +154,7 @@ static srftq_status run_misc(srftq::Op op, const srftq_shape* s, const srftq::Pt
   switch (s->d) {
     case 64: return from_hip(srftq::run_misc_d64(op, *s, p, hs));
     case 128: return from_hip(srftq::run_misc_d128(op, *s, p, hs));
+    case 256: return from_hip(srftq::run_misc_d256(op, *s, p, hs));
     default: return SRFTQ_ERR_UNSUPPORTED;
   }
 }

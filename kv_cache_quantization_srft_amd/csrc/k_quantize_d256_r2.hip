@@ -1,0 +1,5 @@
+// quantize kernels, d = 256, rotation selector 2.
+#define SRFTQ_D 256
+#define SRFTQ_PART 0
+#define SRFTQ_ROTSEL 2
+#include "dispatch.inc"

@@ -28,8 +28,10 @@
 #ifndef SRFTQ_DEQUANT_WAVES
 #define SRFTQ_DEQUANT_WAVES 2
 #endif
-#define SRFTQ_QUANT_OCC __attribute__((amdgpu_waves_per_eu(SRFTQ_QUANT_WAVES)))
-#define SRFTQ_DEQUANT_OCC __attribute__((amdgpu_waves_per_eu(SRFTQ_DEQUANT_WAVES)))
+// d = 256 keeps 256 fp32 coordinates per lane: one wave per SIMD, so that
+// each lane has the whole 512-register file (arch + accumulation VGPRs).
+#define SRFTQ_QUANT_OCC __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1 : SRFTQ_QUANT_WAVES)))
+#define SRFTQ_DEQUANT_OCC __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1 : SRFTQ_DEQUANT_WAVES)))
 
 namespace srftq {
 
@@ -180,15 +182,43 @@ struct RowTile {
 // A D-float row (lambda) fetched by LDS-DMA: lanes 0..D/4-1 move 16 B each.
 template <int D>
 __device__ __forceinline__ void issue_row_f32(const float* src, int lane, uint8_t* lds) {
+  static_assert(D <= 256, "one DMA instruction per row");
   if (lane < D / 4) dma_to_lds<16>(src, 16u * (uint32_t)lane, lds_addr(lds));
 }
 
-// A head's D int8 signs fetched by LDS-DMA: lane l < D/2 moves bytes 2l, 2l+1
-// into the low half of LDS dword l (a sub-dword DMA fills one 4-byte slot
-// per lane).  The kernel turns slot l into sign mask l in place.
+// A head's D int8 signs fetched by LDS-DMA: pair m = 64i + l (lane l of
+// instruction i, m < D/2) moves bytes 2m, 2m+1 into the low half of LDS
+// dword m (a sub-dword DMA fills one 4-byte slot per lane).  The kernel then
+// turns slot m into sign mask m in place (build_masks).
+template <int D>
+struct SignRow {
+  static constexpr int kMasks = D / 2;                 // one per packed fp16 pair
+  static constexpr int kSlots = kMasks < 64 ? 64 : kMasks;
+  static constexpr int kInst = (kMasks + 63) / 64;
+};
 template <int D>
 __device__ __forceinline__ void issue_signs(const int8_t* row, int lane, uint32_t* lds) {
-  if (lane < D / 2) dma_to_lds<2>(row, 2u * (uint32_t)lane, lds_addr(lds));
+  static_for<SignRow<D>::kInst>([&](auto ii) {
+    constexpr int i = decltype(ii)::value;
+    if (64 * i + lane < SignRow<D>::kMasks)
+      dma_to_lds<2>(row + 128 * i, 2u * (uint32_t)lane, lds_addr(lds + 64 * i));
+  });
+}
+// Raw sign slots of this lane (read before the next DMA reuses the row).
+template <int D>
+__device__ __forceinline__ void read_sign_slots(const uint32_t* lds, int lane,
+                                                uint32_t (&u)[SignRow<D>::kInst]) {
+  static_for<SignRow<D>::kInst>([&](auto ii) {
+    constexpr int i = decltype(ii)::value;
+    u[i] = lds[64 * i + lane];
+  });
+}
+template <int D>
+__device__ __forceinline__ void build_masks(uint32_t* lds, int lane, const uint32_t (&u)[SignRow<D>::kInst]) {
+  static_for<SignRow<D>::kInst>([&](auto ii) {
+    constexpr int i = decltype(ii)::value;
+    lds[64 * i + lane] = sign_mask_of(u[i]);
+  });
 }
 
 // Number of global store instructions store_words<N> / store_scales issue.
@@ -271,10 +301,11 @@ __global__ __launch_bounds__(64) SRFTQ_QUANT_OCC void quantize_kernel(const uint
   constexpr int SB = 2 * D / G;           // scale bytes per vector
   constexpr int NCW = CodeWords<D, BITS>::kWords;
   constexpr int NSW = ScaleWords<D, G>::kWords;
-  constexpr int NST = store_count<NCW>() + 1;   // global stores per tile
+  constexpr int NST = store_count<NCW>() + (D / G == 1 ? 1 : store_count<NSW>());   // global stores per tile
   __shared__ __attribute__((aligned(16))) uint8_t lds[XT::kBytes];
   __shared__ __attribute__((aligned(16))) float lam_lds[LAM ? 2 * D : 4];
-  __shared__ __attribute__((aligned(16))) uint32_t smask[2 * 64];   // sign masks, double-buffered
+  constexpr int SM = SignRow<D>::kSlots;
+  __shared__ __attribute__((aligned(16))) uint32_t smask[2 * SM];   // sign masks, double-buffered
 
   const int lane = threadIdx.x;
   const int stride = gridDim.x;
@@ -294,7 +325,7 @@ __global__ __launch_bounds__(64) SRFTQ_QUANT_OCC void quantize_kernel(const uint
     nv = left < 64 ? (int)left : 64;
     XT::issue((const uint8_t*)x + row_index(a, c.bh, t0) * (int64_t)(2 * D), rsb, nv, lane, plan, lds);
     if constexpr (LAM) issue_row_f32<D>(lambda + (int64_t)c.bh * D, lane, (uint8_t*)(lam_lds + buf * D));
-    issue_signs<D>(signs + (int64_t)c.bh * a.sign_stride, lane, smask + buf * 64);
+    issue_signs<D>(signs + (int64_t)c.bh * a.sign_stride, lane, smask + buf * SM);
   };
 
   int nv, buf = 0;
@@ -306,7 +337,8 @@ __global__ __launch_bounds__(64) SRFTQ_QUANT_OCC void quantize_kernel(const uint
     uint32_t w[D / 2];
     XT::read_row(lds, lane, w);
     const int cb = buf;
-    const uint32_t su = smask[cb * 64 + lane];
+    uint32_t su[SignRow<D>::kInst];
+    read_sign_slots<D>(smask + cb * SM, lane, su);
     wait_lgkm0();   // the reads are done before the next DMA reuses the tile
 
     const Cursor now = cur;
@@ -317,9 +349,9 @@ __global__ __launch_bounds__(64) SRFTQ_QUANT_OCC void quantize_kernel(const uint
       issue(cur, nv, buf);
     }
 
-    smask[cb * 64 + lane] = sign_mask_of(su);   // in order before the broadcast reads
+    build_masks<D>(smask + cb * SM, lane, su);   // in order before the broadcast reads
     float y[D];
-    forward<D, ROT, VAR>(w, LdsSigns{smask + cb * 64}, y);
+    forward<D, ROT, VAR>(w, LdsSigns{smask + cb * SM}, y);
     uint32_t codes[NCW];
     uint32_t scales[NSW];
     quantize_tail<D, G, BITS, ROT, VAR, LAM>(y, lam_lds + cb * D, codes, scales);
@@ -374,7 +406,8 @@ __global__ __launch_bounds__(64) SRFTQ_DEQUANT_OCC void dequantize_kernel(const 
   __shared__ __attribute__((aligned(16))) uint8_t stile[ST::kBytes < 16 ? 16 : ST::kBytes];
   __shared__ __attribute__((aligned(16))) uint8_t otile[OT::kBytes];
   __shared__ __attribute__((aligned(16))) float lam_lds[LAM ? 2 * D : 4];
-  __shared__ __attribute__((aligned(16))) uint32_t smask[2 * 64];   // sign masks, double-buffered
+  constexpr int SM = SignRow<D>::kSlots;
+  __shared__ __attribute__((aligned(16))) uint32_t smask[2 * SM];   // sign masks, double-buffered
 
   const int lane = threadIdx.x;
   const int stride = gridDim.x;
@@ -408,7 +441,7 @@ __global__ __launch_bounds__(64) SRFTQ_DEQUANT_OCC void dequantize_kernel(const 
     CT::issue(codes_in + r0 * CB, rsb_c, nv, lane, cplan, ctile);
     ST::issue((const uint8_t*)scales_in + r0 * SB, rsb_s, nv, lane, splan, stile);
     if constexpr (LAM) issue_row_f32<D>(lambda + (int64_t)c.bh * D, lane, (uint8_t*)(lam_lds + buf * D));
-    issue_signs<D>(signs + (int64_t)c.bh * a.sign_stride, lane, smask + buf * 64);
+    issue_signs<D>(signs + (int64_t)c.bh * a.sign_stride, lane, smask + buf * SM);
   };
 
   int nv, buf = 0;
@@ -420,7 +453,11 @@ __global__ __launch_bounds__(64) SRFTQ_DEQUANT_OCC void dequantize_kernel(const 
     CT::read_row(ctile, lane, cw);
     ST::read_row(stile, lane, sw);
     const int cb = buf;
-    smask[cb * 64 + lane] = sign_mask_of(smask[cb * 64 + lane]);
+    {
+      uint32_t su[SignRow<D>::kInst];
+      read_sign_slots<D>(smask + cb * SM, lane, su);
+      build_masks<D>(smask + cb * SM, lane, su);
+    }
     if constexpr (LAM) {
       // e_j / lambda_j, computed lane-parallel in place, read back broadcast
       float* lt = lam_lds + cb * D;
@@ -446,7 +483,7 @@ __global__ __launch_bounds__(64) SRFTQ_DEQUANT_OCC void dequantize_kernel(const 
     inverse<D, ROT, VAR>(y, xr);
 
     // fp16 RNE, then the sign multiply as an XOR on the packed halves
-    const LdsSigns sg{smask + cb * 64};
+    const LdsSigns sg{smask + cb * SM};
     uint32_t o[D / 2];
     static_for<D / 8>([&](auto qq) {
       constexpr int q = decltype(qq)::value;

@@ -40,6 +40,7 @@ using RunFn = hipError_t (*)(const srftq_shape&, const Ptrs&, hipStream_t);
   hipError_t run_misc_d##d(Op op, const srftq_shape&, const Ptrs&, hipStream_t);
 SRFTQ_DECL_RUN(64)
 SRFTQ_DECL_RUN(128)
+SRFTQ_DECL_RUN(256)
 #undef SRFTQ_DECL_RUN
 
 inline int rot_selector(const srftq_shape& s) {

@@ -41,6 +41,9 @@ def test_version_and_status_strings():
     (dict(B=0, T=5, H=8, d=128, group=16, bits=4), S.SRFTQ_OK),
     (dict(B=1, T=10, H=8, d=128, group=128, bits=8), S.SRFTQ_OK),
     (dict(B=1, T=10, H=8, d=96, group=16, bits=4), S.SRFTQ_ERR_UNSUPPORTED),
+    (dict(B=1, T=10, H=4, d=256, group=16, bits=4), S.SRFTQ_OK),
+    (dict(B=1, T=10, H=4, d=256, group=256, bits=8), S.SRFTQ_OK),
+    (dict(B=1, T=10, H=4, d=512, group=16, bits=4), S.SRFTQ_ERR_UNSUPPORTED),
     (dict(B=1, T=10, H=8, d=128, group=16, bits=3), S.SRFTQ_ERR_UNSUPPORTED),
     (dict(B=1, T=10, H=8, d=128, group=12, bits=4), S.SRFTQ_ERR_UNSUPPORTED),
     (dict(B=1, T=10, H=8, d=128, group=4, bits=4), S.SRFTQ_ERR_UNSUPPORTED),

@@ -59,7 +59,7 @@ def test_tiny_workload_full(rot, variant):
     print(st)
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("group,bits", [(8, 4), (16, 4), (32, 8), (64, 4), (0, 8)])
 @pytest.mark.parametrize("rot,variant", ROTS[:3])
 @pytest.mark.parametrize("lam", [False, True])
@@ -73,9 +73,10 @@ def test_ragged_matrix(d, group, bits, rot, variant, lam):
 
 @pytest.mark.parametrize("T", [1, 63, 64, 65, 129])
 @pytest.mark.parametrize("H", [1, 5])
-def test_token_counts(T, H):
-    x, s, _ = rand_case(77 + T, 1, T, H, 128)
-    print(f"[tokens T={T} H={H}]", flush=True)
+@pytest.mark.parametrize("d", [128, 256])
+def test_token_counts(T, H, d):
+    x, s, _ = rand_case(77 + T, 1, T, H, d)
+    print(f"[tokens T={T} H={H} d={d}]", flush=True)
     run_and_check(x, s, None, 16, 4, "srft", "default")
 
 
@@ -124,7 +125,7 @@ def test_zero_subnormal_and_saturated_groups():
             run_and_check(x, None, None, g, bits, rot, "default")
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("rot,variant", ROTS)
 def test_rotate_and_unrotate(d, rot, variant):
     x, s, _ = rand_case(900 + d, 2, 70, 3, d, scale=3.0)
@@ -147,7 +148,7 @@ def test_variants_agree():
     assert np.mean(qa != qb) <= 1e-4
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("rot", ["srft", "srht"])
 def test_calibrate_lambda(d, rot):
     x, s, _ = rand_case(55 + d, 2, 300, 2, d, scale=2.0)
@@ -234,6 +235,26 @@ def test_outlier_workload_full_size_sampled():
     print(_check_sampled(x, s, lam, codes, scales, xhat, w, "srft"))
 
 
-@pytest.mark.skip(reason="d=256 (wide-head workload) kernels are not built yet")
-def test_wide_workload():
-    pass
+@pytest.mark.parametrize("rot,variant", [("srft", "default"), ("srft", "paired"), ("srht", "default")])
+def test_wide_workload_reduced(rot, variant):
+    w = W.WORKLOADS["wide"].scaled(T=700)
+    x, s = W.generate(w)
+    lam = oracle.calibrate_lambda(x, s, rot)
+    print(f"[wide reduced {rot}/{variant}] {x.shape}", flush=True)
+    print(run_and_check(x, s, lam, w.group, w.bits, rot, variant))
+
+
+@pytest.mark.parametrize("rot", ["srft", "srht"])
+def test_wide_workload_full_size_sampled(rot):
+    w = W.WORKLOADS["wide"]
+    x, s = W.generate(w)
+    # lambda input: the oracle's calibration over the first 512 tokens
+    lam = oracle.calibrate_lambda(np.ascontiguousarray(x[:, :512]), s, rot)
+    print(f"[wide full {rot}] {x.shape}", flush=True)
+    xd, sd, ld = dev(x), dev(s), dev(lam)
+    codes, scales = S.quantize(xd, sd, ld, w.group, w.bits, rot)
+    xhat = S.dequantize(codes, scales, sd, ld, w.group, w.bits, rot)
+    torch.cuda.synchronize()
+    rel = (torch.linalg.vector_norm(xhat.float() - xd.float()) / torch.linalg.vector_norm(xd.float())).item()
+    print(_check_sampled(x, s, lam, codes, scales, xhat, w, rot), "rel_l2", rel)
+    assert rel < 0.2
