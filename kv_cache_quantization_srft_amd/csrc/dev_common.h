@@ -102,10 +102,13 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // kernels order it themselves with wait_vm<>() / wait_lgkm0(), and they
 // issue no other vector-memory loads whose results the compiler tracks.
 // "s_nop 0" is the one wait state required between writing M0 and an LDS-DMA.
-template <int SIZE>
+template <int SIZE, bool STREAM = false>
 __device__ __forceinline__ void dma_to_lds(const void* sbase, uint32_t voff, uint32_t lds) {
   static_assert(SIZE == 16 || SIZE == 4 || SIZE == 2, "LDS-DMA size");
-  if constexpr (SIZE == 16)
+  if constexpr (SIZE == 16 && STREAM)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+                 :: "v"(voff), "s"(sbase), "s"(lds) : "memory", "m0");
+  else if constexpr (SIZE == 16)
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                  :: "v"(voff), "s"(sbase), "s"(lds) : "memory", "m0");
   else if constexpr (SIZE == 4)

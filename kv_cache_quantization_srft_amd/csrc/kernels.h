@@ -143,7 +143,7 @@ struct RowTile {
 #pragma unroll
       for (int i = 0; i < kInst; ++i) {
         const uint8_t* g = base + (size_t)(i / kPat) * (size_t)(kPat * kRpi) * rsb;
-        dma_to_lds<kElem>(g, plan.off[i % kPat], l0 + i * 64 * kSlot);
+        dma_to_lds<kElem, true>(g, plan.off[i % kPat], l0 + i * 64 * kSlot);
       }
     } else {
 #pragma unroll
@@ -514,7 +514,11 @@ __global__ __launch_bounds__(64) SRFTQ_DEQUANT_OCC void dequantize_kernel(const 
         // o_lds[m] already holds the rows of pattern m; add whole periods only
         const uint4 q = *(const uint4*)(otile + (i / OT::kPat) * (OT::kPat * OT::kRpi * D) + o_lds[m]);
         uint8_t* dst = obase + (size_t)(i / OT::kPat) * (size_t)(OT::kPat * OT::kRpi) * rsb_x + h * D + o_glb[m];
-        if (nv_now == 64 || i * OT::kRpi + lane / OT::kCpr < nv_now) *(uint4*)dst = q;
+        if (nv_now == 64 || i * OT::kRpi + lane / OT::kCpr < nv_now) {
+          typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+          const u32x4_t v = {q.x, q.y, q.z, q.w};
+          __builtin_nontemporal_store(v, (u32x4_t*)dst);
+        }
       });
       wave_fence();
     });
