@@ -45,6 +45,25 @@ struct Geo {
   int32_t tiles_t;       // ceil(T / 64)
   int32_t n_tiles;       // tiles_t * BH
   int32_t sign_stride;   // elements between heads' sign rows: D, or 0 for a shared row
+  int32_t tpb;           // streaming kernels: tiles per block (consecutive); 0 = persistent grid
+};
+
+// Tiles of one block of a streaming kernel: either tpb consecutive tiles
+// starting at blockIdx*tpb, or (tpb == 0) every gridDim-th tile.
+struct TileRange {
+  int first, step, remaining;   // remaining = tiles after the first
+  __device__ __forceinline__ explicit TileRange(const Geo& a) {
+    if (a.tpb > 0) {
+      first = (int)blockIdx.x * a.tpb;
+      step = 1;
+      const int n = a.n_tiles - first;
+      remaining = (n < a.tpb ? n : a.tpb) - 1;
+    } else {
+      first = (int)blockIdx.x;
+      step = (int)gridDim.x;
+      remaining = (a.n_tiles - 1 - first) / step;
+    }
+  }
 };
 
 
@@ -308,16 +327,17 @@ __global__ __launch_bounds__(64) SRFTQ_QUANT_OCC void quantize_kernel(const uint
   __shared__ __attribute__((aligned(16))) uint32_t smask[2 * SM];   // sign masks, double-buffered
 
   const int lane = threadIdx.x;
-  const int stride = gridDim.x;
-  if ((int)blockIdx.x >= a.n_tiles) return;
+  const TileRange tr(a);
+  if (tr.first >= a.n_tiles) return;
+  const int stride = tr.step;
   const uint32_t rsb = (uint32_t)a.H * (uint32_t)(2 * D);   // x row stride, bytes
   typename XT::Plan plan;
   plan.init(lane, rsb);
   const int dk = stride / a.BH, dbh = stride - dk * a.BH;
 
   Cursor cur;
-  cur.init(blockIdx.x, a.BH);
-  int remaining = (a.n_tiles - 1 - (int)blockIdx.x) / stride;     // tiles after this one
+  cur.init(tr.first, a.BH);
+  int remaining = tr.remaining;     // tiles after this one
 
   auto issue = [&](const Cursor& c, int& nv, int buf) {
     const int64_t t0 = (int64_t)c.k * 64;
@@ -410,8 +430,9 @@ __global__ __launch_bounds__(64) SRFTQ_DEQUANT_OCC void dequantize_kernel(const 
   __shared__ __attribute__((aligned(16))) uint32_t smask[2 * SM];   // sign masks, double-buffered
 
   const int lane = threadIdx.x;
-  const int stride = gridDim.x;
-  if ((int)blockIdx.x >= a.n_tiles) return;
+  const TileRange tr(a);
+  if (tr.first >= a.n_tiles) return;
+  const int stride = tr.step;
   const uint32_t rsb_c = CB, rsb_s = SB;   // cache rows are contiguous
   const uint32_t rsb_x = (uint32_t)a.H * (uint32_t)(2 * D);
   typename CT::Plan cplan;
@@ -430,8 +451,8 @@ __global__ __launch_bounds__(64) SRFTQ_DEQUANT_OCC void dequantize_kernel(const 
   const int dk = stride / a.BH, dbh = stride - dk * a.BH;
 
   Cursor cur;
-  cur.init(blockIdx.x, a.BH);
-  int remaining = (a.n_tiles - 1 - (int)blockIdx.x) / stride;
+  cur.init(tr.first, a.BH);
+  int remaining = tr.remaining;
 
   auto issue = [&](const Cursor& c, int& nv, int buf) {
     const int64_t t0 = (int64_t)c.k * 64;
@@ -479,6 +500,9 @@ __global__ __launch_bounds__(64) SRFTQ_DEQUANT_OCC void dequantize_kernel(const 
 
     float y[D];
     dequantize_head<D, G, BITS, ROT, VAR, LAM>(cw, sw, lam_lds + cb * D, y);
+    // d = 256 fills the register file: keep the scheduler from interleaving
+    // the head with the transform, which would need more than 512 registers
+    if constexpr (D >= 256) __builtin_amdgcn_sched_barrier(0);
     float xr[D];
     inverse<D, ROT, VAR>(y, xr);
 

@@ -54,6 +54,13 @@ int device_cu_count();
 // Resident blocks per CU of a kernel at a block size (cached per kernel).
 int blocks_per_cu(const void* kernel, int block);
 
+// Tiles per block of the streaming kernels (0 = persistent grid).  One tile
+// per block lets the hardware dispatcher balance the load across CUs (waves
+// of a persistent grid finish up to 40 % apart); at d = 256, with one wave
+// per SIMD, the persistent grid's one-tile-ahead prefetch hides more latency.
+// SRFTQ_TILES_PER_BLOCK overrides it (tuning).
+int tiles_per_block(int d);
+
 // Persistent grid: at most (resident blocks per CU) x CUs, at least 1.
 inline int persistent_grid(const void* kernel, int n_tiles, int block) {
   long g = (long)blocks_per_cu(kernel, block) * (long)device_cu_count();

@@ -265,6 +265,8 @@ __device__ __forceinline__ void dequantize_head(const uint32_t (&codes)[CodeWord
         constexpr int j = g * G + decltype(kk)::value;
         y[j] = __builtin_fmaf(u[j], s, ns) * lam[j];
       });
+      // d = 256 fills the register file: one group's table reads at a time
+      if constexpr (D >= 256) __builtin_amdgcn_sched_barrier(0);
     });
   } else {
     static_for<NG>([&](auto gg) {

@@ -247,19 +247,22 @@ __device__ __forceinline__ void hermitian_unpack(const float (&Zr)[D / 2], const
   });
 }
 
-// In-place natural-order Walsh-Hadamard transform of length M (unnormalized).
-template <int M>
-__device__ __forceinline__ void wht(float (&v)[M]) {
-  static_for<(M > 1 ? __builtin_ctz(M) : 0)>([&](auto ss) {
-    constexpr int h = 1 << decltype(ss)::value;
+// In-place natural-order (Sylvester) Walsh-Hadamard transform of the M
+// values v[OFF .. OFF+M) (unnormalized), depth first:
+// H_M [a; b] = [H a + H b; H a - H b], so each half is finished before the
+// combining stage, which keeps few temporaries live at d = 256.
+template <int M, int OFF = 0, int LEN>
+__device__ __forceinline__ void wht(float (&v)[LEN]) {
+  if constexpr (M > 1) {
+    wht<M / 2, OFF>(v);
+    wht<M / 2, OFF + M / 2>(v);
     static_for<M / 2>([&](auto ii) {
-      constexpr int i = decltype(ii)::value;
-      constexpr int lo = (i / h) * 2 * h + (i % h);
-      const float a = v[lo], b = v[lo + h];
-      v[lo] = a + b;
-      v[lo + h] = a - b;
+      constexpr int i = OFF + decltype(ii)::value;
+      const float a = v[i], b = v[i + M / 2];
+      v[i] = a + b;
+      v[i + M / 2] = a - b;
     });
-  });
+  }
 }
 
 // ----------------------------------------------------------------------------
@@ -384,18 +387,18 @@ __device__ __forceinline__ void inverse(const float (&y)[D], float (&x)[D]) {
       x[j] = y[j];
     });
   } else if constexpr (ROT == ROT_SRHT) {
-    float u[N], v[N];
-    static_for<N>([&](auto kk) {
-      constexpr int k = decltype(kk)::value;
-      u[k] = y[k];
-      v[k] = y[N + k];
+    // in place in x: the two half-length transforms, then the top-bit stage
+    static_for<D>([&](auto jj) {
+      constexpr int j = decltype(jj)::value;
+      x[j] = y[j];
     });
-    wht<N>(u);
-    wht<N>(v);
+    wht<N, 0>(x);
+    wht<N, N>(x);
     static_for<N>([&](auto rr) {
       constexpr int r = decltype(rr)::value;
-      x[r] = u[r] + v[r];
-      x[r + N] = u[r] - v[r];
+      const float u = x[r], v = x[r + N];
+      x[r] = u + v;
+      x[r + N] = u - v;
     });
   } else if constexpr (VAR == VAR_PAIRED) {
     // Re-pair: Z_k = E_k + i O_k with 2E_k = X_k + conj X_{N-k},
