@@ -52,6 +52,8 @@ def test_version_and_status_strings():
     (dict(B=1, T=-1, H=8, d=128, group=16, bits=4), S.SRFTQ_ERR_SHAPE),
     (dict(B=1, T=10, H=0, d=128, group=16, bits=4), S.SRFTQ_ERR_SHAPE),
     (dict(B=1 << 20, T=1 << 30, H=8, d=128, group=16, bits=4), S.SRFTQ_ERR_SHAPE),
+    (dict(B=1, T=2, H=65535, d=64, group=32, bits=8), S.SRFTQ_OK),
+    (dict(B=1, T=2, H=65536, d=64, group=32, bits=8), S.SRFTQ_ERR_SHAPE),
 ])
 def test_validate(kw, expect):
     assert S.srftq_validate(S.make_shape(**kw)) == expect

@@ -258,3 +258,19 @@ def test_wide_workload_full_size_sampled(rot):
     rel = (torch.linalg.vector_norm(xhat.float() - xd.float()) / torch.linalg.vector_norm(xd.float())).item()
     print(_check_sampled(x, s, lam, codes, scales, xhat, w, rot), "rel_l2", rel)
     assert rel < 0.2
+
+
+def test_largest_head_count():
+    """H = 65535, the largest the ABI accepts: x rows 16 MiB apart inside one
+    64-token tile (per-lane DMA offsets near their 32-bit range)."""
+    x, s, l = rand_case(4242, 1, 2, 65535, 64, lam=True)
+    print(f"[H=65535] {x.shape}", flush=True)
+    print(run_and_check(x, s, l, 32, 8, "srft", "default"))
+
+
+def test_many_tensors_single_token():
+    """B = 4096 tensors of one token each (decode-shaped): one ragged tile per
+    (tensor, head)."""
+    x, s, _ = rand_case(4343, 4096, 1, 2, 128)
+    print(f"[B=4096, T=1] {x.shape}", flush=True)
+    print(run_and_check(x, s, None, 16, 4, "srht", "default"))
