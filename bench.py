@@ -31,10 +31,16 @@ KERNEL_SOURCES = ["dev_common.h", "xform.h", "quant.h", "kernels.h", "dispatch.i
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources with comments and whitespace removed, so a
+    traffic record stays valid across edits that change no code."""
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "kv_cache_quantization_srft_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "kv_cache_quantization_srft_amd", "csrc", f)) as fh:
+            src = fh.read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", "", src)
+        h.update("".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -6,16 +6,19 @@
 // mask per packed fp16 pair, and both are read back as LDS broadcasts.
 // Tiles are numbered token-chunk-major, head-minor, so the waves resident at
 // any moment cover adjacent rows of the [B,T,H,d] tensors.
-// Each block is one wave; the grid is persistent (about the number of
-// resident waves) and walks the tiles with a fixed stride.
+// Each block is one wave and takes Geo::tpb consecutive tiles (one, at
+// d <= 128, so that the hardware dispatcher balances the CUs), or, with
+// tpb = 0, the grid is persistent and every block walks the tiles with a
+// fixed stride (d = 256).  A block with more than one tile fetches the next
+// tile while the current one computes.
 //
-// Input staging (quantize): the next tile's 64 rows are fetched straight into
-// LDS with global_load_lds_dwordx4 (one instruction = 1 KiB, fully coalesced)
-// while the current tile computes; lanes then read their own row with
-// ds_read_b128 through an XOR swizzle that keeps every 8- and 16-lane phase
-// on distinct banks.
+// Input staging: the tile's rows (quantize: 64 fp16 rows; dequantize: code
+// and scale rows) go straight into LDS with global_load_lds_dwordx4 (one
+// instruction = 1 KiB of whole rows, streaming cache hint); lanes then read
+// their own row with ds_read_b128 through an XOR swizzle that keeps every 8-
+// and 16-lane phase on distinct banks.
 // Output staging (dequantize): rows go to LDS and leave as 1 KiB coalesced
-// global stores.
+// nontemporal stores.
 #pragma once
 
 #include "quant.h"
@@ -36,8 +39,7 @@
 namespace srftq {
 
 // Sizes of a launch.  Data pointers travel as separate __restrict__ kernel
-// arguments so the compiler may read signs and lambda through scalar loads;
-// `signs` is never null (the host substitutes a row of +1).
+// arguments; `signs` is never null (the host substitutes a row of +1).
 struct Geo {
   int64_t T;
   int32_t H;
