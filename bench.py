@@ -63,7 +63,19 @@ def load_traffic(kernel: str, workload: str):
     return t.get("hbm_bytes_per_launch")
 
 
-def _counter_means(csv_path: str, counter: str) -> dict:
+def _kernel_family(name: str, w) -> str | None:
+    """'quantize' / 'dequantize' for the workload's own kernel instance
+    (template arguments d, group, bits), 'copy' for the copy probe."""
+    import re
+    inst = rf"<\s*{w.d},\s*{w.group},\s*{w.bits},"
+    if re.search(r"dequantize_kernel" + inst, name):
+        return "dequantize"
+    if re.search(r"(?<!de)quantize_kernel" + inst, name):
+        return "quantize"
+    return "copy" if "neg" in name else None
+
+
+def _counter_means(csv_path: str, counter: str, w) -> dict:
     """Mean counter value per dispatch, by kernel family, from a rocprofv3
     counter_collection.csv (values summed over the counter's instances)."""
     import csv
@@ -72,10 +84,7 @@ def _counter_means(csv_path: str, counter: str) -> dict:
         for row in csv.DictReader(f):
             if row.get("Counter_Name") != counter:
                 continue
-            name = row.get("Kernel_Name", "")
-            fam = ("dequantize" if "dequantize_kernel" in name else
-                   "quantize" if "quantize_kernel" in name else
-                   "copy" if "neg" in name else None)
+            fam = _kernel_family(row.get("Kernel_Name", ""), w)
             if fam is None:
                 continue
             key = (fam, row.get("Dispatch_Id"))
@@ -94,8 +103,8 @@ def write_traffic(fetch_csv: str, write_csv: str, workload: str) -> None:
     from kv_cache_quantization_srft_amd import workloads as W
     w = W.WORKLOADS[workload]
     copy_bytes = 2 * w.d * w.nvec
-    fetch = _counter_means(fetch_csv, "FETCH_SIZE")
-    write = _counter_means(write_csv, "WRITE_SIZE")
+    fetch = _counter_means(fetch_csv, "FETCH_SIZE", w)
+    write = _counter_means(write_csv, "WRITE_SIZE", w)
     f_scale = copy_bytes / (fetch["copy"] * 1024.0)
     w_scale = copy_bytes / (write["copy"] * 1024.0)
     bpv = algorithmic_bytes_per_vector(w.d, w.group, w.bits)
@@ -139,6 +148,91 @@ def cpu_baseline(w, x, s, lam, target_s: float = 15.0):
                       f"quantize + dequantize, fp64 direct DFT, {dt:.1f} s"}
 
 
+def decode_append_latency(steps: int = 1000, graph_steps: int = 100) -> dict:
+    """The decode-append shape: 256 sequences each append one token per step
+    ([256, 1, H=8, d=64], int8, group 32) into a per-head cache of
+    `steps` rows through srftq_cache_append, write positions advanced on the
+    device.  Reported: the per-step time of eager calls through the Python
+    binding (host-bound at this size), and of the same steps replayed from
+    a HIP graph of `graph_steps` steps (GPU time per step)."""
+    import numpy as np
+    import torch
+
+    from kv_cache_quantization_srft_amd import srftq as S
+    from kv_cache_quantization_srft_amd import workloads as W
+
+    w = W.WORKLOADS["decode"]
+    B, H, d = w.T, w.H, w.d
+    dev = torch.device("cuda:0")
+    vals = torch.from_numpy(W.values(w, B=graph_steps)).to(dev)          # [steps, 256, H, d]
+    xs = [vals[i].unsqueeze(1).contiguous() for i in range(graph_steps)]   # [256, 1, H, d] each
+    sd = torch.from_numpy(W.signs(w, B=B)).to(dev)
+    codes = torch.zeros((B, H, steps, d * w.bits // 8), dtype=torch.uint8, device=dev)
+    scales = torch.zeros((B, H, steps, d // w.group), dtype=torch.float16, device=dev)
+    pos = torch.zeros((B,), dtype=torch.int32, device=dev)
+
+    def one(i):
+        S.cache_append(xs[i % graph_steps], codes, scales, pos, sd, None, w.group, w.bits)
+        pos.add_(1)
+
+    for i in range(20):
+        one(i)
+    torch.cuda.synchronize()
+    pos.zero_()
+    wall = []
+    torch.cuda.synchronize()
+    for i in range(steps):
+        t = time.perf_counter()
+        one(i)
+        torch.cuda.synchronize()
+        wall.append((time.perf_counter() - t) * 1e6)
+    wall = np.array(wall)
+    eager_codes, eager_scales = codes.clone(), scales.clone()
+
+    # the same steps captured once and replayed (positions keep advancing on
+    # the device; rows past the capacity would be dropped, none are reached)
+    pos.zero_()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        one(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(graph_steps):
+            one(i)
+    reps = max(1, (steps - 1) // graph_steps)
+    codes.zero_()
+    scales.zero_()
+    pos.zero_()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    pos.zero_()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    graph_us = e0.elapsed_time(e1) * 1e3 / (reps * graph_steps)
+    # every replayed step wrote the rows an eager step wrote from the same input
+    n = reps * graph_steps
+    same = bool(torch.equal(codes[:, :, :n], eager_codes[:, :, :n])
+                and torch.equal(scales[:, :, :n].view(torch.int16), eager_scales[:, :, :n].view(torch.int16)))
+    return {"workload": f"decode-append: {B} sequences x 1 token, H={H}, d={d}, "
+                        f"SRFT, group {w.group}, int{w.bits}, {steps} steps",
+            "vectors_per_step": B * H,
+            "eager_us_per_step": {"mean": float(wall.mean()), "p50": float(np.percentile(wall, 50)),
+                                  "p99": float(np.percentile(wall, 99))},
+            "graph_us_per_step": graph_us,
+            "graph_ns_per_vector": graph_us * 1e3 / (B * H),
+            "graph_rows_match_eager": same,
+            "step": "srftq_cache_append of the new tokens, then the positions advanced (+1)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -149,6 +243,7 @@ def main():
                          "steps run at the clocks a sustained load settles to")
     ap.add_argument("--workload", default="outlier")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode-append latency figures")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic_<kernel>_<workload>.json from two rocprofv3 "
                          "counter_collection.csv files of this benchmark, then exit")
@@ -261,6 +356,8 @@ def main():
     # sanity: reconstruction error of the round trip
     rel = (torch.linalg.vector_norm(xhat.float() - xd.float()) / torch.linalg.vector_norm(xd.float())).item()
 
+    dec = None if args.no_decode else decode_append_latency()
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, x, s, lam_h)
@@ -293,6 +390,7 @@ def main():
         "hbm_peak_frac_dequantize": per_kernel["dequantize"]["hbm_frac"],
         "step": "srftq_quantize then srftq_dequantize of every vector (one launch each)",
         "reconstruction_rel_l2": rel,
+        "decode_append": dec,
         "device": torch.cuda.get_device_name(0),
         "input_generation_s": gen_s,
     }

@@ -156,6 +156,37 @@ srftq_status srftq_unrotate(const srftq_shape* shape, const float* y,
 srftq_status srftq_calibrate_lambda(const srftq_shape* shape, const uint16_t* x,
                                     const int8_t* signs, float* lambda, void* stream);
 
+/*
+ * Quantize-on-append into a preallocated cache (the pages integrate the
+ * fused kernel as a growing int4 KV cache: a HuggingFace Cache subclass,
+ * "When Quantization Is Free", Metodologia section 2).  The new tokens
+ * x [B,T,H,d] (T tokens per tensor, e.g. T = 1 per decode step) are rotated
+ * and quantized exactly as by srftq_quantize, and token t of tensor b is
+ * written to row pos[b] + t of each of its heads in the caches
+ *   codes   [B,H,t_cap,d*bits/8]   scales  [B,H,t_cap,d/group]
+ * (the head-major layout of srftq_quantize with t_cap rows per head).
+ *   pos     in  int32 [B] on the device (4-B aligned), or NULL for row t.
+ *           Read on the device when the kernel runs, so a decode loop can
+ *           advance it on the stream without a host round trip.
+ *   Rows outside [0, t_cap) are not written (their tokens are dropped);
+ *   every other row of the caches is left as it was.
+ *   t_cap   >= 0 (0: nothing is written).  Other arguments, alignment and
+ *           errors as for srftq_quantize.
+ */
+srftq_status srftq_cache_append(const srftq_shape* shape, int64_t t_cap, const int32_t* pos,
+                                const uint16_t* x, const int8_t* signs, const float* lambda,
+                                uint8_t* codes, uint16_t* scales, void* stream);
+
+/*
+ * Read the first T rows of every head of a cache written by
+ * srftq_cache_append (t_cap rows per head, T <= t_cap, else
+ * SRFTQ_ERR_SHAPE): dequantize + unrotate as srftq_dequantize, into
+ * x_out fp16 [B,T,H,d].  With t_cap == T this is srftq_dequantize.
+ */
+srftq_status srftq_cache_read(const srftq_shape* shape, int64_t t_cap, const uint8_t* codes,
+                              const uint16_t* scales, const int8_t* signs, const float* lambda,
+                              uint16_t* x_out, void* stream);
+
 /* Static description of a status code. */
 const char* srftq_status_string(srftq_status status);
 

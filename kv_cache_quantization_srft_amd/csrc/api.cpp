@@ -103,6 +103,56 @@ srftq_status check_side(const int8_t* signs, const float* lambda) {
   return SRFTQ_OK;
 }
 
+// A cache of t_cap rows per head must keep byte offsets within int64 range
+// (the same bound validate() puts on T).
+srftq_status validate_cache(const srftq_shape* s, int64_t t_cap) {
+  if (t_cap < 0) return SRFTQ_ERR_SHAPE;
+  if (s->B > 0 && t_cap > (int64_t)0x7fffffffffffLL / (s->B * (int64_t)s->H * s->d)) return SRFTQ_ERR_SHAPE;
+  return SRFTQ_OK;
+}
+
+srftq_status quantize_into(const srftq_shape* s, int64_t pitch, const int32_t* pos, const uint16_t* x,
+                           const int8_t* signs, const float* lambda, uint8_t* codes, uint16_t* scales,
+                           void* stream) {
+  srftq_status st;
+  if (!x || !codes || !scales) return SRFTQ_ERR_NULL;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return SRFTQ_ERR_ALIGN;
+  if (pos && !aligned4(pos)) return SRFTQ_ERR_ALIGN;
+  if ((st = check_side(signs, lambda)) != SRFTQ_OK) return st;
+  srftq::Ptrs p = {};
+  p.x = x;
+  p.signs = signs ? signs : srftq::plus_ones_ptr();
+  p.signs_shared = (signs == nullptr);
+  if (!p.signs) return SRFTQ_ERR_HIP;
+  p.lambda = lambda;
+  p.codes_out = codes;
+  p.scales_out = scales;
+  p.pitch = pitch;
+  p.pos = pos;
+  const srftq::RunFn fn = pick(kQuantize, s);
+  return fn ? from_hip(fn(*s, p, (hipStream_t)stream)) : SRFTQ_ERR_UNSUPPORTED;
+}
+
+srftq_status dequantize_from(const srftq_shape* s, int64_t pitch, const uint8_t* codes,
+                             const uint16_t* scales, const int8_t* signs, const float* lambda,
+                             uint16_t* x_out, void* stream) {
+  srftq_status st;
+  if (!codes || !scales || !x_out) return SRFTQ_ERR_NULL;
+  if (!aligned16(codes) || !aligned16(scales) || !aligned16(x_out)) return SRFTQ_ERR_ALIGN;
+  if ((st = check_side(signs, lambda)) != SRFTQ_OK) return st;
+  srftq::Ptrs p = {};
+  p.codes_in = codes;
+  p.scales_in = scales;
+  p.signs = signs ? signs : srftq::plus_ones_ptr();
+  p.signs_shared = (signs == nullptr);
+  if (!p.signs) return SRFTQ_ERR_HIP;
+  p.lambda = lambda;
+  p.x_out = x_out;
+  p.pitch = pitch;
+  const srftq::RunFn fn = pick(kDequantize, s);
+  return fn ? from_hip(fn(*s, p, (hipStream_t)stream)) : SRFTQ_ERR_UNSUPPORTED;
+}
+
 }  // namespace
 
 extern "C" {
@@ -124,19 +174,7 @@ srftq_status srftq_quantize(const srftq_shape* s, const uint16_t* x, const int8_
   srftq_status st = validate(s);
   if (st != SRFTQ_OK) return st;
   if (nvec(s) == 0) return SRFTQ_OK;
-  if (!x || !codes || !scales) return SRFTQ_ERR_NULL;
-  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return SRFTQ_ERR_ALIGN;
-  if ((st = check_side(signs, lambda)) != SRFTQ_OK) return st;
-  srftq::Ptrs p = {};
-  p.x = x;
-  p.signs = signs ? signs : srftq::plus_ones_ptr();
-  p.signs_shared = (signs == nullptr);
-  if (!p.signs) return SRFTQ_ERR_HIP;
-  p.lambda = lambda;
-  p.codes_out = codes;
-  p.scales_out = scales;
-  const srftq::RunFn fn = pick(kQuantize, s);
-  return fn ? from_hip(fn(*s, p, (hipStream_t)stream)) : SRFTQ_ERR_UNSUPPORTED;
+  return quantize_into(s, 0, nullptr, x, signs, lambda, codes, scales, stream);
 }
 
 srftq_status srftq_dequantize(const srftq_shape* s, const uint8_t* codes, const uint16_t* scales,
@@ -144,21 +182,29 @@ srftq_status srftq_dequantize(const srftq_shape* s, const uint8_t* codes, const 
   srftq_status st = validate(s);
   if (st != SRFTQ_OK) return st;
   if (nvec(s) == 0) return SRFTQ_OK;
-  if (!codes || !scales || !x_out) return SRFTQ_ERR_NULL;
-  if (!aligned16(codes) || !aligned16(scales) || !aligned16(x_out)) return SRFTQ_ERR_ALIGN;
-  if ((st = check_side(signs, lambda)) != SRFTQ_OK) return st;
-  srftq::Ptrs p = {};
-  p.codes_in = codes;
-  p.scales_in = scales;
-  p.signs = signs ? signs : srftq::plus_ones_ptr();
-  p.signs_shared = (signs == nullptr);
-  if (!p.signs) return SRFTQ_ERR_HIP;
-  p.lambda = lambda;
-  p.x_out = x_out;
-  const srftq::RunFn fn = pick(kDequantize, s);
-  return fn ? from_hip(fn(*s, p, (hipStream_t)stream)) : SRFTQ_ERR_UNSUPPORTED;
+  return dequantize_from(s, 0, codes, scales, signs, lambda, x_out, stream);
 }
 
+srftq_status srftq_cache_append(const srftq_shape* s, int64_t t_cap, const int32_t* pos,
+                                const uint16_t* x, const int8_t* signs, const float* lambda,
+                                uint8_t* codes, uint16_t* scales, void* stream) {
+  srftq_status st = validate(s);
+  if (st != SRFTQ_OK) return st;
+  if ((st = validate_cache(s, t_cap)) != SRFTQ_OK) return st;
+  if (nvec(s) == 0 || t_cap == 0) return SRFTQ_OK;
+  return quantize_into(s, t_cap, pos, x, signs, lambda, codes, scales, stream);
+}
+
+srftq_status srftq_cache_read(const srftq_shape* s, int64_t t_cap, const uint8_t* codes,
+                              const uint16_t* scales, const int8_t* signs, const float* lambda,
+                              uint16_t* x_out, void* stream) {
+  srftq_status st = validate(s);
+  if (st != SRFTQ_OK) return st;
+  if ((st = validate_cache(s, t_cap)) != SRFTQ_OK) return st;
+  if (t_cap < s->T) return SRFTQ_ERR_SHAPE;
+  if (nvec(s) == 0) return SRFTQ_OK;
+  return dequantize_from(s, t_cap, codes, scales, signs, lambda, x_out, stream);
+}
 static srftq_status run_misc(srftq::Op op, const srftq_shape* s, const srftq::Ptrs& p, void* stream) {
   hipStream_t hs = (hipStream_t)stream;
   switch (s->d) {

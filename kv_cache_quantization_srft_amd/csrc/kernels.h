@@ -41,7 +41,9 @@ namespace srftq {
 // Sizes of a launch.  Data pointers travel as separate __restrict__ kernel
 // arguments; `signs` is never null (the host substitutes a row of +1).
 struct Geo {
-  int64_t T;
+  int64_t T;             // tokens of x (per tensor)
+  int64_t pitch;         // cache rows per head (>= T except when appending)
+  const int32_t* pos;    // append: first cache row of each tensor's tokens, or null (row t)
   int32_t H;
   int32_t BH;            // B * H
   int32_t tiles_t;       // ceil(T / 64)
@@ -92,10 +94,10 @@ __device__ __forceinline__ int64_t row_index(const Geo& a, int bh, int64_t t) {
   return ((int64_t)b * a.T + t) * a.H + h;
 }
 
-// Row of token t of head bh in the head-major quantized cache [B,H,T,.]:
-// a tile's 64 code and scale rows are one contiguous run.
+// Row t of head bh in the head-major quantized cache [B,H,pitch,.]: a tile's
+// 64 code and scale rows are one contiguous run.
 __device__ __forceinline__ int64_t cache_row(const Geo& a, int bh, int64_t t) {
-  return (int64_t)bh * a.T + t;
+  return (int64_t)bh * a.pitch + t;
 }
 
 // ----------------------------------------------------------------------------
@@ -303,7 +305,9 @@ __device__ __forceinline__ void load_scales(const uint8_t* src, uint32_t (&s)[Sc
 }
 
 // ----------------------------------------------------------------------------
-// Quantize: fp16 [B,T,H,D] -> codes + fp16 scales, head-major [B,H,T,.].
+// Quantize: fp16 [B,T,H,D] -> codes + fp16 scales, head-major [B,H,pitch,.]
+// (pitch = T, or the capacity of an append cache, where token t of tensor b
+// goes to row pos[b] + t).
 //
 // Loop per tile: wait for the tile's LDS-DMA (not for the previous tile's
 // stores), read the own row from LDS, issue the next tile's DMA, transform +
@@ -378,12 +382,22 @@ __global__ __launch_bounds__(64) SRFTQ_QUANT_OCC void quantize_kernel(const uint
     uint32_t scales[NSW];
     quantize_tail<D, G, BITS, ROT, VAR, LAM>(y, lam_lds + cb * D, codes, scales);
 
-    if (lane < nv_now) {
-      const int64_t r0 = cache_row(a, now.bh, (int64_t)now.k * 64);   // uniform
+    // Cache row of token 0 of the tile (uniform); when appending, tokens
+    // start at the tensor's position and rows outside [0, pitch) are dropped.
+    int64_t t0 = (int64_t)now.k * 64;
+    bool ok = lane < nv_now;
+    if (a.pos) {
+      t0 += a.pos[now.bh / a.H];
+      ok = ok && t0 + lane >= 0 && t0 + lane < a.pitch;
+    }
+    if (ok) {
+      const int64_t r0 = cache_row(a, now.bh, t0);
       store_words<NCW>(codes_out + r0 * CB + (uint32_t)lane * CB, codes);
       store_scales<D, G>((uint8_t*)scales_out + r0 * SB + (uint32_t)lane * SB, scales);
     }
-    return nv_now == 64;
+    // with dropped rows a whole wave may skip its stores: then the next
+    // wait must not count on them
+    return nv_now == 64 && !a.pos;
   };
 
   // The first tile is peeled so that every entry into the loop has this
@@ -404,7 +418,7 @@ __global__ __launch_bounds__(64) SRFTQ_QUANT_OCC void quantize_kernel(const uint
 }
 
 // ----------------------------------------------------------------------------
-// Dequantize: codes + scales [B,H,T,.] -> fp16 [B,T,H,D].  Codes, scales and lambda
+// Dequantize: rows [0, T) of codes + scales [B,H,pitch,.] -> fp16 [B,T,H,D].  Codes, scales and lambda
 // arrive by coalesced LDS-DMA (prefetched one tile ahead); output rows are
 // staged through LDS half a row at a time and leave as 1 KiB coalesced
 // stores.

@@ -23,6 +23,8 @@ struct Ptrs {
   uint16_t* x_out;
   float* y_out;
   float* lambda_out;
+  int64_t pitch;          // cache rows per head; 0 = T (the cache holds exactly x's tokens)
+  const int32_t* pos;     // append positions [B] (device) or null
 };
 
 // Per-d entry points (one translation unit per d, direction and rotation

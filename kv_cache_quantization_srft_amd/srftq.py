@@ -7,8 +7,9 @@ missing library raises.
 
 The C functions keep their names here (``srftq_quantize`` ...) and take the
 same arguments, with a ``Shape`` in place of ``const srftq_shape*``.  The
-convenience wrappers ``quantize`` / ``dequantize`` / ``rotate`` /
-``unrotate`` / ``calibrate_lambda`` allocate outputs with torch.
+convenience wrappers ``quantize`` / ``dequantize`` / ``cache_append`` /
+``cache_read`` / ``rotate`` / ``unrotate`` / ``calibrate_lambda`` allocate
+outputs with torch.
 """
 from __future__ import annotations
 
@@ -68,11 +69,14 @@ def lib() -> ctypes.CDLL:
         L.srftq_rotate.argtypes = [sp, vp, vp, vp, vp]
         L.srftq_unrotate.argtypes = [sp, vp, vp, vp, vp]
         L.srftq_calibrate_lambda.argtypes = [sp, vp, vp, vp, vp]
+        L.srftq_cache_append.argtypes = [sp, ctypes.c_int64, vp, vp, vp, vp, vp, vp, vp]
+        L.srftq_cache_read.argtypes = [sp, ctypes.c_int64, vp, vp, vp, vp, vp, vp]
         L.srftq_status_string.argtypes = [ctypes.c_int]
         L.srftq_status_string.restype = ctypes.c_char_p
         L.srftq_version.argtypes = []
         for f in ("srftq_validate", "srftq_quantize", "srftq_dequantize", "srftq_rotate",
-                  "srftq_unrotate", "srftq_calibrate_lambda", "srftq_version"):
+                  "srftq_unrotate", "srftq_calibrate_lambda", "srftq_cache_append",
+                  "srftq_cache_read", "srftq_version"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -126,6 +130,16 @@ def srftq_quantize(shape, x, signs, lam, codes, scales, stream=None) -> int:
 def srftq_dequantize(shape, codes, scales, signs, lam, x_out, stream=None) -> int:
     return lib().srftq_dequantize(ctypes.byref(shape), _dp(codes), _dp(scales), _dp(signs), _dp(lam),
                                   _dp(x_out), _stream(stream))
+
+
+def srftq_cache_append(shape, t_cap, pos, x, signs, lam, codes, scales, stream=None) -> int:
+    return lib().srftq_cache_append(ctypes.byref(shape), int(t_cap), _dp(pos), _dp(x), _dp(signs),
+                                    _dp(lam), _dp(codes), _dp(scales), _stream(stream))
+
+
+def srftq_cache_read(shape, t_cap, codes, scales, signs, lam, x_out, stream=None) -> int:
+    return lib().srftq_cache_read(ctypes.byref(shape), int(t_cap), _dp(codes), _dp(scales), _dp(signs),
+                                  _dp(lam), _dp(x_out), _stream(stream))
 
 
 def srftq_rotate(shape, x, signs, y, stream=None) -> int:
@@ -226,6 +240,63 @@ def dequantize(codes, scales, signs=None, lam=None, group=16, bits=4, rot="srft"
     out = _out(out, oshape, torch.float16, codes.device, "out")
     sh = make_shape(B, T, H, d, group, bits, rot, variant)
     _check(srftq_dequantize(sh, codes, scales, signs, lam, out, stream), "srftq_dequantize")
+    return out
+
+
+def _cache_dims(codes, scales, d, bits, group, name="codes"):
+    """(B, H, t_cap) of a cache pair [B,H,t_cap,d*bits/8] / [B,H,t_cap,d/group]."""
+    if codes.dim() != 4:
+        raise ValueError(f"{name} must be [B,H,t_cap,d*bits/8]")
+    B, H, t_cap, cb = codes.shape
+    if cb != d * bits // 8:
+        raise ValueError(f"{name} rows must hold {d * bits // 8} bytes, got {cb}")
+    want = (B, H, t_cap, max(d // max(group, 1), 1))
+    if tuple(scales.shape) != want:
+        raise ValueError(f"scales must have shape {want}, got {tuple(scales.shape)}")
+    return B, H, t_cap
+
+
+def cache_append(x, codes, scales, pos=None, signs=None, lam=None, group=16, bits=4, rot="srft",
+                 variant="default", stream=None):
+    """Quantize the new tokens x fp16 [B,T,H,d] into the caches codes uint8
+    [B,H,t_cap,d*bits/8] / scales fp16 [B,H,t_cap,d/group] in place: token t
+    of tensor b goes to row pos[b] + t (pos int32 [B] on the device, or None
+    for row t); rows outside [0, t_cap) are dropped."""
+    import torch
+    if x.dim() != 4:
+        raise ValueError("x must be [B,T,H,d]")
+    B, T, H, d = x.shape
+    _req(x, torch.float16, "x")
+    _req(codes, torch.uint8, "codes")
+    _req(scales, torch.float16, "scales")
+    _req(signs, torch.int8, "signs")
+    _req(lam, torch.float32, "lambda")
+    _req(pos, torch.int32, "pos")
+    Bc, Hc, t_cap = _cache_dims(codes, scales, d, bits, group)
+    if (Bc, Hc) != (B, H):
+        raise ValueError(f"cache is for B={Bc}, H={Hc}; x has B={B}, H={H}")
+    if pos is not None and tuple(pos.shape) != (B,):
+        raise ValueError(f"pos must have shape ({B},)")
+    sh = make_shape(B, T, H, d, group, bits, rot, variant)
+    _check(srftq_cache_append(sh, t_cap, pos, x, signs, lam, codes, scales, stream), "srftq_cache_append")
+    return codes, scales
+
+
+def cache_read(codes, scales, T, signs=None, lam=None, group=16, bits=4, rot="srft", variant="default",
+               d=None, out=None, stream=None):
+    """Dequantize + unrotate rows [0, T) of every head of a cache
+    [B,H,t_cap,.] -> fp16 [B,T,H,d]."""
+    import torch
+    _req(codes, torch.uint8, "codes")
+    _req(scales, torch.float16, "scales")
+    _req(signs, torch.int8, "signs")
+    _req(lam, torch.float32, "lambda")
+    if d is None:
+        d = codes.shape[-1] * 8 // bits
+    B, H, t_cap = _cache_dims(codes, scales, d, bits, group)
+    out = _out(out, (B, int(T), H, d), torch.float16, codes.device, "out")
+    sh = make_shape(B, int(T), H, d, group, bits, rot, variant)
+    _check(srftq_cache_read(sh, t_cap, codes, scales, signs, lam, out, stream), "srftq_cache_read")
     return out
 
 

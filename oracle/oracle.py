@@ -159,6 +159,36 @@ def dequantize(codes, scales, signs=None, lam=None, group=16, bits=4, rot="srft"
     return (x, x64) if return_f64 else x
 
 
+def cache_append(codes_cache, scales_cache, x16, pos=None, signs=None, lam=None, group=16, bits=4,
+                 rot="srft"):
+    """Appending to a growing quantized cache (the pages run their fused
+    kernel inside an int4 KV cache that grows by the new tokens of each
+    step; "When Quantization Is Free", Metodologia section 2).  In place:
+    x [B, n, H, d] is quantized as by ``quantize`` and token t of tensor b is
+    written to row pos[b] + t of each head of codes_cache [B, H, t_cap, .]
+    and scales_cache [B, H, t_cap, .]; a token whose row falls outside
+    [0, t_cap) is not written, and no other row changes."""
+    assert np.asarray(x16).ndim == 4
+    codes, scales = quantize(x16, signs, lam, group, bits, rot)   # [B, H, n, .]
+    B, H, n = codes.shape[:3]
+    t_cap = codes_cache.shape[2]
+    for b in range(B):
+        start = 0 if pos is None else int(pos[b])
+        for t in range(n):
+            row = start + t
+            if 0 <= row < t_cap:
+                codes_cache[b, :, row] = codes[b, :, t]
+                scales_cache[b, :, row] = scales[b, :, t]
+    return codes_cache, scales_cache
+
+
+def cache_read(codes_cache, scales_cache, T, signs=None, lam=None, group=16, bits=4, rot="srft",
+               d=None):
+    """The reconstruction (fp16 bits) of rows [0, T) of every head of a
+    cache [B, H, t_cap, .]: ``dequantize`` of that prefix."""
+    return dequantize(codes_cache[:, :, :T], scales_cache[:, :, :T], signs, lam, group, bits, rot, d=d)
+
+
 def calibrate_lambda(x16, signs=None, rot="srft") -> np.ndarray:
     """fp32 lambda [B,H,d] (or [H,d] for 3-D x) = 1/RMS over tokens of rotated coords."""
     x, B, T, H, d = _as4(_bits(x16))

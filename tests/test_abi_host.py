@@ -118,6 +118,31 @@ def test_argument_errors_return_before_launch():
     assert S.srftq_quantize(bad, a, None, None, a, a, stream=0) == S.SRFTQ_ERR_UNSUPPORTED
 
 
+def test_cache_argument_errors_return_before_launch():
+    sh = S.make_shape(2, 5, 8, 128, 16, 4)
+    a = _Fake(0x10000)
+    # capacity: negative, or fewer rows than a read asks for
+    assert S.srftq_cache_append(sh, -1, None, a, None, None, a, a, stream=0) == S.SRFTQ_ERR_SHAPE
+    assert S.srftq_cache_read(sh, -1, a, a, None, None, a, stream=0) == S.SRFTQ_ERR_SHAPE
+    assert S.srftq_cache_read(sh, 4, a, a, None, None, a, stream=0) == S.SRFTQ_ERR_SHAPE
+    assert S.srftq_cache_append(sh, 1 << 45, None, a, None, None, a, a, stream=0) == S.SRFTQ_ERR_SHAPE
+    # NULL and misaligned pointers
+    assert S.srftq_cache_append(sh, 16, None, None, None, None, a, a, stream=0) == S.SRFTQ_ERR_NULL
+    assert S.srftq_cache_append(sh, 16, None, a, None, None, a, None, stream=0) == S.SRFTQ_ERR_NULL
+    assert S.srftq_cache_read(sh, 16, a, a, None, None, None, stream=0) == S.SRFTQ_ERR_NULL
+    assert S.srftq_cache_append(sh, 16, _Fake(0x10002), a, None, None, a, a, stream=0) == S.SRFTQ_ERR_ALIGN
+    assert S.srftq_cache_append(sh, 16, None, a, None, None, _Fake(0x10008), a, stream=0) == S.SRFTQ_ERR_ALIGN
+    assert S.srftq_cache_read(sh, 16, a, a, None, None, _Fake(0x10004), stream=0) == S.SRFTQ_ERR_ALIGN
+    # shape errors first, as for every other call
+    bad = S.make_shape(2, 5, 8, 96, 16, 4)
+    assert S.srftq_cache_append(bad, 16, None, a, None, None, a, a, stream=0) == S.SRFTQ_ERR_UNSUPPORTED
+    # nothing to do: no tokens, or no rows to write into
+    assert S.srftq_cache_append(sh, 0, None, None, None, None, None, None, stream=0) == S.SRFTQ_OK
+    empty = S.make_shape(2, 0, 8, 128, 16, 4)
+    assert S.srftq_cache_append(empty, 16, None, None, None, None, None, None, stream=0) == S.SRFTQ_OK
+    assert S.srftq_cache_read(empty, 16, None, None, None, None, None, stream=0) == S.SRFTQ_OK
+
+
 def test_empty_problem_is_a_no_op():
     sh = S.make_shape(1, 0, 8, 128, 16, 4)
     assert S.srftq_quantize(sh, None, None, None, None, None, stream=0) == S.SRFTQ_OK

@@ -418,3 +418,61 @@ def test_fp32_reciprocal_of_every_fp16_is_correctly_rounded():
         e = abs(Fraction(r_) - exact)
         assert e <= abs(Fraction(u_) - exact) and e <= abs(Fraction(d_) - exact)
         assert e != abs(Fraction(u_) - exact) and e != abs(Fraction(d_) - exact)   # never a tie
+
+
+# --------------------------------------------------------------------------
+# The growing cache: appending places per-vector results, nothing else.
+# --------------------------------------------------------------------------
+
+def _sentinel_cache(B, H, cap, d, g, bits):
+    return (np.full((B, H, cap, d * bits // 8), 0xA5, dtype=np.uint8),
+            np.full((B, H, cap, d // g), 0x5A5A, dtype=np.uint16))
+
+
+def test_cache_grown_step_by_step_equals_one_quantize():
+    """The quantizer acts on each vector alone, so a cache filled one decode
+    step at a time (or in chunks of any length) holds exactly the codes of
+    quantizing the whole sequence at once; rows never appended keep their
+    contents, and reading the prefix is dequantizing those codes."""
+    B, T, H, d, g, bits, cap = 3, 9, 2, 64, 32, 8, 12
+    rng = np.random.default_rng(41)
+    x = _rand_x(rng, (B, T, H, d))
+    s = _rand_signs(rng, B, H, d)
+    lam = rng.uniform(0.5, 2.0, size=(B, H, d)).astype(np.float32)
+    whole_c, whole_s = oracle.quantize(x, s, lam, g, bits, "srft")
+
+    cc, cs = _sentinel_cache(B, H, cap, d, g, bits)
+    for t in range(T):
+        oracle.cache_append(cc, cs, x[:, t:t + 1], np.full(B, t, np.int32), s, lam, g, bits, "srft")
+    assert np.array_equal(cc[:, :, :T], whole_c) and np.array_equal(cs[:, :, :T], whole_s)
+    assert np.all(cc[:, :, T:] == 0xA5) and np.all(cs[:, :, T:] == 0x5A5A)
+
+    cc2, cs2 = _sentinel_cache(B, H, cap, d, g, bits)
+    for a, b in ((0, 4), (4, 5), (5, 9)):
+        oracle.cache_append(cc2, cs2, x[:, a:b], np.full(B, a, np.int32), s, lam, g, bits, "srft")
+    assert np.array_equal(cc2, cc) and np.array_equal(cs2, cs)
+
+    got = oracle.cache_read(cc, cs, T, s, lam, g, bits, "srft", d=d)
+    assert np.array_equal(got, oracle.dequantize(whole_c, whole_s, s, lam, g, bits, "srft", d=d))
+
+
+def test_cache_append_ragged_positions_and_dropped_rows():
+    """Tensor b's token t lands in row pos[b] + t; a row before 0 or past
+    the capacity is dropped.  The expected placement is written out by hand."""
+    B, n, H, d, g, bits, cap = 4, 3, 2, 64, 16, 4, 6
+    rng = np.random.default_rng(43)
+    x = _rand_x(rng, (B, n, H, d))
+    s = _rand_signs(rng, B, H, d)
+    pos = np.array([0, 2, 5, -1], dtype=np.int32)
+    qc, qs = oracle.quantize(x, s, None, g, bits, "srht")          # [B, H, n, .]
+    cc, cs = _sentinel_cache(B, H, cap, d, g, bits)
+    oracle.cache_append(cc, cs, x, pos, s, None, g, bits, "srht")
+    ec, es = _sentinel_cache(B, H, cap, d, g, bits)
+    placed = {(0, 0): 0, (0, 1): 1, (0, 2): 2,      # (tensor, token) -> row
+              (1, 0): 2, (1, 1): 3, (1, 2): 4,
+              (2, 0): 5,                            # tokens 1, 2 fall past row 5
+              (3, 1): 0, (3, 2): 1}                 # token 0 falls before row 0
+    for (b, t), r in placed.items():
+        ec[b, :, r] = qc[b, :, t]
+        es[b, :, r] = qs[b, :, t]
+    assert np.array_equal(cc, ec) and np.array_equal(cs, es)
