@@ -189,6 +189,41 @@ def cache_read(codes_cache, scales_cache, T, signs=None, lam=None, group=16, bit
     return dequantize(codes_cache[:, :, :T], scales_cache[:, :, :T], signs, lam, group, bits, rot, d=d)
 
 
+def decode_attention(q16, k_codes, k_scales, v_codes, v_scales, T=None, lengths=None, signs_k=None,
+                     lam_k=None, signs_v=None, lam_v=None, group=16, bits=4, rot="srft", scale=None):
+    """Attention of one query token per tensor over quantized K/V caches, the
+    consumer the pages' growing int4 cache is read by at every decode step
+    ("When Quantization Is Free", Resultados Clave: the speed-up comes from
+    reading a third of the fp16 bytes per step).  Plain definition, fp64:
+      out[b, r] = sum_{t < L_b} softmax_t(scale * q[b, r] . k^[b, t, h]) v^[b, t, h]
+    with h = r // R (R = query heads per KV head), L_b = lengths[b] clamped to
+    [0, T] (T when lengths is None; T defaults to the caches' rows), k^ and v^
+    the fp64 reconstructions of ``dequantize`` (before its fp16 rounding), and
+    scale = 1/sqrt(d) by default.  A tensor with no tokens gives zeros.
+    q16: fp16 [B, H*R, d]; caches [B, H, t_cap, .]."""
+    q = f16_to_f64(_bits(np.asarray(q16)))
+    B, HR, d = q.shape
+    H, t_cap = k_codes.shape[1], k_codes.shape[2]
+    R = HR // H
+    T = t_cap if T is None else int(T)
+    scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    _, k = dequantize(k_codes[:, :, :T], k_scales[:, :, :T], signs_k, lam_k, group, bits, rot, d=d,
+                      return_f64=True)
+    _, v = dequantize(v_codes[:, :, :T], v_scales[:, :, :T], signs_v, lam_v, group, bits, rot, d=d,
+                      return_f64=True)                                    # [B, T, H, d]
+    out = np.zeros((B, HR, d), dtype=np.float64)
+    for b in range(B):
+        L = T if lengths is None else min(max(int(lengths[b]), 0), T)
+        if L == 0:
+            continue
+        for r in range(HR):
+            h = r // R
+            s = scale * (k[b, :L, h] @ q[b, r])
+            p = np.exp(s - s.max())
+            out[b, r] = (p / p.sum()) @ v[b, :L, h]
+    return out
+
+
 def calibrate_lambda(x16, signs=None, rot="srft") -> np.ndarray:
     """fp32 lambda [B,H,d] (or [H,d] for 3-D x) = 1/RMS over tokens of rotated coords."""
     x, B, T, H, d = _as4(_bits(x16))

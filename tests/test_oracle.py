@@ -476,3 +476,78 @@ def test_cache_append_ragged_positions_and_dropped_rows():
         ec[b, :, r] = qc[b, :, t]
         es[b, :, r] = qs[b, :, t]
     assert np.array_equal(cc, ec) and np.array_equal(cs, es)
+
+
+# --------------------------------------------------------------------------
+# Decode attention over the quantized cache.
+# --------------------------------------------------------------------------
+
+def _attn_case(seed, B, T, H, R, d, g, bits, rot, lam=True):
+    rng = np.random.default_rng(seed)
+    k = _rand_x(rng, (B, T, H, d))
+    v = _rand_x(rng, (B, T, H, d), 2.0)
+    sk, sv = _rand_signs(rng, B, H, d), _rand_signs(rng, B, H, d)
+    lk = rng.uniform(0.5, 2.0, size=(B, H, d)).astype(np.float32) if lam else None
+    lv = rng.uniform(0.5, 2.0, size=(B, H, d)).astype(np.float32) if lam else None
+    kc, ks = oracle.quantize(k, sk, lk, g, bits, rot)
+    vc, vs = oracle.quantize(v, sv, lv, g, bits, rot)
+    q = _rand_x(rng, (B, H * R, d))
+    return q, (kc, ks, sk, lk), (vc, vs, sv, lv)
+
+
+def _attn(q, K, V, g, bits, rot, **kw):
+    return oracle.decode_attention(q, K[0], K[1], V[0], V[1], signs_k=K[2], lam_k=K[3], signs_v=V[2],
+                                   lam_v=V[3], group=g, bits=bits, rot=rot, **kw)
+
+
+def test_attention_matches_torch_sdpa():
+    """Against torch's scaled_dot_product_attention (fp64, CPU) on the
+    oracle's own reconstructions, with grouped query heads and a length mask."""
+    import torch
+    B, T, H, R, d, g, bits = 2, 37, 2, 3, 64, 16, 4
+    q, K, V = _attn_case(61, B, T, H, R, d, g, bits, "srft")
+    lengths = np.array([37, 20], dtype=np.int32)
+    got = _attn(q, K, V, g, bits, "srft", lengths=lengths)
+    _, kh = oracle.dequantize(K[0], K[1], K[2], K[3], g, bits, "srft", d=d, return_f64=True)
+    _, vh = oracle.dequantize(V[0], V[1], V[2], V[3], g, bits, "srft", d=d, return_f64=True)
+    kt = torch.from_numpy(kh).permute(0, 2, 1, 3).repeat_interleave(R, dim=1)    # [B, H*R, T, d]
+    vt = torch.from_numpy(vh).permute(0, 2, 1, 3).repeat_interleave(R, dim=1)
+    qt = torch.from_numpy(q.astype(np.float64))[:, :, None]                    # [B, H*R, 1, d]
+    mask = torch.from_numpy(np.arange(T)[None, :] < lengths[:, None])[:, None, None]   # [B, 1, 1, T]
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask)[:, :, 0]
+    assert np.allclose(got, ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_attention_special_cases():
+    """One token returns its value; equal keys average the values; no tokens
+    give zeros; rows past the length do not matter."""
+    B, T, H, R, d, g, bits = 1, 24, 1, 2, 64, 32, 8
+    q, K, V = _attn_case(62, B, T, H, R, d, g, bits, "srht")
+    _, vh = oracle.dequantize(V[0], V[1], V[2], V[3], g, bits, "srht", d=d, return_f64=True)
+    one = _attn(q, K, V, g, bits, "srht", lengths=np.array([1], np.int32))
+    assert np.allclose(one, vh[0, 0, 0][None, None], rtol=1e-13, atol=1e-13)
+    Ke = (np.repeat(K[0][:, :, :1], T, axis=2), np.repeat(K[1][:, :, :1], T, axis=2), K[2], K[3])
+    avg = _attn(q, Ke, V, g, bits, "srht", lengths=np.array([10], np.int32))
+    assert np.allclose(avg, vh[0, :10, 0].mean(axis=0)[None, None], rtol=1e-12, atol=1e-12)
+    zero = _attn(q, K, V, g, bits, "srht", lengths=np.array([0], np.int32))
+    assert np.all(zero == 0)
+    K2 = (K[0].copy(), K[1].copy(), K[2], K[3])
+    K2[0][:, :, 12:] ^= 0x5A
+    a = _attn(q, K, V, g, bits, "srht", lengths=np.array([12], np.int32))
+    b = _attn(q, K2, V, g, bits, "srht", lengths=np.array([12], np.int32))
+    assert np.array_equal(a, b)
+
+
+def test_attention_scores_in_the_rotated_domain():
+    """The identity the GPU path relies on: q . k^ = (M (s_k . q)) . y^ with
+    y^_j = c_j sigma_G / lambda_j, since M is orthonormal."""
+    from oracle.compare import decode_codes
+    B, T, H, R, d, g, bits = 1, 9, 1, 1, 128, 16, 4
+    q, K, _ = _attn_case(63, B, T, H, R, d, g, bits, "srft")
+    _, kh = oracle.dequantize(K[0], K[1], K[2], K[3], g, bits, "srft", d=d, return_f64=True)
+    direct = kh[0, :, 0] @ q[0, 0].astype(np.float64)
+    u = oracle.rotate(q[:, None], K[2], "srft")[0, 0, 0]                       # M (s . q)
+    c = decode_codes(K[0], bits, d)[0, 0].astype(np.float64)                   # [T, d]
+    sig = np.repeat(K[1].view(np.float16).astype(np.float64)[0, 0], g, axis=-1)
+    yh = c * sig / K[3][0, 0].astype(np.float64)
+    assert np.allclose(yh @ u, direct, rtol=1e-12, atol=1e-12)
