@@ -187,6 +187,55 @@ srftq_status srftq_cache_read(const srftq_shape* shape, int64_t t_cap, const uin
                               const uint16_t* scales, const int8_t* signs, const float* lambda,
                               uint16_t* x_out, void* stream);
 
+/*
+ * Decode attention over the quantized cache: for each tensor b and query
+ * head r (query heads h*R .. h*R+R-1 share KV head h), with one new query
+ * token per tensor,
+ *   out[b, r] = sum_{t < len_b} softmax_t(scale * q[b, r] . k^[b, t, h]) v^[b, t, h]
+ * where k^, v^ are the exact reconstructions s (.) M^T (c sigma / lambda)
+ * of the cached codes (srftq_dequantize before its fp16 rounding).  The
+ * pages' cache exists to be read by attention at every decode step, moving
+ * a third of the fp16 bytes ("When Quantization Is Free", Resultados Clave:
+ * the bandwidth saving is where the speed-up comes from); here attention
+ * reads the codes directly and never materializes k^ or v^: scores are
+ * taken against the rotated query M (s_k . q), the output is accumulated in
+ * the rotated domain and unrotated once per query head.
+ *   shape      B tensors, T = most tokens attended (<= t_cap), H KV heads,
+ *              d, group (>= 16), bits, rot as the caches were written;
+ *              variant is ignored.
+ *   q_per_kv   R, query heads per KV head, 1..16.
+ *   q          fp16 [B, H*R, d], 16-B aligned.
+ *   k, v       the K and V caches: codes [B,H,t_cap,d*bits/8] and scales
+ *              [B,H,t_cap,d/group] (16-B aligned), signs and lambda
+ *              [B,H,d] or NULL, as written by srftq_cache_append /
+ *              srftq_quantize.
+ *   lengths    int32 [B] on the device (4-B aligned): tokens attended per
+ *              tensor, clamped to [0, T]; NULL = T for every tensor.  A
+ *              tensor with no tokens gets a zero output.
+ *   scale      softmax scale (e.g. 1/sqrt(d)), finite.
+ *   out        fp32 [B, H*R, d], 16-B aligned.
+ *   workspace  device memory of at least srftq_attention_workspace_bytes
+ *              (16-B aligned), owned by the caller; contents on entry are
+ *              ignored.  Calls that share a workspace must not overlap.
+ * The P.V product takes p * sigma_v rounded once to fp16 (as attention
+ * kernels round P); every other step is fp32.  Errors as for
+ * srftq_quantize; a short workspace is SRFTQ_ERR_SHAPE.
+ */
+typedef struct {
+    const uint8_t*  codes;
+    const uint16_t* scales;
+    const int8_t*   signs;
+    const float*    lambda;
+} srftq_cache_view;
+
+size_t srftq_attention_workspace_bytes(const srftq_shape* shape, int32_t q_per_kv);
+
+srftq_status srftq_decode_attention(const srftq_shape* shape, int64_t t_cap, int32_t q_per_kv,
+                                    const uint16_t* q, const srftq_cache_view* k,
+                                    const srftq_cache_view* v, const int32_t* lengths,
+                                    float scale, float* out, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* srftq_status_string(srftq_status status);
 

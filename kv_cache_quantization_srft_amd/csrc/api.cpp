@@ -153,11 +153,110 @@ srftq_status dequantize_from(const srftq_shape* s, int64_t pitch, const uint8_t*
   return fn ? from_hip(fn(*s, p, (hipStream_t)stream)) : SRFTQ_ERR_UNSUPPORTED;
 }
 
+// Decode attention: tokens per wave (a multiple of 16) chosen so that the
+// grid has about 8192 waves, and the workspace carve-up.
+struct AttnPlan {
+  int span = 16;
+  int n_chunks = 1;
+  size_t off_exp = 0, off_ml = 0, off_acc = 0, bytes = 0;
+};
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+bool attn_plan(const srftq_shape* s, int32_t R, AttnPlan* p) {
+  if (validate(s) != SRFTQ_OK || R < 1 || R > 16 || s->group < 16) return false;
+  const int64_t BH = s->B * (int64_t)s->H;
+  const int64_t work = BH * s->T;
+  int64_t span = (work + 8191) / 8192;
+  span = (span + 15) / 16 * 16;
+  if (span < 16) span = 16;
+  if (span > 1024) span = 1024;
+  int64_t nc = (s->T + 4 * span - 1) / (4 * span);
+  if (nc < 1) nc = 1;
+  if (BH * nc > 0x7fffffffLL || BH * R > 0x7fffffffLL) return false;
+  p->span = (int)span;
+  p->n_chunks = (int)nc;
+  const size_t uq = (size_t)BH * R * s->d * 4;
+  const size_t ml = (size_t)BH * nc * R * 2 * 4;
+  const size_t acc = (size_t)BH * nc * R * s->d * 4;
+  p->off_exp = align256(uq);
+  p->off_ml = p->off_exp + align256((size_t)BH * R * 4);
+  p->off_acc = p->off_ml + align256(ml);
+  p->bytes = p->off_acc + align256(acc);
+  return true;
+}
+
+const srftq::RunAttnFn kAttention[3] = {srftq::run_attention_d64, srftq::run_attention_d128,
+                                        srftq::run_attention_d256};
+
 }  // namespace
 
 extern "C" {
 
 srftq_status srftq_validate(const srftq_shape* shape) { return validate(shape); }
+
+size_t srftq_attention_workspace_bytes(const srftq_shape* s, int32_t q_per_kv) {
+  AttnPlan p;
+  return attn_plan(s, q_per_kv, &p) ? p.bytes : 0;
+}
+
+srftq_status srftq_decode_attention(const srftq_shape* s, int64_t t_cap, int32_t R, const uint16_t* q,
+                                    const srftq_cache_view* k, const srftq_cache_view* v,
+                                    const int32_t* lengths, float scale, float* out, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  srftq_status st = validate(s);
+  if (st != SRFTQ_OK) return st;
+  if (R < 1 || R > 16) return SRFTQ_ERR_SHAPE;
+  if (s->group < 16) return SRFTQ_ERR_UNSUPPORTED;
+  if ((st = validate_cache(s, t_cap)) != SRFTQ_OK) return st;
+  if (t_cap < s->T) return SRFTQ_ERR_SHAPE;
+  if (!(scale == scale) || scale > 3.0e38f || scale < -3.0e38f) return SRFTQ_ERR_SHAPE;
+  AttnPlan plan;
+  if (!attn_plan(s, R, &plan)) return SRFTQ_ERR_SHAPE;
+  if (s->B * (int64_t)s->H == 0) return SRFTQ_OK;
+  if (!q || !k || !v || !out || !workspace) return SRFTQ_ERR_NULL;
+  if (!k->codes || !k->scales || !v->codes || !v->scales) return SRFTQ_ERR_NULL;
+  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace) || !aligned16(k->codes) ||
+      !aligned16(k->scales) || !aligned16(v->codes) || !aligned16(v->scales))
+    return SRFTQ_ERR_ALIGN;
+  if (lengths && !aligned4(lengths)) return SRFTQ_ERR_ALIGN;
+  if ((st = check_side(k->signs, k->lambda)) != SRFTQ_OK) return st;
+  if ((st = check_side(v->signs, v->lambda)) != SRFTQ_OK) return st;
+  if (workspace_bytes < plan.bytes) return SRFTQ_ERR_SHAPE;
+  const int8_t* ones = srftq::plus_ones_ptr();
+  if (!ones) return SRFTQ_ERR_HIP;
+  srftq::AttnArgs a = {};
+  a.geo.T = s->T;
+  a.geo.pitch = t_cap;
+  a.geo.H = s->H;
+  a.geo.R = R;
+  a.geo.BH = (int32_t)(s->B * s->H);
+  a.geo.span = plan.span;
+  a.geo.n_chunks = plan.n_chunks;
+  a.geo.sign_stride_k = k->signs ? s->d : 0;
+  a.geo.sign_stride_v = v->signs ? s->d : 0;
+  a.geo.scale_log2e = (float)((double)scale * 1.4426950408889634);
+  a.rot = s->rot;
+  a.group = s->group;
+  a.bits = s->bits;
+  a.q = q;
+  a.codes_k = k->codes;
+  a.scales_k = k->scales;
+  a.signs_k = k->signs ? k->signs : ones;
+  a.lam_k = k->lambda;
+  a.codes_v = v->codes;
+  a.scales_v = v->scales;
+  a.signs_v = v->signs ? v->signs : ones;
+  a.lam_v = v->lambda;
+  a.lengths = lengths;
+  a.out = out;
+  a.uq = (float*)workspace;
+  a.uexp = (float*)((char*)workspace + plan.off_exp);
+  a.ws_ml = (float*)((char*)workspace + plan.off_ml);
+  a.ws_acc = (float*)((char*)workspace + plan.off_acc);
+  const int di = s->d == 64 ? 0 : s->d == 128 ? 1 : 2;
+  return from_hip(kAttention[di](a, (hipStream_t)stream));
+}
 
 size_t srftq_codes_bytes(const srftq_shape* s) {
   if (validate(s) != SRFTQ_OK) return 0;

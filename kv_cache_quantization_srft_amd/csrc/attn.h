@@ -1,0 +1,525 @@
+// attn.h -- decode attention that reads the quantized cache directly.
+//
+// For one new query token per tensor b and query head r of KV head h (R query
+// heads share a KV head):
+//   o_r = sum_{t < len_b} softmax_t(scale * q_r . k^_t) v^_t,
+// where k^_t, v^_t are the exact reconstructions s (.) M^T y^ of the cached
+// codes, y^_j = c_j sigma_G(j) / lambda_j (the dequantizer of the pages'
+// int4 KV cache, "When Quantization Is Free", Metodologia 1-2, before any fp16
+// rounding).  M is orthonormal, so q . k^ = (M (s_k . q)) . y^: the scores are
+// taken in the rotated domain against the codes themselves, the output is
+// accumulated there as well, and each query head is unrotated once at the end:
+//   o_r = s_v (.) M^T ( sum_t p_t c^v_t sigma^v_t / lambda_v ).
+//
+// Kernels (one launch each):
+//   attn_qprep_kernel    u_r = M (s_k . q_r) * scale * log2(e) / lambda_k,
+//                        stored as 2^-e_r u_r with e_r putting max |u_r| in
+//                        [2^10, 2^11) (so that its fp16 parts neither
+//                        overflow nor go subnormal) plus the factor 2^e_r
+//                        (one block per (tensor, KV head), one lane per
+//                        query head).
+//   attn_partial_kernel  one block of 4 waves per chunk of 4 * span tokens of
+//                        one (tensor, KV head); per 16-token block a wave
+//                        computes the scores of 16 query heads (R used, the
+//                        rest zero) with v_mfma_f32_16x16x16_f16 -- the codes
+//                        are exact in fp16 (A), the query coordinates are
+//                        split into fp16 hi + lo parts (B, two MFMAs) -- and
+//                        scales each group's fp32 partial by its sigma; keeps
+//                        an online softmax in base 2; accumulates P.V with a
+//                        second MFMA whose A operand is fp16(c_v * sigma_v)
+//                        and whose B operand is fp16(2^14 p) (p <= 1 after
+//                        the running max, so the terms that matter stay
+//                        normal fp16 numbers; the 2^14 cancels against the
+//                        softmax sum, accumulated from the same values):
+//                        two roundings to fp16 per term, the only steps
+//                        beyond fp32 in the path.  The 4 waves merge through
+//                        LDS and write one (max, sum, accumulator) per query
+//                        head and chunk.
+//   attn_combine_kernel  merges the chunks of one query head, divides by the
+//                        softmax sum and lambda_v, unrotates and signs.
+//
+// Staging: every 16-token block's K codes (whole rows), V codes (transposed
+// by dword: [dword][token], so that a lane's four tokens of one coordinate
+// are one 16-byte LDS read) and both scale rows arrive by LDS-DMA into a
+// double buffer per wave, one block ahead; rows past the tensor's length are
+// never read (their lanes re-read the last valid row, whose finite values
+// the softmax masks).
+#pragma once
+
+#include "kernels.h"
+#include "launch.h"
+
+namespace srftq {
+
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Byte sizes of the per-wave staging and of the merge area of attn_partial_kernel.
+template <int D, int G, int BITS>
+struct AttnTile {
+  static constexpr int RB = D * BITS / 8;       // code bytes per token
+  static constexpr int NG = D / G;              // groups per token
+  static constexpr int SRB = 2 * NG;            // scale bytes per token
+  static constexpr int NB = D / 16;             // MFMA k-blocks per token
+  static constexpr int CT = 16 * RB;            // code bytes of a 16-token block
+  static constexpr int ST = 16 * SRB;           // scale bytes of a block
+  static constexpr int KC_INST = (CT + 1023) / 1024;   // K codes: 16 B per lane
+  static constexpr int KC_BYTES = 1024 * KC_INST;
+  static constexpr int VC_INST = CT / 256;             // V codes: 4 B per lane, transposed
+  static constexpr int SE = SRB >= 4 ? 4 : 2;          // scale rows: 4 B (2 B) per lane
+  // LDS-DMA fills a whole dword slot per lane: 2-byte rows sit 4 bytes apart
+  static constexpr int SSLOT = SE < 4 ? 4 : SE;
+  static constexpr int S_INST = (ST + 64 * SE - 1) / (64 * SE);
+  static constexpr int S_BYTES = 64 * SSLOT * S_INST;
+  static constexpr int OFF_VC = KC_BYTES;
+  static constexpr int OFF_KS = OFF_VC + CT;
+  static constexpr int OFF_VS = OFF_KS + S_BYTES;
+  static constexpr int STAGE = OFF_VS + S_BYTES;       // one buffer
+  static constexpr int NDMA = KC_INST + VC_INST + 2 * S_INST;   // DMA instructions per block
+  static constexpr int WAVE_BYTES = 2 * STAGE;
+  static constexpr int MERGE_ACC = 4 * NB * 64 * 16;   // [wave][kb][lane] float4
+  static constexpr int MERGE_BYTES = MERGE_ACC + 4 * 16 * 8;
+  static constexpr int LDS_BYTES = 4 * WAVE_BYTES > MERGE_BYTES ? 4 * WAVE_BYTES : MERGE_BYTES;
+  static_assert(G >= 16 && G % 16 == 0, "a group spans whole MFMA k-blocks");
+  static_assert(CT % 256 == 0, "V codes move in 256-byte DMA instructions");
+  static_assert(NDMA < 32, "two blocks of DMA in flight fit the vmcnt counter");
+};
+
+__device__ __forceinline__ uint32_t lds_u32(uint32_t byte_addr) {
+  return *(const __attribute__((address_space(3))) uint32_t*)(uintptr_t)byte_addr;
+}
+__device__ __forceinline__ u32x4_t lds_u32x4(uint32_t byte_addr) {
+  return *(const __attribute__((address_space(3))) u32x4_t*)(uintptr_t)byte_addr;
+}
+__device__ __forceinline__ uint32_t lds_u16(uint32_t byte_addr) {
+  return *(const __attribute__((address_space(3))) uint16_t*)(uintptr_t)byte_addr;
+}
+
+// Two fp16 lanes holding 0x6400 | n (= 1024 + n), minus the bias: exact small
+// integers.
+__device__ __forceinline__ uint32_t f16x2_minus(uint32_t w, float bias) {
+  half2_t h = __builtin_bit_cast(half2_t, w);
+  h = h - (half2_t){(_Float16)bias, (_Float16)bias};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+__device__ __forceinline__ uint32_t f16x2_mul(uint32_t a, uint32_t b) {
+  const half2_t h = __builtin_bit_cast(half2_t, a) * __builtin_bit_cast(half2_t, b);
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+__device__ __forceinline__ half4_t half4_of(uint32_t lo, uint32_t hi) {
+  const uint2 v = make_uint2(lo, hi);
+  return __builtin_bit_cast(half4_t, v);
+}
+
+// fp16 value of a scale: half `hi` of a dword.
+__device__ __forceinline__ float f16_half(uint32_t w, int hi) { return hi ? hhi(w) : hlo(w); }
+
+// Scale sigma of group g of row `row` in an LDS scale tile (rows of SRB
+// bytes; 2-byte rows sit in 4-byte slots).
+template <int SRB>
+__device__ __forceinline__ float tile_scale(uint32_t tile, int row, int g) {
+  if constexpr (SRB >= 4) {
+    const uint32_t w = lds_u32(tile + (uint32_t)(row * SRB + 4 * (g >> 1)));
+    return f16_half(w, g & 1);
+  } else {
+    return hlo(lds_u16(tile + (uint32_t)(row * 4)));
+  }
+}
+
+// The fp16 scales of group g of rows `row` and `row + 1`, packed (low, high).
+template <int SRB>
+__device__ __forceinline__ uint32_t scale_pair(uint32_t tile, int row, int g) {
+  if constexpr (SRB >= 4) {
+    const uint32_t w0 = lds_u32(tile + (uint32_t)(row * SRB + 4 * (g >> 1)));
+    const uint32_t w1 = lds_u32(tile + (uint32_t)((row + 1) * SRB + 4 * (g >> 1)));
+    return __builtin_amdgcn_perm(w1, w0, (g & 1) ? 0x07060302u : 0x05040100u);
+  } else {
+    return lds_u16(tile + (uint32_t)(row * 4)) | (lds_u16(tile + (uint32_t)((row + 1) * 4)) << 16);
+  }
+}
+
+// ----------------------------------------------------------------------------
+// u = M (s_k . q) * scale * log2(e) / lambda_k for the R query heads of one
+// (tensor, KV head): block = (tensor, KV head), lane r < R = query head.
+// ----------------------------------------------------------------------------
+template <int D, int ROT>
+__global__ __launch_bounds__(64) void attn_qprep_kernel(const uint16_t* __restrict__ q,
+                                                        const int8_t* __restrict__ signs_k,
+                                                        const float* __restrict__ lam_k,
+                                                        float* __restrict__ uq,
+                                                        float* __restrict__ uexp, AttnGeo a) {
+  using Sc = Scales<D, ROT, VAR_REAL>;
+  const int bh = blockIdx.x;
+  const int r = threadIdx.x;
+  if (r >= a.R) return;
+  const int64_t v = (int64_t)bh * a.R + r;     // = b*H*R + h*R + r
+  uint32_t w[D / 2];
+  load_words<D / 2>((const uint8_t*)q + v * (2 * D), w);
+  const HeadSigns sg(signs_k + (int64_t)bh * a.sign_stride_k);
+  float y[D];
+  forward<D, ROT, VAR_REAL>(w, sg, y);
+  float mx = 0.0f;
+  static_for<D>([&](auto jj) {
+    constexpr int j = decltype(jj)::value;
+    float u = y[j] * (float)(Sc::is_edge(j) ? Sc::kFwdEdge : Sc::kFwdBulk) * a.scale_log2e;
+    if (lam_k) u = u / lam_k[(int64_t)bh * D + j];
+    y[j] = u;
+    mx = __builtin_fmaxf(mx, __builtin_fabsf(u));
+  });
+  // power of two 2^e with max |u| / 2^e in [2^10, 2^11) (e = 0 for u = 0)
+  const int e = mx > 0.0f ? __builtin_amdgcn_frexp_expf(mx) - 11 : 0;
+  const float down = __builtin_ldexpf(1.0f, -e);
+  uint32_t o[D];
+  static_for<D>([&](auto jj) {
+    constexpr int j = decltype(jj)::value;
+    o[j] = as_u32(y[j] * down);
+  });
+  store_words<D>((uint8_t*)uq + v * (4 * D), o);
+  uexp[v] = __builtin_ldexpf(1.0f, e);
+}
+
+// ----------------------------------------------------------------------------
+// Partial attention of one chunk of one (tensor, KV head).
+// Lane roles in a wave: jl = lane & 15, q = lane >> 4.
+//   score MFMA  D[token][head]:  A = K codes, lane holds token jl, coordinates
+//               16kb + 4q + {0,2,1,3} (int4) or {0,1,2,3} (int8); B = u, lane
+//               holds head jl at the same coordinates; D: tokens 4q+e, head jl.
+//   P.V MFMA    D[coord][head]:  A = V codes, lane holds coordinate 16kb + jl
+//               of tokens 4q+e; B = fp16(p * sigma_v), tokens 4q+e, head jl
+//               (the score layout); D: coordinates 16kb + 4q + e, head jl.
+// ----------------------------------------------------------------------------
+template <int D, int G, int BITS>
+__global__ __launch_bounds__(256) void attn_partial_kernel(const uint8_t* __restrict__ codes_k,
+                                                           const uint16_t* __restrict__ scales_k,
+                                                           const uint8_t* __restrict__ codes_v,
+                                                           const uint16_t* __restrict__ scales_v,
+                                                           const int32_t* __restrict__ lengths,
+                                                           const float* __restrict__ uq,
+                                                           const float* __restrict__ uexp,
+                                                           float* __restrict__ ws_ml,
+                                                           float* __restrict__ ws_acc, AttnGeo a) {
+  using Tl = AttnTile<D, G, BITS>;
+  constexpr int RB = Tl::RB, SRB = Tl::SRB, NB = Tl::NB, CT = Tl::CT;
+  constexpr int KB_PER_G = G / 16;
+  constexpr float kBias = BITS == 4 ? 1032.0f : 1152.0f;   // 1024 + offset of the code
+  constexpr float kPScale = 14.0f;                          // B = fp16(2^14 p)
+  __shared__ __attribute__((aligned(16))) uint8_t smem[Tl::LDS_BYTES];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int c = (int)(blockIdx.x % (unsigned)a.n_chunks);
+  const int bh = (int)(blockIdx.x / (unsigned)a.n_chunks);
+  const int b = bh / a.H;
+  const int jl = lane & 15, q = lane >> 4;
+
+  int64_t len = a.T;
+  if (lengths) {
+    const int64_t lb = lengths[b];
+    len = lb < 0 ? 0 : (lb < a.T ? lb : a.T);
+  }
+  const int64_t t_begin = ((int64_t)c * 4 + wave) * a.span;
+  int64_t t_end = t_begin + a.span;
+  t_end = t_end < len ? t_end : len;
+  const int nblk = t_end > t_begin ? (int)((t_end - t_begin + 15) / 16) : 0;
+
+  const int64_t row0 = (int64_t)bh * a.pitch;
+  const uint8_t* kc = codes_k + row0 * RB;
+  const uint8_t* vc = codes_v + row0 * RB;
+  const uint8_t* ks = (const uint8_t*)scales_k + row0 * SRB;
+  const uint8_t* vs = (const uint8_t*)scales_v + row0 * SRB;
+  const uint32_t lds_wave = lds_addr(smem) + (uint32_t)wave * Tl::WAVE_BYTES;
+
+  // B operands of the scores: u of head jl, hi and lo fp16 parts.
+  half4_t bhi[NB], blo[NB];
+  const float uscale = uexp[(int64_t)bh * a.R + (jl < a.R ? jl : 0)];
+  {
+    const bool live = jl < a.R;
+    const float* u = uq + ((int64_t)bh * a.R + (live ? jl : 0)) * D;
+    static_for<NB>([&](auto kk) {
+      constexpr int kb = decltype(kk)::value;
+      float4 v = *(const float4*)(u + 16 * kb + 4 * q);
+      if (!live) v = make_float4(0.f, 0.f, 0.f, 0.f);
+      const float e[4] = {v.x, BITS == 4 ? v.z : v.y, BITS == 4 ? v.y : v.z, v.w};
+      static_for<4>([&](auto ee) {
+        constexpr int i = decltype(ee)::value;
+        const _Float16 h = (_Float16)e[i];
+        bhi[kb][i] = h;
+        blo[kb][i] = (_Float16)(e[i] - (float)h);
+      });
+    });
+  }
+
+  auto issue = [&](int blk, int buf) {
+    const int64_t t0 = t_begin + 16 * (int64_t)blk;
+    const int64_t left = t_end - t0;
+    const int nv = left < 16 ? (int)left : 16;
+    const uint32_t base = lds_wave + (uint32_t)buf * Tl::STAGE;
+    const uint8_t* kcb = kc + t0 * RB;
+    const uint8_t* vcb = vc + t0 * RB;
+    const uint8_t* ksb = ks + t0 * SRB;
+    const uint8_t* vsb = vs + t0 * SRB;
+    // K codes, whole rows; offsets past the valid rows re-read the last valid chunk
+    const uint32_t klim = (uint32_t)(nv * RB - 16);
+    static_for<Tl::KC_INST>([&](auto ii) {
+      constexpr int i = decltype(ii)::value;
+      uint32_t off = (uint32_t)(1024 * i + 16 * lane);
+      off = off < klim ? off : klim;
+      dma_to_lds<16, true>(kcb, off, base + 1024 * i);
+    });
+    // V codes transposed: LDS dword 64i + lane holds dword w = 4i + lane/16 of row lane%16
+    const int rr = (lane & 15) < nv ? (lane & 15) : nv - 1;
+    static_for<Tl::VC_INST>([&](auto ii) {
+      constexpr int i = decltype(ii)::value;
+      const uint32_t off = (uint32_t)(rr * RB + 4 * (4 * i + (lane >> 4)));
+      dma_to_lds<4>(vcb, off, base + Tl::OFF_VC + 256 * i);
+    });
+    // scale rows
+    const uint32_t slim = (uint32_t)(nv * SRB - Tl::SE);
+    static_for<Tl::S_INST>([&](auto ii) {
+      constexpr int i = decltype(ii)::value;
+      uint32_t off = (uint32_t)(64 * Tl::SE * i + Tl::SE * lane);
+      off = off < slim ? off : slim;
+      dma_to_lds<Tl::SE>(ksb, off, base + Tl::OFF_KS + 64 * Tl::SSLOT * i);
+      dma_to_lds<Tl::SE>(vsb, off, base + Tl::OFF_VS + 64 * Tl::SSLOT * i);
+    });
+  };
+
+  float4_t acc[NB];
+  static_for<NB>([&](auto kk) { acc[decltype(kk)::value] = (float4_t){0.f, 0.f, 0.f, 0.f}; });
+  float m_run = -__builtin_inff();
+  float l_part = 0.0f;
+
+  // per-lane constant selectors
+  const uint32_t ksel = (q & 1) ? 0x0C030C02u : 0x0C010C00u;            // K int4: half q&1 of the dword
+  uint32_t vsel, vsh;
+  if constexpr (BITS == 4) {
+    const uint32_t bsel = (uint32_t)((jl & 7) >> 1);
+    vsel = 0x0C000C00u | bsel | ((4u + bsel) << 16);
+    vsh = (uint32_t)(jl & 1) * 4u;
+  } else {
+    const uint32_t bsel = (uint32_t)(jl & 3);
+    vsel = 0x0C000C00u | bsel | ((4u + bsel) << 16);
+    vsh = 0;
+  }
+
+  if (nblk > 0) issue(0, 0);
+  for (int blk = 0; blk < nblk; ++blk) {
+    const int cur = blk & 1;
+    wait_lgkm0();
+    wave_fence();
+    if (blk + 1 < nblk) {
+      issue(blk + 1, cur ^ 1);
+      wait_vm<Tl::NDMA>();
+    } else {
+      wait_vm<0>();
+    }
+    wave_fence();
+    const uint32_t base = lds_wave + (uint32_t)cur * Tl::STAGE;
+    const int64_t t0 = t_begin + 16 * (int64_t)blk;
+    const int nv = (t_end - t0) < 16 ? (int)(t_end - t0) : 16;
+
+    // ---- scores: S[e] = sum_G sigma_k(4q+e, G) * sum_{k in G} c_k u_k ----
+    float S[4] = {0.f, 0.f, 0.f, 0.f};
+    float4_t dg = (float4_t){0.f, 0.f, 0.f, 0.f};
+    static_for<NB>([&](auto kk) {
+      constexpr int kb = decltype(kk)::value;
+      half4_t A;
+      if constexpr (BITS == 4) {
+        const uint32_t x = lds_u32(base + (uint32_t)(jl * RB + 4 * (2 * kb + (q >> 1)))) ^ 0x88888888u;
+        const uint32_t z = __builtin_amdgcn_perm(0u, x, ksel);
+        const uint32_t a0 = f16x2_minus((z & 0x000F000Fu) | 0x64006400u, kBias);
+        const uint32_t a1 = f16x2_minus(((z >> 4) & 0x000F000Fu) | 0x64006400u, kBias);
+        A = half4_of(a0, a1);
+      } else {
+        const uint32_t x = lds_u32(base + (uint32_t)(jl * RB + 4 * (4 * kb + q)));
+        const uint32_t a0 = f16x2_minus(__builtin_amdgcn_perm(0u, x, 0x0C010C00u) ^ 0x64806480u, kBias);
+        const uint32_t a1 = f16x2_minus(__builtin_amdgcn_perm(0u, x, 0x0C030C02u) ^ 0x64806480u, kBias);
+        A = half4_of(a0, a1);
+      }
+      if constexpr (kb % KB_PER_G == 0)
+        dg = __builtin_amdgcn_mfma_f32_16x16x16f16(A, bhi[kb], (float4_t){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      else
+        dg = __builtin_amdgcn_mfma_f32_16x16x16f16(A, bhi[kb], dg, 0, 0, 0);
+      dg = __builtin_amdgcn_mfma_f32_16x16x16f16(A, blo[kb], dg, 0, 0, 0);
+      if constexpr (kb % KB_PER_G == KB_PER_G - 1) {
+        constexpr int g = kb / KB_PER_G;
+        static_for<4>([&](auto ee) {
+          constexpr int e = decltype(ee)::value;
+          S[e] += tile_scale<SRB>(base + Tl::OFF_KS, 4 * q + e, g) * dg[e];
+        });
+      }
+    });
+
+    // ---- online softmax (base 2) over the block's valid tokens ----
+    static_for<4>([&](auto ee) {
+      constexpr int e = decltype(ee)::value;
+      S[e] = 4 * q + e < nv ? S[e] * uscale : -__builtin_inff();
+    });
+    float mx = __builtin_fmaxf(__builtin_fmaxf(S[0], S[1]), __builtin_fmaxf(S[2], S[3]));
+    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16));
+    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
+    if (__builtin_amdgcn_ballot_w64(mx > m_run)) {
+      const float m_new = __builtin_fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_part *= alpha;
+      static_for<NB>([&](auto kk) {
+        constexpr int kb = decltype(kk)::value;
+        acc[kb] *= alpha;
+      });
+      m_run = m_new;
+    }
+    float p[4];   // 2^14 * softmax numerator, <= 2^14
+    static_for<4>([&](auto ee) {
+      constexpr int e = decltype(ee)::value;
+      p[e] = __builtin_amdgcn_exp2f(S[e] - (m_run - kPScale));
+    });
+    l_part += (p[0] + p[1]) + (p[2] + p[3]);
+
+    // ---- P.V: acc[coord][head] += sum_t fp16(c_v(t, coord) sigma_v(t, G)) fp16(2^14 p_t) ----
+    const half4_t Bv = half4_of(pack_f16x2(p[0], p[1]), pack_f16x2(p[2], p[3]));
+    uint32_t sv01 = 0, sv23 = 0;   // sigma_v of the lane's tokens (4q, 4q+1), (4q+2, 4q+3), group of kb
+    static_for<NB>([&](auto kk) {
+      constexpr int kb = decltype(kk)::value;
+      if constexpr (kb % KB_PER_G == 0) {
+        constexpr int g = kb / KB_PER_G;
+        sv01 = scale_pair<SRB>(base + Tl::OFF_VS, 4 * q, g);
+        sv23 = scale_pair<SRB>(base + Tl::OFF_VS, 4 * q + 2, g);
+      }
+      // the four tokens 4q..4q+3 of one dword of the transposed V tile
+      const uint32_t wdw = BITS == 4 ? (uint32_t)(2 * kb + (jl >> 3)) : (uint32_t)(4 * kb + (jl >> 2));
+      const u32x4_t x = lds_u32x4(base + Tl::OFF_VC + 4u * (wdw * 16u + 4u * (uint32_t)q));
+      uint32_t a0, a1;
+      if constexpr (BITS == 4) {
+        const uint32_t z0 = (__builtin_amdgcn_perm(x.y, x.x, vsel) >> vsh) ^ 0x00080008u;
+        const uint32_t z1 = (__builtin_amdgcn_perm(x.w, x.z, vsel) >> vsh) ^ 0x00080008u;
+        a0 = f16x2_minus((z0 & 0x000F000Fu) | 0x64006400u, kBias);
+        a1 = f16x2_minus((z1 & 0x000F000Fu) | 0x64006400u, kBias);
+      } else {
+        a0 = f16x2_minus(__builtin_amdgcn_perm(x.y, x.x, vsel) ^ 0x64806480u, kBias);
+        a1 = f16x2_minus(__builtin_amdgcn_perm(x.w, x.z, vsel) ^ 0x64806480u, kBias);
+      }
+      a0 = f16x2_mul(a0, sv01);
+      a1 = f16x2_mul(a1, sv23);
+      acc[kb] = __builtin_amdgcn_mfma_f32_16x16x16f16(half4_of(a0, a1), Bv, acc[kb], 0, 0, 0);
+    });
+  }
+
+  // softmax sum of head jl over the wave's tokens
+  float l_w = l_part + __shfl_xor(l_part, 16);
+  l_w += __shfl_xor(l_w, 32);
+
+  // ---- merge the 4 waves through LDS (the staging area is reused) ----
+  __syncthreads();
+  const uint32_t macc = lds_addr(smem);
+  const uint32_t mml = macc + Tl::MERGE_ACC;
+  static_for<NB>([&](auto kk) {
+    constexpr int kb = decltype(kk)::value;
+    *(__attribute__((address_space(3))) float4_t*)(uintptr_t)(macc + 16u * ((uint32_t)(wave * NB + kb) * 64u + lane)) = acc[kb];
+  });
+  if (q == 0) {
+    *(__attribute__((address_space(3))) float2_t*)(uintptr_t)(mml + 8u * (uint32_t)(wave * 16 + jl)) = (float2_t){m_run, l_w};
+  }
+  __syncthreads();
+
+  float mw[4], fw[4];
+  float m = -__builtin_inff();
+  static_for<4>([&](auto ww) {
+    constexpr int w = decltype(ww)::value;
+    mw[w] = (*(const __attribute__((address_space(3))) float2_t*)(uintptr_t)(mml + 8u * (uint32_t)(w * 16 + jl)))[0];
+    m = __builtin_fmaxf(m, mw[w]);
+  });
+  static_for<4>([&](auto ww) {
+    constexpr int w = decltype(ww)::value;
+    fw[w] = mw[w] == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(mw[w] - m);
+  });
+  const int64_t slot = ((int64_t)bh * a.n_chunks + c) * a.R + jl;   // valid for jl < R
+  static_for<NB>([&](auto kk) {
+    constexpr int kb = decltype(kk)::value;
+    if (kb % 4 == wave) {
+      float4_t s = (float4_t){0.f, 0.f, 0.f, 0.f};
+      static_for<4>([&](auto ww) {
+        constexpr int w = decltype(ww)::value;
+        const float4_t v = *(const __attribute__((address_space(3))) float4_t*)(uintptr_t)(macc + 16u * ((uint32_t)(w * NB + kb) * 64u + lane));
+        s += fw[w] * v;
+      });
+      if (jl < a.R) *(float4_t*)(ws_acc + slot * D + 16 * kb + 4 * q) = s;
+    }
+  });
+  if (wave == 0 && q == 0 && jl < a.R) {
+    float l = 0.0f;
+    static_for<4>([&](auto ww) {
+      constexpr int w = decltype(ww)::value;
+      l += fw[w] * (*(const __attribute__((address_space(3))) float2_t*)(uintptr_t)(mml + 8u * (uint32_t)(w * 16 + jl)))[1];
+    });
+    *(float2_t*)(ws_ml + 2 * slot) = (float2_t){m, l};
+  }
+}
+
+// ----------------------------------------------------------------------------
+// One query head: merge its chunks, w = acc / (l * lambda_v), o = s_v . M^T w.
+// Block = (tensor, query head); lanes split the coordinates, lane 0 unrotates.
+// ----------------------------------------------------------------------------
+template <int D, int ROT>
+__global__ __launch_bounds__(64) void attn_combine_kernel(const float* __restrict__ ws_ml,
+                                                          const float* __restrict__ ws_acc,
+                                                          const int8_t* __restrict__ signs_v,
+                                                          const float* __restrict__ lam_v,
+                                                          float* __restrict__ out, AttnGeo a) {
+  using Sc = Scales<D, ROT, VAR_REAL>;
+  constexpr int PER = D / 64;
+  __shared__ __attribute__((aligned(16))) float ybuf[D];
+  const int64_t v = blockIdx.x;               // b*H*R + h*R + r
+  const int bh = (int)(v / a.R);
+  const int r = (int)(v - (int64_t)bh * a.R);
+  const int lane = threadIdx.x;
+  const int NC = a.n_chunks;
+  const int64_t s0 = (int64_t)bh * NC * a.R + r;   // slot of chunk 0; chunk c at s0 + c*R
+
+  float m = -__builtin_inff();
+  for (int ch = 0; ch < NC; ++ch) m = __builtin_fmaxf(m, ws_ml[2 * (s0 + (int64_t)ch * a.R)]);
+  float l = 0.0f, w[PER];
+  static_for<PER>([&](auto kk) { w[decltype(kk)::value] = 0.0f; });
+  for (int ch = 0; ch < NC; ++ch) {
+    const int64_t s = s0 + (int64_t)ch * a.R;
+    const float mc = ws_ml[2 * s];
+    const float f = mc == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(mc - m);
+    l += f * ws_ml[2 * s + 1];
+    static_for<PER>([&](auto kk) {
+      constexpr int k = decltype(kk)::value;
+      w[k] += f * ws_acc[s * D + lane + 64 * k];
+    });
+  }
+  const float inv_l = l > 0.0f ? 1.0f / l : 0.0f;
+  static_for<PER>([&](auto kk) {
+    constexpr int k = decltype(kk)::value;
+    const int j = lane + 64 * k;
+    float y = w[k] * inv_l;
+    if (lam_v) y = y / lam_v[(int64_t)bh * D + j];
+    ybuf[j] = y * (float)(Sc::is_edge(j) ? Sc::kInvEdge : Sc::kInvBulk);
+  });
+  __syncthreads();
+  if (lane != 0) return;
+  float y[D];
+  static_for<D / 4>([&](auto kk) {
+    constexpr int k = decltype(kk)::value;
+    const float4 t = *(const float4*)(ybuf + 4 * k);
+    y[4 * k] = t.x;
+    y[4 * k + 1] = t.y;
+    y[4 * k + 2] = t.z;
+    y[4 * k + 3] = t.w;
+  });
+  float x[D];
+  inverse<D, ROT, VAR_REAL>(y, x);
+  const HeadSigns sg(signs_v + (int64_t)bh * a.sign_stride_v);
+  uint32_t o[D];
+  static_for<D>([&](auto jj) {
+    constexpr int j = decltype(jj)::value;
+    o[j] = as_u32(x[j]) ^ (sg.sbit(j) << 31);
+  });
+  store_words<D>((uint8_t*)out + v * (4 * D), o);
+}
+
+}  // namespace srftq

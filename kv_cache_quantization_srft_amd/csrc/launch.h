@@ -50,6 +50,44 @@ inline int rot_selector(const srftq_shape& s) {
   return s.rot == SRFTQ_ROT_SRHT ? 2 : 3;
 }
 
+// Decode attention over the quantized cache (attn.h).
+struct AttnGeo {
+  int64_t T;             // tokens attended at most (lengths are clamped to it)
+  int64_t pitch;         // cache rows per head
+  int32_t H;             // KV heads per tensor
+  int32_t R;             // query heads per KV head, 1..16
+  int32_t BH;            // B * H
+  int32_t span;          // tokens per wave, a multiple of 16
+  int32_t n_chunks;      // chunks per (tensor, KV head); a chunk is 4 * span tokens
+  int32_t sign_stride_k; // elements between K heads' sign rows: d, or 0 (shared row)
+  int32_t sign_stride_v;
+  float scale_log2e;     // softmax scale * log2(e)
+};
+
+struct AttnArgs {
+  AttnGeo geo;
+  int rot, group, bits;
+  const uint16_t* q;
+  const uint8_t* codes_k;
+  const uint16_t* scales_k;
+  const int8_t* signs_k;   // never null (shared +1 row when the caller passes none)
+  const float* lam_k;
+  const uint8_t* codes_v;
+  const uint16_t* scales_v;
+  const int8_t* signs_v;
+  const float* lam_v;
+  const int32_t* lengths;
+  float* out;
+  float* uq;       // workspace: rotated queries [B*H*R, d], normalized by a power of two
+  float* uexp;     // workspace: that power of two per query head [B*H*R]
+  float* ws_ml;    // workspace: per (head, chunk, query head) max and sum
+  float* ws_acc;   // workspace: per (head, chunk, query head) accumulator [d]
+};
+using RunAttnFn = hipError_t (*)(const AttnArgs&, hipStream_t);
+hipError_t run_attention_d64(const AttnArgs&, hipStream_t);
+hipError_t run_attention_d128(const AttnArgs&, hipStream_t);
+hipError_t run_attention_d256(const AttnArgs&, hipStream_t);
+
 // Number of compute units of the current device (cached per device).
 int device_cu_count();
 

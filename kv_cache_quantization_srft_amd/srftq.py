@@ -8,8 +8,8 @@ missing library raises.
 The C functions keep their names here (``srftq_quantize`` ...) and take the
 same arguments, with a ``Shape`` in place of ``const srftq_shape*``.  The
 convenience wrappers ``quantize`` / ``dequantize`` / ``cache_append`` /
-``cache_read`` / ``rotate`` / ``unrotate`` / ``calibrate_lambda`` allocate
-outputs with torch.
+``cache_read`` / ``decode_attention`` / ``rotate`` / ``unrotate`` /
+``calibrate_lambda`` allocate outputs (and workspace) with torch.
 """
 from __future__ import annotations
 
@@ -46,6 +46,12 @@ def make_shape(B, T, H, d, group=16, bits=4, rot="srft", variant="default") -> S
     return Shape(int(B), int(T), int(H), int(d), int(group), int(bits), r, v)
 
 
+class CacheView(ctypes.Structure):
+    """srftq_cache_view: device pointers of one cache (codes, scales, signs, lambda)."""
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("signs", ctypes.c_void_p), ("lam", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -71,12 +77,17 @@ def lib() -> ctypes.CDLL:
         L.srftq_calibrate_lambda.argtypes = [sp, vp, vp, vp, vp]
         L.srftq_cache_append.argtypes = [sp, ctypes.c_int64, vp, vp, vp, vp, vp, vp, vp]
         L.srftq_cache_read.argtypes = [sp, ctypes.c_int64, vp, vp, vp, vp, vp, vp]
+        cv = ctypes.POINTER(CacheView)
+        L.srftq_attention_workspace_bytes.argtypes = [sp, ctypes.c_int32]
+        L.srftq_attention_workspace_bytes.restype = ctypes.c_size_t
+        L.srftq_decode_attention.argtypes = [sp, ctypes.c_int64, ctypes.c_int32, vp, cv, cv, vp,
+                                             ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
         L.srftq_status_string.argtypes = [ctypes.c_int]
         L.srftq_status_string.restype = ctypes.c_char_p
         L.srftq_version.argtypes = []
         for f in ("srftq_validate", "srftq_quantize", "srftq_dequantize", "srftq_rotate",
                   "srftq_unrotate", "srftq_calibrate_lambda", "srftq_cache_append",
-                  "srftq_cache_read", "srftq_version"):
+                  "srftq_cache_read", "srftq_decode_attention", "srftq_version"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -140,6 +151,23 @@ def srftq_cache_append(shape, t_cap, pos, x, signs, lam, codes, scales, stream=N
 def srftq_cache_read(shape, t_cap, codes, scales, signs, lam, x_out, stream=None) -> int:
     return lib().srftq_cache_read(ctypes.byref(shape), int(t_cap), _dp(codes), _dp(scales), _dp(signs),
                                   _dp(lam), _dp(x_out), _stream(stream))
+
+
+def srftq_attention_workspace_bytes(shape, q_per_kv) -> int:
+    return int(lib().srftq_attention_workspace_bytes(ctypes.byref(shape), int(q_per_kv)))
+
+
+def cache_view(codes, scales, signs=None, lam=None) -> CacheView:
+    return CacheView(_dp(codes), _dp(scales), _dp(signs), _dp(lam))
+
+
+def srftq_decode_attention(shape, t_cap, q_per_kv, q, k_view, v_view, lengths, scale, out, workspace,
+                           workspace_bytes, stream=None) -> int:
+    return lib().srftq_decode_attention(ctypes.byref(shape), int(t_cap), int(q_per_kv), _dp(q),
+                                        None if k_view is None else ctypes.byref(k_view),
+                                        None if v_view is None else ctypes.byref(v_view), _dp(lengths),
+                                        float(scale), _dp(out), _dp(workspace), int(workspace_bytes),
+                                        _stream(stream))
 
 
 def srftq_rotate(shape, x, signs, y, stream=None) -> int:
@@ -297,6 +325,49 @@ def cache_read(codes, scales, T, signs=None, lam=None, group=16, bits=4, rot="sr
     out = _out(out, (B, int(T), H, d), torch.float16, codes.device, "out")
     sh = make_shape(B, int(T), H, d, group, bits, rot, variant)
     _check(srftq_cache_read(sh, t_cap, codes, scales, signs, lam, out, stream), "srftq_cache_read")
+    return out
+
+
+def decode_attention(q, k_codes, k_scales, v_codes, v_scales, k_signs=None, k_lam=None, v_signs=None,
+                     v_lam=None, lengths=None, T=None, scale=None, group=16, bits=4, rot="srft",
+                     workspace=None, out=None, stream=None):
+    """Attention of one new query token per tensor over quantized K/V caches.
+    q fp16 [B, H*R, d]; caches [B, H, t_cap, .] (srftq_cache_append layout);
+    lengths int32 [B] (device) or None (= T, default t_cap); scale defaults
+    to 1/sqrt(d).  Returns fp32 [B, H*R, d]."""
+    import math
+
+    import torch
+    _req(q, torch.float16, "q")
+    for t, dt, n in ((k_codes, torch.uint8, "k_codes"), (k_scales, torch.float16, "k_scales"),
+                     (v_codes, torch.uint8, "v_codes"), (v_scales, torch.float16, "v_scales"),
+                     (k_signs, torch.int8, "k_signs"), (v_signs, torch.int8, "v_signs"),
+                     (k_lam, torch.float32, "k_lam"), (v_lam, torch.float32, "v_lam"),
+                     (lengths, torch.int32, "lengths")):
+        _req(t, dt, n)
+    if q.dim() != 3:
+        raise ValueError("q must be [B, H*R, d]")
+    B, HR, d = q.shape
+    Bc, H, t_cap = _cache_dims(k_codes, k_scales, d, bits, group, "k_codes")
+    if _cache_dims(v_codes, v_scales, d, bits, group, "v_codes") != (Bc, H, t_cap) or Bc != B:
+        raise ValueError("K and V caches must both be [B, H, t_cap, .] for q's B")
+    if HR % H:
+        raise ValueError(f"q has {HR} heads, not a multiple of the {H} KV heads")
+    R = HR // H
+    T = t_cap if T is None else int(T)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    sh = make_shape(B, T, H, d, group, bits, rot)
+    need = srftq_attention_workspace_bytes(sh, R)
+    if need == 0 and B * H > 0:
+        _check(SRFTQ_ERR_SHAPE, "srftq_attention_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
+    out = _out(out, (B, HR, d), torch.float32, q.device, "out")
+    kv = cache_view(k_codes, k_scales, k_signs, k_lam)
+    vv = cache_view(v_codes, v_scales, v_signs, v_lam)
+    _check(srftq_decode_attention(sh, t_cap, R, q, kv, vv, lengths, scale, out, workspace,
+                                  workspace.numel() * workspace.element_size(), stream),
+           "srftq_decode_attention")
     return out
 
 

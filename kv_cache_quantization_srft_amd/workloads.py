@@ -29,6 +29,10 @@ sub-stream per quantity):
               group 16; int4.
 
 Signs: one +-1 vector per (tensor, head), int8, drawn uniformly.
+
+Decode-attention queries (``attention_queries``): for a workload whose
+tensors are the K and V caches of B/2 layers, one N(0,1) fp16 query token per
+layer and query head ([B/2, H*R, d]), from their own sub-stream.
 """
 from __future__ import annotations
 
@@ -38,7 +42,7 @@ import numpy as np
 
 MASTER_SEED = 20260508
 
-_STREAM = {"x": 1, "signs": 2, "sigma": 3, "outlier": 4}
+_STREAM = {"x": 1, "signs": 2, "sigma": 3, "outlier": 4, "query": 5}
 
 
 @dataclass(frozen=True)
@@ -143,6 +147,14 @@ def values(w: Workload, B: int | None = None, T: int | None = None,
             v *= g[b][None]
             out[b, t0:t1] = v.astype(np.float16)
     return out
+
+
+def attention_queries(w: Workload, R: int) -> np.ndarray:
+    """Decode-step queries for a workload whose B tensors are the K and V
+    caches of B/2 layers (K = even tensors, V = odd): fp16 [B/2, H*R, d],
+    N(0, 1), one new token per layer and R query heads per KV head."""
+    r = _rng(w.seed, "query")
+    return r.standard_normal((w.B // 2, w.H * R, w.d)).astype(np.float16)
 
 
 def generate(w: Workload):

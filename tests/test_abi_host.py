@@ -143,6 +143,37 @@ def test_cache_argument_errors_return_before_launch():
     assert S.srftq_cache_read(empty, 16, None, None, None, None, None, stream=0) == S.SRFTQ_OK
 
 
+def test_attention_workspace_and_argument_errors():
+    sh = S.make_shape(2, 1000, 2, 128, 16, 4)
+    need = S.srftq_attention_workspace_bytes(sh, 6)
+    # rotated queries + per-query-head exponents + per-chunk (max, sum) and accumulators
+    assert need >= 2 * 2 * 6 * 128 * 4 + 2 * 2 * 6 * (2 + 128) * 4
+    assert S.srftq_attention_workspace_bytes(sh, 0) == 0
+    assert S.srftq_attention_workspace_bytes(sh, 17) == 0
+    assert S.srftq_attention_workspace_bytes(S.make_shape(2, 1000, 2, 128, 8, 4), 6) == 0
+    a, mis = _Fake(0x10000), _Fake(0x10008)
+    kv = S.CacheView(0x10000, 0x10000, None, None)
+    call = lambda shape=sh, t_cap=1000, R=6, q=a, k=kv, v=kv, lengths=None, scale=0.1, out=a, ws=a, nbytes=need: \
+        S.srftq_decode_attention(shape, t_cap, R, q, k, v, lengths, scale, out, ws, nbytes, stream=0)
+    assert call(R=0) == S.SRFTQ_ERR_SHAPE
+    assert call(R=17) == S.SRFTQ_ERR_SHAPE
+    assert call(shape=S.make_shape(2, 1000, 2, 128, 8, 4)) == S.SRFTQ_ERR_UNSUPPORTED
+    assert call(shape=S.make_shape(2, 1000, 2, 96, 16, 4)) == S.SRFTQ_ERR_UNSUPPORTED
+    assert call(t_cap=999) == S.SRFTQ_ERR_SHAPE
+    assert call(scale=float("nan")) == S.SRFTQ_ERR_SHAPE
+    assert call(scale=float("inf")) == S.SRFTQ_ERR_SHAPE
+    assert call(q=None) == S.SRFTQ_ERR_NULL
+    assert call(ws=None) == S.SRFTQ_ERR_NULL
+    assert call(k=S.CacheView(0x10000, None, None, None)) == S.SRFTQ_ERR_NULL
+    assert call(out=mis) == S.SRFTQ_ERR_ALIGN
+    assert call(v=S.CacheView(0x10008, 0x10000, None, None)) == S.SRFTQ_ERR_ALIGN
+    assert call(lengths=_Fake(0x10002)) == S.SRFTQ_ERR_ALIGN
+    assert call(k=S.CacheView(0x10000, 0x10000, 0x10001, None)) == S.SRFTQ_ERR_ALIGN
+    assert call(nbytes=need - 1) == S.SRFTQ_ERR_SHAPE
+    # no tensors or no heads: nothing to do
+    assert call(shape=S.make_shape(0, 1000, 2, 128, 16, 4), q=None, out=None, ws=None) == S.SRFTQ_OK
+
+
 def test_empty_problem_is_a_no_op():
     sh = S.make_shape(1, 0, 8, 128, 16, 4)
     assert S.srftq_quantize(sh, None, None, None, None, None, stream=0) == S.SRFTQ_OK
@@ -158,6 +189,9 @@ def test_device_calls_without_a_device_report_hip_error():
     sh = S.make_shape(1, 64, 8, 128, 16, 4)
     a = _Fake(0x10000)
     assert S.srftq_quantize(sh, a, None, None, a, a, stream=0) == S.SRFTQ_ERR_HIP
+    kv = S.CacheView(0x10000, 0x10000, None, None)
+    need = S.srftq_attention_workspace_bytes(sh, 2)
+    assert S.srftq_decode_attention(sh, 64, 2, a, kv, kv, None, 0.1, a, a, need, stream=0) == S.SRFTQ_ERR_HIP
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
