@@ -233,6 +233,58 @@ def decode_append_latency(steps: int = 1000, graph_steps: int = 100) -> dict:
             "step": "srftq_cache_append of the new tokens, then the positions advanced (+1)"}
 
 
+def decode_attention_timing(w, codes, scales, sd, lam, steps: int, R: int = 6) -> dict:
+    """One decode step of attention over the workload's caches read as 28
+    layers' K (even tensors) and V (odd tensors): srftq_decode_attention of
+    one new query token per layer, R query heads per KV head, all layers in
+    one call.  Algorithmic bytes: every cached code and scale of K and V once
+    (queries and outputs are under 0.1 %)."""
+    import numpy as np
+    import torch
+
+    from kv_cache_quantization_srft_amd import srftq as S
+    from kv_cache_quantization_srft_amd import workloads as W
+
+    dev = codes.device
+    kc, vc = codes[0::2].contiguous(), codes[1::2].contiguous()
+    ks, vs = scales[0::2].contiguous(), scales[1::2].contiguous()
+    sk, sv = sd[0::2].contiguous(), sd[1::2].contiguous()
+    lk = None if lam is None else lam[0::2].contiguous()
+    lv = None if lam is None else lam[1::2].contiguous()
+    q = torch.from_numpy(W.attention_queries(w, R)).to(dev)
+    L = w.B // 2
+    sh = S.make_shape(L, w.T, w.H, w.d, w.group, w.bits)
+    ws = torch.empty((S.srftq_attention_workspace_bytes(sh, R),), dtype=torch.uint8, device=dev)
+    out = torch.empty((L, w.H * R, w.d), dtype=torch.float32, device=dev)
+
+    def call():
+        S.decode_attention(q, kc, ks, vc, vs, sk, lk, sv, lv, group=w.group, bits=w.bits,
+                           workspace=ws, out=out)
+
+    for _ in range(20):
+        call()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in evs:
+        e0.record()
+        call()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    bpv = w.d * w.bits // 8 + 2 * (w.d // w.group)
+    nbytes = 2 * L * w.H * w.T * bpv
+    fp16_bytes = 2 * L * w.H * w.T * 2 * w.d
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": f"decode attention: {L} layers x K+V caches [T={w.T}, H={w.H}, d={w.d}], "
+                        f"group {w.group}, int{w.bits}, {R} query heads per KV head, one query token",
+            "ms": ms, "algorithmic_bytes": nbytes, "GBps": gbps, "hbm_frac": gbps / HBM_PEAK_GBPS,
+            "cached_tokens_per_s": L * w.H * w.T / (ms * 1e-3),
+            "fp16_cache_bytes": fp16_bytes,
+            "fp16_cache_read_ms_at_same_GBps": fp16_bytes / (gbps * 1e9) * 1e3,
+            "step": "srftq_decode_attention (query rotation, partial attention over token chunks, "
+                    "chunk merge + unrotation: three launches)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -243,7 +295,8 @@ def main():
                          "steps run at the clocks a sustained load settles to")
     ap.add_argument("--workload", default="outlier")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-decode", action="store_true", help="skip the decode-append latency figures")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the decode-append latency and decode-attention figures")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic_<kernel>_<workload>.json from two rocprofv3 "
                          "counter_collection.csv files of this benchmark, then exit")
@@ -357,6 +410,7 @@ def main():
     rel = (torch.linalg.vector_norm(xhat.float() - xd.float()) / torch.linalg.vector_norm(xd.float())).item()
 
     dec = None if args.no_decode else decode_append_latency()
+    attn = None if args.no_decode else decode_attention_timing(w, codes, scales, sd, lam, args.steps)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -391,6 +445,7 @@ def main():
         "step": "srftq_quantize then srftq_dequantize of every vector (one launch each)",
         "reconstruction_rel_l2": rel,
         "decode_append": dec,
+        "decode_attention": attn,
         "device": torch.cuda.get_device_name(0),
         "input_generation_s": gen_s,
     }

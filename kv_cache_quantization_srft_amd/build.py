@@ -45,6 +45,10 @@ def _compile(src: str) -> str:
         return obj
     path = os.path.join(CSRC, src)
     flags = DEVICE_FLAGS if src.endswith(".hip") else HOST_FLAGS
+    if src.startswith("k_attn"):
+        # MFMA results in VGPRs: the attention kernels read every score tile
+        # back for VALU work, which AGPR results would have to copy first
+        flags = flags + ["-mllvm", "-amdgpu-mfma-vgpr-form"]
     cmd = [HIPCC] + flags + ["-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:

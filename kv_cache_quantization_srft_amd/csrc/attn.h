@@ -16,8 +16,7 @@
 //                        stored as 2^-e_r u_r with e_r putting max |u_r| in
 //                        [2^10, 2^11) (so that its fp16 parts neither
 //                        overflow nor go subnormal) plus the factor 2^e_r
-//                        (one block per (tensor, KV head), one lane per
-//                        query head).
+//                        (one lane per query head).
 //   attn_partial_kernel  one block of 4 waves per chunk of 4 * span tokens of
 //                        one (tensor, KV head); per 16-token block a wave
 //                        computes the scores of 16 query heads (R used, the
@@ -41,7 +40,7 @@
 // Staging: every 16-token block's K codes (whole rows), V codes (transposed
 // by dword: [dword][token], so that a lane's four tokens of one coordinate
 // are one 16-byte LDS read) and both scale rows arrive by LDS-DMA into a
-// double buffer per wave, one block ahead; rows past the tensor's length are
+// ring of NS stages per wave, NS - 1 blocks ahead; rows past the tensor's length are
 // never read (their lanes re-read the last valid row, whose finite values
 // the softmax masks).
 #pragma once
@@ -77,13 +76,16 @@ struct AttnTile {
   static constexpr int OFF_VS = OFF_KS + S_BYTES;
   static constexpr int STAGE = OFF_VS + S_BYTES;       // one buffer
   static constexpr int NDMA = KC_INST + VC_INST + 2 * S_INST;   // DMA instructions per block
-  static constexpr int WAVE_BYTES = 2 * STAGE;
+  // blocks in flight per wave: enough bytes outstanding to cover HBM latency,
+  // within the 6-bit vmcnt counter
+  static constexpr int NS = 1 + 63 / NDMA < 4 ? 1 + 63 / NDMA : 4;
+  static constexpr int WAVE_BYTES = NS * STAGE;
   static constexpr int MERGE_ACC = 4 * NB * 64 * 16;   // [wave][kb][lane] float4
   static constexpr int MERGE_BYTES = MERGE_ACC + 4 * 16 * 8;
   static constexpr int LDS_BYTES = 4 * WAVE_BYTES > MERGE_BYTES ? 4 * WAVE_BYTES : MERGE_BYTES;
   static_assert(G >= 16 && G % 16 == 0, "a group spans whole MFMA k-blocks");
   static_assert(CT % 256 == 0, "V codes move in 256-byte DMA instructions");
-  static_assert(NDMA < 32, "two blocks of DMA in flight fit the vmcnt counter");
+  static_assert(NS >= 2 && (NS - 1) * NDMA <= 63, "the blocks in flight fit the vmcnt counter");
 };
 
 __device__ __forceinline__ uint32_t lds_u32(uint32_t byte_addr) {
@@ -95,6 +97,45 @@ __device__ __forceinline__ u32x4_t lds_u32x4(uint32_t byte_addr) {
 __device__ __forceinline__ uint32_t lds_u16(uint32_t byte_addr) {
   return *(const __attribute__((address_space(3))) uint16_t*)(uintptr_t)byte_addr;
 }
+typedef const __attribute__((address_space(3))) uint32_t* lds_u32p;
+typedef const __attribute__((address_space(3))) u32x4_t* lds_u32x4p;
+__device__ __forceinline__ lds_u32p lds_ptr32(uint32_t byte_addr) { return (lds_u32p)(uintptr_t)byte_addr; }
+__device__ __forceinline__ lds_u32x4p lds_ptr128(uint32_t byte_addr) { return (lds_u32x4p)(uintptr_t)byte_addr; }
+
+// ((z ^ 0x00080008) & 0x000F000F) | 0x64006400: the nibbles at bits 0-3 and
+// 16-19 of z, offset by 8 (two's complement -> 0..15), as the fp16 pair
+// 1024 + n (one v_bitop3).
+__device__ __forceinline__ uint32_t nib_f16x2(uint32_t z) {
+  return ((z ^ 0x00080008u) & 0x000F000Fu) | 0x64006400u;
+}
+
+// Wait until at most k * N vector-memory operations are in flight, k < NS.
+template <int N, int NS>
+__device__ __forceinline__ void wait_blocks(int k) {
+  static_for<NS>([&](auto kk) {
+    constexpr int i = decltype(kk)::value;
+    if (k == i) wait_vm<i * N>();
+  });
+}
+
+// Sign masks of one lane's own head, held in registers (a sign source for
+// forward() when the lanes of a wave belong to different heads).
+// The sign diagonal applied to a lane's own fp16 words (each lane may belong
+// to a different head), before a transform that then takes no signs.
+template <int D>
+__device__ __forceinline__ void apply_lane_signs(const int8_t* row, uint32_t (&w)[D / 2]) {
+  const uint32_t* r = (const uint32_t*)row;   // 4-byte aligned
+  static_for<D / 4>([&](auto ii) {
+    constexpr int i = decltype(ii)::value;
+    const uint32_t sb = r[i];
+    w[2 * i] ^= sign_mask_of(sb);
+    w[2 * i + 1] ^= sign_mask_of(sb >> 16);
+  });
+}
+struct NoSigns {
+  __device__ __forceinline__ uint32_t mask(int) const { return 0u; }
+  __device__ __forceinline__ uint4 mask4(int) const { return make_uint4(0u, 0u, 0u, 0u); }
+};
 
 // Two fp16 lanes holding 0x6400 | n (= 1024 + n), minus the bias: exact small
 // integers.
@@ -142,8 +183,8 @@ __device__ __forceinline__ uint32_t scale_pair(uint32_t tile, int row, int g) {
 }
 
 // ----------------------------------------------------------------------------
-// u = M (s_k . q) * scale * log2(e) / lambda_k for the R query heads of one
-// (tensor, KV head): block = (tensor, KV head), lane r < R = query head.
+// u = M (s_k . q) * scale * log2(e) / lambda_k, one lane per query head
+// v = b*H*R + h*R + r (KV head bh = v / R).
 // ----------------------------------------------------------------------------
 template <int D, int ROT>
 __global__ __launch_bounds__(64) void attn_qprep_kernel(const uint16_t* __restrict__ q,
@@ -152,32 +193,45 @@ __global__ __launch_bounds__(64) void attn_qprep_kernel(const uint16_t* __restri
                                                         float* __restrict__ uq,
                                                         float* __restrict__ uexp, AttnGeo a) {
   using Sc = Scales<D, ROT, VAR_REAL>;
-  const int bh = blockIdx.x;
-  const int r = threadIdx.x;
-  if (r >= a.R) return;
-  const int64_t v = (int64_t)bh * a.R + r;     // = b*H*R + h*R + r
+  const int64_t v = (int64_t)blockIdx.x * 64 + threadIdx.x;
+  if (v >= (int64_t)a.BH * a.R) return;
+  const int64_t bh = v / a.R;
   uint32_t w[D / 2];
   load_words<D / 2>((const uint8_t*)q + v * (2 * D), w);
-  const HeadSigns sg(signs_k + (int64_t)bh * a.sign_stride_k);
+  apply_lane_signs<D>(signs_k + bh * a.sign_stride_k, w);
   float y[D];
-  forward<D, ROT, VAR_REAL>(w, sg, y);
+  forward<D, ROT, VAR_REAL>(w, NoSigns{}, y);
+  const float* lam = lam_k ? lam_k + bh * D : nullptr;
+  const bool lam16 = ((uintptr_t)lam & 15u) == 0;   // rows of 16-byte aligned lambda load as float4
   float mx = 0.0f;
-  static_for<D>([&](auto jj) {
-    constexpr int j = decltype(jj)::value;
-    float u = y[j] * (float)(Sc::is_edge(j) ? Sc::kFwdEdge : Sc::kFwdBulk) * a.scale_log2e;
-    if (lam_k) u = u / lam_k[(int64_t)bh * D + j];
-    y[j] = u;
-    mx = __builtin_fmaxf(mx, __builtin_fabsf(u));
+  static_for<D / 4>([&](auto kk) {
+    constexpr int k = decltype(kk)::value;
+    float li[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+    if (lam) {
+      if (lam16) {
+        const float4 l4 = *(const float4*)(lam + 4 * k);
+        li[0] = l4.x, li[1] = l4.y, li[2] = l4.z, li[3] = l4.w;
+      } else {
+        static_for<4>([&](auto ee) { li[decltype(ee)::value] = lam[4 * k + decltype(ee)::value]; });
+      }
+    }
+    static_for<4>([&](auto ee) {
+      constexpr int e = decltype(ee)::value;
+      constexpr int j = 4 * k + e;
+      float u = y[j] * (float)(Sc::is_edge(j) ? Sc::kFwdEdge : Sc::kFwdBulk) * a.scale_log2e;
+      if (lam) u = u * __builtin_amdgcn_rcpf(li[e]);
+      y[j] = u;
+      mx = __builtin_fmaxf(mx, __builtin_fabsf(u));
+    });
   });
   // power of two 2^e with max |u| / 2^e in [2^10, 2^11) (e = 0 for u = 0)
   const int e = mx > 0.0f ? __builtin_amdgcn_frexp_expf(mx) - 11 : 0;
   const float down = __builtin_ldexpf(1.0f, -e);
-  uint32_t o[D];
-  static_for<D>([&](auto jj) {
-    constexpr int j = decltype(jj)::value;
-    o[j] = as_u32(y[j] * down);
+  float4* dst = (float4*)(uq + v * D);
+  static_for<D / 4>([&](auto kk) {
+    constexpr int k = decltype(kk)::value;
+    dst[k] = make_float4(y[4 * k] * down, y[4 * k + 1] * down, y[4 * k + 2] * down, y[4 * k + 3] * down);
   });
-  store_words<D>((uint8_t*)uq + v * (4 * D), o);
   uexp[v] = __builtin_ldexpf(1.0f, e);
 }
 
@@ -305,17 +359,16 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const uint8_t* __rest
     vsh = 0;
   }
 
-  if (nblk > 0) issue(0, 0);
+  constexpr int NS = Tl::NS;
+  for (int i = 0; i < NS - 1 && i < nblk; ++i) issue(i, i);
   for (int blk = 0; blk < nblk; ++blk) {
-    const int cur = blk & 1;
-    wait_lgkm0();
+    const int cur = blk % NS;
+    wait_lgkm0();   // the stage about to be refilled has been read
     wave_fence();
-    if (blk + 1 < nblk) {
-      issue(blk + 1, cur ^ 1);
-      wait_vm<Tl::NDMA>();
-    } else {
-      wait_vm<0>();
-    }
+    const int nxt = blk + NS - 1;
+    if (nxt < nblk) issue(nxt, nxt % NS);
+    const int rest = nblk - 1 - blk;
+    wait_blocks<Tl::NDMA, NS>(rest < NS - 1 ? rest : NS - 1);   // this block has landed
     wave_fence();
     const uint32_t base = lds_wave + (uint32_t)cur * Tl::STAGE;
     const int64_t t0 = t_begin + 16 * (int64_t)blk;
@@ -324,17 +377,18 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const uint8_t* __rest
     // ---- scores: S[e] = sum_G sigma_k(4q+e, G) * sum_{k in G} c_k u_k ----
     float S[4] = {0.f, 0.f, 0.f, 0.f};
     float4_t dg = (float4_t){0.f, 0.f, 0.f, 0.f};
+    // this lane's K code dwords: row jl, dword 2kb + q/2 (int4) or 4kb + q (int8)
+    const lds_u32p krow = lds_ptr32(base + (uint32_t)(jl * RB + 4 * (BITS == 4 ? (q >> 1) : q)));
     static_for<NB>([&](auto kk) {
       constexpr int kb = decltype(kk)::value;
       half4_t A;
       if constexpr (BITS == 4) {
-        const uint32_t x = lds_u32(base + (uint32_t)(jl * RB + 4 * (2 * kb + (q >> 1)))) ^ 0x88888888u;
-        const uint32_t z = __builtin_amdgcn_perm(0u, x, ksel);
-        const uint32_t a0 = f16x2_minus((z & 0x000F000Fu) | 0x64006400u, kBias);
-        const uint32_t a1 = f16x2_minus(((z >> 4) & 0x000F000Fu) | 0x64006400u, kBias);
+        const uint32_t z = __builtin_amdgcn_perm(0u, krow[2 * kb], ksel);
+        const uint32_t a0 = f16x2_minus(nib_f16x2(z), kBias);
+        const uint32_t a1 = f16x2_minus(nib_f16x2(z >> 4), kBias);
         A = half4_of(a0, a1);
       } else {
-        const uint32_t x = lds_u32(base + (uint32_t)(jl * RB + 4 * (4 * kb + q)));
+        const uint32_t x = krow[4 * kb];
         const uint32_t a0 = f16x2_minus(__builtin_amdgcn_perm(0u, x, 0x0C010C00u) ^ 0x64806480u, kBias);
         const uint32_t a1 = f16x2_minus(__builtin_amdgcn_perm(0u, x, 0x0C030C02u) ^ 0x64806480u, kBias);
         A = half4_of(a0, a1);
@@ -380,6 +434,9 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const uint8_t* __rest
 
     // ---- P.V: acc[coord][head] += sum_t fp16(c_v(t, coord) sigma_v(t, G)) fp16(2^14 p_t) ----
     const half4_t Bv = half4_of(pack_f16x2(p[0], p[1]), pack_f16x2(p[2], p[3]));
+    // transposed V tile: dword w of tokens 4q..4q+3 at 16-byte index 4w + q;
+    // this lane's coordinate sits in dword 2kb + jl/8 (int4) or 4kb + jl/4 (int8)
+    const lds_u32x4p vcol = lds_ptr128(base + Tl::OFF_VC) + (uint32_t)(4 * (BITS == 4 ? (jl >> 3) : (jl >> 2)) + q);
     uint32_t sv01 = 0, sv23 = 0;   // sigma_v of the lane's tokens (4q, 4q+1), (4q+2, 4q+3), group of kb
     static_for<NB>([&](auto kk) {
       constexpr int kb = decltype(kk)::value;
@@ -389,14 +446,11 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const uint8_t* __rest
         sv23 = scale_pair<SRB>(base + Tl::OFF_VS, 4 * q + 2, g);
       }
       // the four tokens 4q..4q+3 of one dword of the transposed V tile
-      const uint32_t wdw = BITS == 4 ? (uint32_t)(2 * kb + (jl >> 3)) : (uint32_t)(4 * kb + (jl >> 2));
-      const u32x4_t x = lds_u32x4(base + Tl::OFF_VC + 4u * (wdw * 16u + 4u * (uint32_t)q));
+      const u32x4_t x = vcol[(BITS == 4 ? 2 : 4) * kb * 4];
       uint32_t a0, a1;
       if constexpr (BITS == 4) {
-        const uint32_t z0 = (__builtin_amdgcn_perm(x.y, x.x, vsel) >> vsh) ^ 0x00080008u;
-        const uint32_t z1 = (__builtin_amdgcn_perm(x.w, x.z, vsel) >> vsh) ^ 0x00080008u;
-        a0 = f16x2_minus((z0 & 0x000F000Fu) | 0x64006400u, kBias);
-        a1 = f16x2_minus((z1 & 0x000F000Fu) | 0x64006400u, kBias);
+        a0 = f16x2_minus(nib_f16x2(__builtin_amdgcn_perm(x.y, x.x, vsel) >> vsh), kBias);
+        a1 = f16x2_minus(nib_f16x2(__builtin_amdgcn_perm(x.w, x.z, vsel) >> vsh), kBias);
       } else {
         a0 = f16x2_minus(__builtin_amdgcn_perm(x.y, x.x, vsel) ^ 0x64806480u, kBias);
         a1 = f16x2_minus(__builtin_amdgcn_perm(x.w, x.z, vsel) ^ 0x64806480u, kBias);
@@ -460,56 +514,80 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const uint8_t* __rest
 
 // ----------------------------------------------------------------------------
 // One query head: merge its chunks, w = acc / (l * lambda_v), o = s_v . M^T w.
-// Block = (tensor, query head); lanes split the coordinates, lane 0 unrotates.
+// Block = (tensor, query head), 4 waves: the threads split the chunks for
+// the maxima and sums, each wave accumulates every fourth chunk with its
+// lanes splitting the coordinates, the waves add up through LDS, and lane 0
+// unrotates.
 // ----------------------------------------------------------------------------
 template <int D, int ROT>
-__global__ __launch_bounds__(64) void attn_combine_kernel(const float* __restrict__ ws_ml,
-                                                          const float* __restrict__ ws_acc,
-                                                          const int8_t* __restrict__ signs_v,
-                                                          const float* __restrict__ lam_v,
-                                                          float* __restrict__ out, AttnGeo a) {
+__global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ ws_ml,
+                                                           const float* __restrict__ ws_acc,
+                                                           const int8_t* __restrict__ signs_v,
+                                                           const float* __restrict__ lam_v,
+                                                           float* __restrict__ out, AttnGeo a) {
   using Sc = Scales<D, ROT, VAR_REAL>;
   constexpr int PER = D / 64;
-  __shared__ __attribute__((aligned(16))) float ybuf[D];
+  __shared__ __attribute__((aligned(16))) float part[4][D];
+  __shared__ float red[2][4];
   const int64_t v = blockIdx.x;               // b*H*R + h*R + r
   const int bh = (int)(v / a.R);
   const int r = (int)(v - (int64_t)bh * a.R);
-  const int lane = threadIdx.x;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int NC = a.n_chunks;
   const int64_t s0 = (int64_t)bh * NC * a.R + r;   // slot of chunk 0; chunk c at s0 + c*R
 
+  // largest chunk maximum and the weighted sum of the chunk sums
   float m = -__builtin_inff();
-  for (int ch = 0; ch < NC; ++ch) m = __builtin_fmaxf(m, ws_ml[2 * (s0 + (int64_t)ch * a.R)]);
-  float l = 0.0f, w[PER];
-  static_for<PER>([&](auto kk) { w[decltype(kk)::value] = 0.0f; });
-  for (int ch = 0; ch < NC; ++ch) {
+  for (int ch = t; ch < NC; ch += 256) m = __builtin_fmaxf(m, ws_ml[2 * (s0 + (int64_t)ch * a.R)]);
+  static_for<6>([&](auto ii) { m = __builtin_fmaxf(m, __shfl_xor(m, 1 << decltype(ii)::value)); });
+  if (lane == 0) red[0][wave] = m;
+  __syncthreads();
+  m = __builtin_fmaxf(__builtin_fmaxf(red[0][0], red[0][1]), __builtin_fmaxf(red[0][2], red[0][3]));
+  auto weight = [&](float mc) { return mc == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(mc - m); };
+  float l = 0.0f;
+  for (int ch = t; ch < NC; ch += 256) {
     const int64_t s = s0 + (int64_t)ch * a.R;
-    const float mc = ws_ml[2 * s];
-    const float f = mc == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(mc - m);
-    l += f * ws_ml[2 * s + 1];
+    l += weight(ws_ml[2 * s]) * ws_ml[2 * s + 1];
+  }
+  static_for<6>([&](auto ii) { l += __shfl_xor(l, 1 << decltype(ii)::value); });
+  if (lane == 0) red[1][wave] = l;
+
+  // accumulators: wave w takes chunks w, w + 4, ...
+  float w[PER];
+  static_for<PER>([&](auto kk) { w[decltype(kk)::value] = 0.0f; });
+#pragma unroll 4
+  for (int ch = wave; ch < NC; ch += 4) {
+    const int64_t s = s0 + (int64_t)ch * a.R;
+    const float f = weight(ws_ml[2 * s]);          // wave-uniform (scalar load)
+    const float* src = ws_acc + s * D + lane;
     static_for<PER>([&](auto kk) {
       constexpr int k = decltype(kk)::value;
-      w[k] += f * ws_acc[s * D + lane + 64 * k];
+      w[k] += f * src[64 * k];
     });
   }
-  const float inv_l = l > 0.0f ? 1.0f / l : 0.0f;
   static_for<PER>([&](auto kk) {
     constexpr int k = decltype(kk)::value;
-    const int j = lane + 64 * k;
-    float y = w[k] * inv_l;
-    if (lam_v) y = y / lam_v[(int64_t)bh * D + j];
-    ybuf[j] = y * (float)(Sc::is_edge(j) ? Sc::kInvEdge : Sc::kInvBulk);
+    part[wave][lane + 64 * k] = w[k];
   });
   __syncthreads();
-  if (lane != 0) return;
+  l = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
+  const float inv_l = l > 0.0f ? 1.0f / l : 0.0f;
+  for (int j = t; j < D; j += 256) {
+    float y = ((part[0][j] + part[1][j]) + (part[2][j] + part[3][j])) * inv_l;
+    if (lam_v) y = y * __builtin_amdgcn_rcpf(lam_v[(int64_t)bh * D + j]);
+    part[0][j] = y * (float)(Sc::is_edge(j) ? Sc::kInvEdge : Sc::kInvBulk);
+  }
+  __syncthreads();
+  if (t != 0) return;
   float y[D];
   static_for<D / 4>([&](auto kk) {
     constexpr int k = decltype(kk)::value;
-    const float4 t = *(const float4*)(ybuf + 4 * k);
-    y[4 * k] = t.x;
-    y[4 * k + 1] = t.y;
-    y[4 * k + 2] = t.z;
-    y[4 * k + 3] = t.w;
+    const float4 q4 = *(const float4*)(&part[0][4 * k]);
+    y[4 * k] = q4.x;
+    y[4 * k + 1] = q4.y;
+    y[4 * k + 2] = q4.z;
+    y[4 * k + 3] = q4.w;
   });
   float x[D];
   inverse<D, ROT, VAR_REAL>(y, x);
