@@ -285,6 +285,48 @@ def decode_attention_timing(w, codes, scales, sd, lam, steps: int, R: int = 6) -
                     "chunk merge + unrotation: three launches)"}
 
 
+def non_pow2_timing(steps: int) -> dict:
+    """Quantize + dequantize at d = 96 (the SRFT with a radix-3 step, per-lane
+    kernels): 8 tensors of fp16 [T=32768, H=8, d=96], N(0,1) drawn on the
+    device from a fixed seed, group 16, int4."""
+    import torch
+
+    from kv_cache_quantization_srft_amd import srftq as S
+
+    B, T, H, d, g, bits = 8, 32768, 8, 96, 16, 4
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20260508)
+    x = torch.randn((B, T, H, d), device=dev, generator=gen).half()
+    s = (torch.randint(0, 2, (B, H, d), device=dev, generator=gen) * 2 - 1).to(torch.int8)
+    codes = torch.empty((B, H, T, d * bits // 8), dtype=torch.uint8, device=dev)
+    scales = torch.empty((B, H, T, d // g), dtype=torch.float16, device=dev)
+    xhat = torch.empty_like(x)
+    for _ in range(10):
+        S.quantize(x, s, None, g, bits, codes=codes, scales=scales)
+        S.dequantize(codes, scales, s, None, g, bits, out=xhat)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    tq = tdq = 0.0
+    for _ in range(steps):
+        ev[0].record()
+        S.quantize(x, s, None, g, bits, codes=codes, scales=scales)
+        ev[1].record()
+        S.dequantize(codes, scales, s, None, g, bits, out=xhat)
+        ev[2].record()
+        torch.cuda.synchronize()
+        tq += ev[0].elapsed_time(ev[1])
+        tdq += ev[1].elapsed_time(ev[2])
+    n = B * T * H
+    bpv = algorithmic_bytes_per_vector(d, g, bits)
+    q_ms, dq_ms = tq / steps, tdq / steps
+    return {"workload": f"{B} x fp16 [T={T}, H={H}, d={d}], SRFT (radix-3 step), group {g}, int{bits}",
+            "quantize_ms": q_ms, "dequantize_ms": dq_ms, "bytes_per_vector": bpv,
+            "quantize_hbm_frac": bpv * n / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "dequantize_hbm_frac": bpv * n / (dq_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "vectors_per_s_step": n / ((q_ms + dq_ms) * 1e-3)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -296,7 +338,7 @@ def main():
     ap.add_argument("--workload", default="outlier")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true",
-                    help="skip the decode-append latency and decode-attention figures")
+                    help="skip the decode-append, decode-attention and d = 96 figures")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic_<kernel>_<workload>.json from two rocprofv3 "
                          "counter_collection.csv files of this benchmark, then exit")
@@ -411,6 +453,7 @@ def main():
 
     dec = None if args.no_decode else decode_append_latency()
     attn = None if args.no_decode else decode_attention_timing(w, codes, scales, sd, lam, args.steps)
+    d96 = None if args.no_decode else non_pow2_timing(min(args.steps, 50))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -446,6 +489,7 @@ def main():
         "reconstruction_rel_l2": rel,
         "decode_append": dec,
         "decode_attention": attn,
+        "non_pow2_d96": d96,
         "device": torch.cuda.get_device_name(0),
         "input_generation_s": gen_s,
     }

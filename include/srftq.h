@@ -82,12 +82,18 @@ typedef enum {
 } srftq_rot;
 
 /*
- * Problem description.  Supported: d in {64, 128, 256}; bits in {4, 8};
- * group a power of two with 8 <= group <= d; rot one of srftq_rot; B, T >= 0,
- * H >= 1 (B*T*H == 0 is a no-op).  `variant` selects the SRFT kernel
- * organisation: 0 = default (fastest), 1 = real-input radix-2 transform,
- * 2 = complex pairing + d/2-point complex FFT + Hermitian unpack; it is
- * ignored for SRHT and NONE.  Every variant computes the same result.
+ * Problem description.  Supported: d in {64, 96, 128, 256}; bits in {4, 8};
+ * group a power of two with 8 <= group <= d dividing d; rot one of
+ * srftq_rot; B, T >= 0, H >= 1 (B*T*H == 0 is a no-op).  `variant` selects
+ * the SRFT kernel organisation: 0 = default (fastest), 1 = real-input
+ * radix-2 transform, 2 = complex pairing + d/2-point complex FFT + Hermitian
+ * unpack; it is ignored for SRHT and NONE.  Every variant computes the same
+ * result.  d = 96 (a head size that is not a power of two: the SRFT is
+ * defined for any even d, "When Quantization Is Free", Metodologia 1, unlike
+ * the Walsh-Hadamard transform) takes the real-input transform with one
+ * radix-3 step, for rot SRFT (variants 0 and 1) and NONE; SRHT and variant 2
+ * need a power of two and return SRFTQ_ERR_UNSUPPORTED.  Decode attention
+ * supports d in {64, 128, 256}.
  */
 typedef struct {
     int64_t B;

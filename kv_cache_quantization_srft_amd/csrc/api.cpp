@@ -58,12 +58,17 @@ bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 srftq_status validate(const srftq_shape* s) {
   if (!s) return SRFTQ_ERR_NULL;
   if (s->B < 0 || s->T < 0 || s->H < 1) return SRFTQ_ERR_SHAPE;
-  if (s->d != 64 && s->d != 128 && s->d != 256) return SRFTQ_ERR_UNSUPPORTED;
+  if (s->d != 64 && s->d != 96 && s->d != 128 && s->d != 256) return SRFTQ_ERR_UNSUPPORTED;
   if (s->bits != 4 && s->bits != 8) return SRFTQ_ERR_UNSUPPORTED;
-  if (!is_pow2(s->group) || s->group < 8 || s->group > s->d) return SRFTQ_ERR_UNSUPPORTED;
+  if (!is_pow2(s->group) || s->group < 8 || s->group > s->d || s->d % s->group != 0)
+    return SRFTQ_ERR_UNSUPPORTED;
   if (s->rot != SRFTQ_ROT_SRFT && s->rot != SRFTQ_ROT_SRHT && s->rot != SRFTQ_ROT_NONE)
     return SRFTQ_ERR_UNSUPPORTED;
   if (s->variant < 0 || s->variant > 2) return SRFTQ_ERR_UNSUPPORTED;
+  // d = 96: the SRFT's real-input transform with a radix-3 step, or no rotation
+  // (the Walsh-Hadamard matrix and the paired complex FFT need a power of two)
+  if (s->d == 96 && (s->rot == SRFTQ_ROT_SRHT || (s->rot == SRFTQ_ROT_SRFT && s->variant == 2)))
+    return SRFTQ_ERR_UNSUPPORTED;
   // 32-bit tile counters and per-lane byte offsets
   if (s->H > 65535) return SRFTQ_ERR_SHAPE;
   const int64_t tiles_t = (s->T + 63) / 64;
@@ -91,7 +96,10 @@ const srftq::RunFn kDequantize[3][4] = {
     {srftq::run_dequantize_d256_r0, srftq::run_dequantize_d256_r1, srftq::run_dequantize_d256_r2,
      srftq::run_dequantize_d256_r3}};
 
-srftq::RunFn pick(const srftq::RunFn (&table)[3][4], const srftq_shape* s) {
+// The kernel for a validated shape: the tiled kernels of d = 64, 128, 256
+// (table), or the per-lane kernels of d = 96 (lane96).
+srftq::RunFn pick(const srftq::RunFn (&table)[3][4], srftq::RunFn lane96, const srftq_shape* s) {
+  if (s->d == 96) return lane96;
   const int di = s->d == 64 ? 0 : s->d == 128 ? 1 : s->d == 256 ? 2 : -1;
   if (di < 0) return nullptr;
   return table[di][srftq::rot_selector(*s)];
@@ -129,7 +137,7 @@ srftq_status quantize_into(const srftq_shape* s, int64_t pitch, const int32_t* p
   p.scales_out = scales;
   p.pitch = pitch;
   p.pos = pos;
-  const srftq::RunFn fn = pick(kQuantize, s);
+  const srftq::RunFn fn = pick(kQuantize, srftq::run_quantize_d96, s);
   return fn ? from_hip(fn(*s, p, (hipStream_t)stream)) : SRFTQ_ERR_UNSUPPORTED;
 }
 
@@ -149,7 +157,7 @@ srftq_status dequantize_from(const srftq_shape* s, int64_t pitch, const uint8_t*
   p.lambda = lambda;
   p.x_out = x_out;
   p.pitch = pitch;
-  const srftq::RunFn fn = pick(kDequantize, s);
+  const srftq::RunFn fn = pick(kDequantize, srftq::run_dequantize_d96, s);
   return fn ? from_hip(fn(*s, p, (hipStream_t)stream)) : SRFTQ_ERR_UNSUPPORTED;
 }
 
@@ -165,6 +173,7 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 bool attn_plan(const srftq_shape* s, int32_t R, AttnPlan* p) {
   if (validate(s) != SRFTQ_OK || R < 1 || R > 16 || s->group < 16) return false;
+  if (s->d != 64 && s->d != 128 && s->d != 256) return false;
   const int64_t BH = s->B * (int64_t)s->H;
   const int64_t work = BH * s->T;
   int64_t span = (work + 8191) / 8192;
@@ -207,7 +216,7 @@ srftq_status srftq_decode_attention(const srftq_shape* s, int64_t t_cap, int32_t
   srftq_status st = validate(s);
   if (st != SRFTQ_OK) return st;
   if (R < 1 || R > 16) return SRFTQ_ERR_SHAPE;
-  if (s->group < 16) return SRFTQ_ERR_UNSUPPORTED;
+  if (s->group < 16 || (s->d != 64 && s->d != 128 && s->d != 256)) return SRFTQ_ERR_UNSUPPORTED;
   if ((st = validate_cache(s, t_cap)) != SRFTQ_OK) return st;
   if (t_cap < s->T) return SRFTQ_ERR_SHAPE;
   if (!(scale == scale) || scale > 3.0e38f || scale < -3.0e38f) return SRFTQ_ERR_SHAPE;
@@ -310,6 +319,7 @@ static srftq_status run_misc(srftq::Op op, const srftq_shape* s, const srftq::Pt
     case 64: return from_hip(srftq::run_misc_d64(op, *s, p, hs));
     case 128: return from_hip(srftq::run_misc_d128(op, *s, p, hs));
     case 256: return from_hip(srftq::run_misc_d256(op, *s, p, hs));
+    case 96: return from_hip(srftq::run_misc_d96(op, *s, p, hs));
     default: return SRFTQ_ERR_UNSUPPORTED;
   }
 }

@@ -44,6 +44,10 @@ SRFTQ_DECL_RUN(64)
 SRFTQ_DECL_RUN(128)
 SRFTQ_DECL_RUN(256)
 #undef SRFTQ_DECL_RUN
+// Head sizes served by the per-lane kernels (kernels_lane.h).
+hipError_t run_quantize_d96(const srftq_shape&, const Ptrs&, hipStream_t);
+hipError_t run_dequantize_d96(const srftq_shape&, const Ptrs&, hipStream_t);
+hipError_t run_misc_d96(Op op, const srftq_shape&, const Ptrs&, hipStream_t);
 
 inline int rot_selector(const srftq_shape& s) {
   if (s.rot == SRFTQ_ROT_SRFT) return s.variant == 2 ? 1 : 0;

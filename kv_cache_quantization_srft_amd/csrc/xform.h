@@ -162,6 +162,48 @@ __device__ __forceinline__ void rdft(const float (&p0)[D / 2], const float (&p1)
 }
 
 // ----------------------------------------------------------------------------
+// d = 3L (L a power of two): the halfcomplex spectrum X of length 3L from the
+// spectra Y_r of the three subsequences x[3m + r] (decimation in time by 3):
+//   X_{k + Ls} = sum_r W^{r(k + Ls)} Y_r,k = A + wb^s B + wb^{2s} C,
+//   A = Y_0,k,  B = W^k Y_1,k,  C = W^{2k} Y_2,k,  W = e^{-2 pi i / 3L},
+//   wb = e^{-2 pi i / 3};
+// for 0 <= k <= L/2 this gives X_k, X_{k+L} and X_{k+2L} = conj X_{L-k}, which
+// together cover bins 0 .. 3L/2.
+// ----------------------------------------------------------------------------
+template <int L>
+__device__ __forceinline__ void hc_combine3(const float (&Y0)[L], const float (&Y1)[L], const float (&Y2)[L],
+                                            float (&X)[3 * L]) {
+  constexpr int D = 3 * L, N = D / 2;
+  constexpr float h3 = (float)(0.86602540378443864676);   // sqrt(3) / 2
+  static_for<L / 2 + 1>([&](auto kk) {
+    constexpr int k = decltype(kk)::value;
+    constexpr bool real = (k == 0 || k == L / 2);            // Y_r,k is real at DC and Nyquist
+    constexpr float c1 = (float)ccos(2.0 * kPi * k / D), s1 = (float)csin(2.0 * kPi * k / D);
+    constexpr float c2 = (float)ccos(4.0 * kPi * k / D), s2 = (float)csin(4.0 * kPi * k / D);
+    const float ar = Y0[k], ai = real ? 0.0f : Y0[L - k];
+    const float y1r = Y1[k], y1i = real ? 0.0f : Y1[L - k];
+    const float y2r = Y2[k], y2i = real ? 0.0f : Y2[L - k];
+    // B = (c1 - i s1) Y1,  C = (c2 - i s2) Y2
+    const float br = __builtin_fmaf(c1, y1r, s1 * y1i), bi = __builtin_fmaf(c1, y1i, -s1 * y1r);
+    const float cr = __builtin_fmaf(c2, y2r, s2 * y2i), ci = __builtin_fmaf(c2, y2i, -s2 * y2r);
+    const float sr = br + cr, si = bi + ci;
+    const float dr = br - cr, di = bi - ci;
+    const float tr = __builtin_fmaf(-0.5f, sr, ar), ti = __builtin_fmaf(-0.5f, si, ai);
+    // X_k = A + S
+    X[k] = ar + sr;
+    if constexpr (k > 0) X[D - k] = ai + si;
+    // X_{k+L} = T - i h3 Dd
+    X[k + L] = __builtin_fmaf(h3, di, tr);
+    if constexpr (k + L < N) X[D - k - L] = __builtin_fmaf(-h3, dr, ti);
+    // X_{k+2L} = T + i h3 Dd = conj X_{L-k}: skip the bins already written (k = 0, L/2)
+    if constexpr (k > 0 && L - k != k) {
+      X[L - k] = __builtin_fmaf(-h3, di, tr);
+      X[D - L + k] = -__builtin_fmaf(h3, dr, ti);
+    }
+  });
+}
+
+// ----------------------------------------------------------------------------
 // VAR_PAIRED forward: complex radix-2 DIT FFT of z_m = x'_2m + i x'_2m+1.
 // Butterfly X_k = E_k + W O_k, X_{k+L/2} = E_k - W O_k in six FMAs.
 // ----------------------------------------------------------------------------
@@ -296,6 +338,13 @@ __device__ __forceinline__ void forward(const uint32_t (&w)[D / 2], const S& sg,
         float Zr[N], Zi[N];
         cfft<N, 1, 0, D, false>(p0, p1, Zr, Zi);
         hermitian_unpack<D>(Zr, Zi, h);
+      } else if constexpr (D % 3 == 0) {
+        constexpr int L = D / 3;
+        float Y0[L], Y1[L], Y2[L];
+        rdft<L, 3, 0, D>(p0, p1, Y0);
+        rdft<L, 3, 1, D>(p0, p1, Y1);
+        rdft<L, 3, 2, D>(p0, p1, Y2);
+        hc_combine3<L>(Y0, Y1, Y2, h);
       } else {
         rdft<D, 1, 0, D>(p0, p1, h);
       }
@@ -378,6 +427,43 @@ __device__ __forceinline__ void icfft(const float (&Zr)[NN], const float (&Zi)[N
   }
 }
 
+// d = 3L: decimation in frequency by 3 of the real inverse
+//   x_n = h_0 + (-1)^n h_{3L/2} + 2 sum_{0<k<3L/2} Re((h_k + i h_{3L-k}) e^{2 pi i k n / 3L}):
+// with G the full Hermitian spectrum, x_{3m+r} is the length-L real inverse of
+//   Z_r,k = W^{-kr} (G_k + w^r G_{k+L} + w^{2r} G_{k+2L}),  w = e^{2 pi i / 3},
+// where G_{k+L} = H_{k+L} and G_{k+2L} = conj H_{L-k} for 0 <= k <= L/2.
+template <int L>
+__device__ __forceinline__ void hc_split3(const float (&h)[3 * L], float (&Z0)[L], float (&Z1)[L], float (&Z2)[L]) {
+  constexpr int D = 3 * L, N = D / 2;
+  constexpr float h3 = (float)(0.86602540378443864676);
+  static_for<L / 2 + 1>([&](auto kk) {
+    constexpr int k = decltype(kk)::value;
+    constexpr float c1 = (float)ccos(2.0 * kPi * k / D), s1 = (float)csin(2.0 * kPi * k / D);
+    constexpr float c2 = (float)ccos(4.0 * kPi * k / D), s2 = (float)csin(4.0 * kPi * k / D);
+    const float gar = h[k], gai = (k == 0) ? 0.0f : h[D - k];
+    const float gbr = h[k + L], gbi = (k + L == N) ? 0.0f : h[D - k - L];
+    const float gcr = h[L - k], gci = (k == L) ? 0.0f : -h[D - L + k];   // conj H_{L-k}
+    const float sr = gbr + gcr, si = gbi + gci;
+    const float dr = gbr - gcr, di = gbi - gci;
+    const float tr = __builtin_fmaf(-0.5f, sr, gar), ti = __builtin_fmaf(-0.5f, si, gai);
+    // T1 = T + i h3 Dd, T2 = T - i h3 Dd
+    const float t1r = __builtin_fmaf(-h3, di, tr), t1i = __builtin_fmaf(h3, dr, ti);
+    const float t2r = __builtin_fmaf(h3, di, tr), t2i = __builtin_fmaf(-h3, dr, ti);
+    // Z0 = G_a + S;  Z1 = (c1 + i s1) T1;  Z2 = (c2 + i s2) T2
+    const float z0r = gar + sr, z0i = gai + si;
+    const float z1r = __builtin_fmaf(c1, t1r, -s1 * t1i), z1i = __builtin_fmaf(c1, t1i, s1 * t1r);
+    const float z2r = __builtin_fmaf(c2, t2r, -s2 * t2i), z2i = __builtin_fmaf(c2, t2i, s2 * t2r);
+    Z0[k] = z0r;
+    Z1[k] = z1r;
+    Z2[k] = z2r;
+    if constexpr (k > 0 && k < L / 2) {
+      Z0[L - k] = z0i;
+      Z1[L - k] = z1i;
+      Z2[L - k] = z2i;
+    }
+  });
+}
+
 template <int D, int ROT, int VAR>
 __device__ __forceinline__ void inverse(const float (&y)[D], float (&x)[D]) {
   constexpr int N = D / 2;
@@ -440,7 +526,16 @@ __device__ __forceinline__ void inverse(const float (&y)[D], float (&x)[D]) {
       constexpr int k = decltype(kk)::value + 1;
       h[D - k] = y[N + k];
     });
-    irdft<D, 1, 0, D, 1>(h, x);
+    if constexpr (D % 3 == 0) {
+      constexpr int L = D / 3;
+      float Z0[L], Z1[L], Z2[L];
+      hc_split3<L>(h, Z0, Z1, Z2);
+      irdft<L, 3, 0, D, 1>(Z0, x);
+      irdft<L, 3, 1, D, 1>(Z1, x);
+      irdft<L, 3, 2, D, 1>(Z2, x);
+    } else {
+      irdft<D, 1, 0, D, 1>(h, x);
+    }
   }
 }
 

@@ -40,7 +40,7 @@ def test_version_and_status_strings():
     (dict(B=1, T=0, H=8, d=128, group=16, bits=4), S.SRFTQ_OK),
     (dict(B=0, T=5, H=8, d=128, group=16, bits=4), S.SRFTQ_OK),
     (dict(B=1, T=10, H=8, d=128, group=128, bits=8), S.SRFTQ_OK),
-    (dict(B=1, T=10, H=8, d=96, group=16, bits=4), S.SRFTQ_ERR_UNSUPPORTED),
+    (dict(B=1, T=10, H=8, d=112, group=16, bits=4), S.SRFTQ_ERR_UNSUPPORTED),
     (dict(B=1, T=10, H=4, d=256, group=16, bits=4), S.SRFTQ_OK),
     (dict(B=1, T=10, H=4, d=256, group=256, bits=8), S.SRFTQ_OK),
     (dict(B=1, T=10, H=4, d=512, group=16, bits=4), S.SRFTQ_ERR_UNSUPPORTED),
@@ -53,6 +53,12 @@ def test_version_and_status_strings():
     (dict(B=1, T=10, H=0, d=128, group=16, bits=4), S.SRFTQ_ERR_SHAPE),
     (dict(B=1 << 20, T=1 << 30, H=8, d=128, group=16, bits=4), S.SRFTQ_ERR_SHAPE),
     (dict(B=1, T=2, H=65535, d=64, group=32, bits=8), S.SRFTQ_OK),
+    (dict(B=1, T=10, H=8, d=96, group=16, bits=4), S.SRFTQ_OK),
+    (dict(B=1, T=10, H=8, d=96, group=32, bits=8, rot=2), S.SRFTQ_OK),
+    (dict(B=1, T=10, H=8, d=96, group=64, bits=4), S.SRFTQ_ERR_UNSUPPORTED),
+    (dict(B=1, T=10, H=8, d=96, group=16, bits=4, rot=1), S.SRFTQ_ERR_UNSUPPORTED),
+    (dict(B=1, T=10, H=8, d=96, group=16, bits=4, variant=2), S.SRFTQ_ERR_UNSUPPORTED),
+    (dict(B=1, T=10, H=8, d=80, group=16, bits=4), S.SRFTQ_ERR_UNSUPPORTED),
     (dict(B=1, T=2, H=65536, d=64, group=32, bits=8), S.SRFTQ_ERR_SHAPE),
 ])
 def test_validate(kw, expect):
@@ -71,7 +77,8 @@ def test_null_shape_pointer():
     assert S.lib().srftq_validate(None) == S.SRFTQ_ERR_NULL
 
 
-@pytest.mark.parametrize("d,group,bits", [(128, 16, 4), (64, 32, 8), (128, 128, 8), (64, 8, 4)])
+@pytest.mark.parametrize("d,group,bits", [(128, 16, 4), (64, 32, 8), (128, 128, 8), (64, 8, 4), (96, 16, 4),
+                                          (96, 32, 8)])
 def test_sizes_match_oracle_layout(d, group, bits):
     B, T, H = 2, 7, 3
     sh = S.make_shape(B, T, H, d, group, bits)
@@ -82,7 +89,7 @@ def test_sizes_match_oracle_layout(d, group, bits):
 
 
 def test_sizes_zero_for_invalid_shape():
-    sh = S.make_shape(1, 10, 8, 96, 16, 4)
+    sh = S.make_shape(1, 10, 8, 112, 16, 4)
     assert S.srftq_codes_bytes(sh) == 0 and S.srftq_scales_count(sh) == 0
 
 
@@ -134,7 +141,7 @@ def test_cache_argument_errors_return_before_launch():
     assert S.srftq_cache_append(sh, 16, None, a, None, None, _Fake(0x10008), a, stream=0) == S.SRFTQ_ERR_ALIGN
     assert S.srftq_cache_read(sh, 16, a, a, None, None, _Fake(0x10004), stream=0) == S.SRFTQ_ERR_ALIGN
     # shape errors first, as for every other call
-    bad = S.make_shape(2, 5, 8, 96, 16, 4)
+    bad = S.make_shape(2, 5, 8, 112, 16, 4)
     assert S.srftq_cache_append(bad, 16, None, a, None, None, a, a, stream=0) == S.SRFTQ_ERR_UNSUPPORTED
     # nothing to do: no tokens, or no rows to write into
     assert S.srftq_cache_append(sh, 0, None, None, None, None, None, None, stream=0) == S.SRFTQ_OK

@@ -59,7 +59,7 @@ def check_placed(cc, cs, x, s, l, pos, g, bits, rot):
 
 @pytest.mark.parametrize("d,g,bits,rot,lam", [
     (128, 16, 4, "srft", True), (64, 32, 8, "srht", False), (256, 16, 4, "srft", True),
-    (128, 8, 4, "none", False)])
+    (128, 8, 4, "none", False), (96, 16, 4, "srft", True), (96, 32, 8, "srft", False)])
 def test_append_ragged_positions(d, g, bits, rot, lam):
     """Several tiles and a ragged tail per head, positions that spill past
     both ends of the capacity."""

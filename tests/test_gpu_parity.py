@@ -139,6 +139,37 @@ def test_rotate_and_unrotate(d, rot, variant):
     compare.check_dequantize(host(xb_g), xb_o)
 
 
+# d = 96: the SRFT with a radix-3 step (per-lane kernels), and no rotation
+@pytest.mark.parametrize("group,bits", [(8, 4), (16, 4), (32, 8), (16, 8), (32, 4)])
+@pytest.mark.parametrize("rot", ["srft", "none"])
+@pytest.mark.parametrize("lam", [False, True])
+def test_ragged_d96(group, bits, rot, lam):
+    x, s, l = rand_case(2000 + group + bits, 2, 100, 3, 96, scale=2.0, lam=lam)
+    x[0, 5, 1, 7] = 40.0
+    print(f"[d=96 g={group} b={bits} {rot} lam={lam}]", flush=True)
+    run_and_check(x, s, l, group, bits, rot, "default")
+
+
+@pytest.mark.parametrize("rot", ["srft", "none"])
+def test_rotate_unrotate_calibrate_d96(rot):
+    x, s, _ = rand_case(2100, 2, 70, 3, 96, scale=3.0)
+    y_g = S.rotate(dev(x), dev(s), rot)
+    y_o = oracle.rotate(x, s, rot)
+    compare.check_rotate(host(y_g), y_o, x)
+    y32 = y_o.astype(np.float32)
+    xb_g = S.unrotate(dev(y32), dev(s), rot)
+    xb_o = oracle.f64_to_f16(oracle.unrotate(y32.astype(np.float64), s, rot))
+    compare.check_dequantize(host(xb_g), xb_o)
+    lg = host(S.calibrate_lambda(dev(x), dev(s), rot))
+    assert np.allclose(lg, oracle.calibrate_lambda(x, s, rot), rtol=1e-4, atol=0)
+
+
+@pytest.mark.parametrize("T", [1, 64, 65, 130])
+def test_token_counts_d96(T):
+    x, s, _ = rand_case(2200 + T, 3, T, 2, 96)
+    run_and_check(x, s, None, 16, 4, "srft", "default")
+
+
 def test_variants_agree():
     x, s, _ = rand_case(31, 1, 300, 4, 128)
     a = S.quantize(dev(x), dev(s), None, 16, 4, "srft", "real")

@@ -94,7 +94,7 @@ def _pack_rfft(x_signed):
     return y
 
 
-@pytest.mark.parametrize("d", [8, 16, 64, 128, 256])
+@pytest.mark.parametrize("d", [8, 16, 64, 96, 128, 256])
 def test_srft_matches_numpy_rfft(d):
     rng = np.random.default_rng(d)
     B, T, H = 2, 5, 3
@@ -121,8 +121,8 @@ def test_srft_brute_force_d8():
         assert np.allclose(y[0, t, 0], ref, atol=1e-13, rtol=0)
 
 
-@pytest.mark.parametrize("rot", ["srft", "srht"])
-@pytest.mark.parametrize("d", [8, 32, 128, 256])
+@pytest.mark.parametrize("rot,d", [(r, d) for r in ("srft", "srht") for d in (8, 32, 128, 256)]
+                         + [("srft", 96), ("srft", 24)])
 def test_rotation_is_orthogonal(rot, d):
     eye = np.eye(d).astype(np.float16).reshape(d, 1, d)          # d basis vectors
     M = oracle.rotate(eye, None, rot).reshape(d, d).T              # columns = M e_j
@@ -130,8 +130,8 @@ def test_rotation_is_orthogonal(rot, d):
     assert np.max(np.abs(M @ M.T - np.eye(d))) < 1e-13
 
 
-@pytest.mark.parametrize("rot", ["srft", "srht", "none"])
-@pytest.mark.parametrize("d", [16, 64, 128, 256])
+@pytest.mark.parametrize("rot,d", [(r, d) for r in ("srft", "srht", "none") for d in (16, 64, 128, 256)]
+                         + [("srft", 96), ("none", 96)])
 def test_parseval_and_inverse(rot, d):
     rng = np.random.default_rng(d + 7)
     x = _rand_x(rng, (2, 9, 2, d), scale=3.0)
