@@ -47,6 +47,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_unrotate.argtypes = [i64, i64, i32, i32, i32, vp, vp, vp]
         L.oracle_quantize.argtypes = [i64, i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]
         L.oracle_dequantize.argtypes = [i64, i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]
+        L.oracle_quantize_dense.argtypes = [i64, i64, i32, i32, i32, i32, vp, i64, vp, vp, vp, vp, vp, vp]
+        L.oracle_dequantize_dense.argtypes = [i64, i64, i32, i32, i32, i32, vp, i64, vp, vp, vp, vp, vp, vp]
         L.oracle_calibrate_lambda.argtypes = [i64, i64, i32, i32, i32, vp, vp, vp]
         L.oracle_f16_array_to_f64.argtypes = [vp, vp, i64]
         L.oracle_f64_array_to_f16.argtypes = [vp, vp, i64]
@@ -55,7 +57,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
         L.oracle_f16_to_f64.restype = ctypes.c_double
         for f in ("oracle_rotate", "oracle_unrotate", "oracle_quantize",
-                  "oracle_dequantize", "oracle_calibrate_lambda", "oracle_num_threads"):
+                  "oracle_dequantize", "oracle_quantize_dense", "oracle_dequantize_dense",
+                  "oracle_calibrate_lambda", "oracle_num_threads"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -153,6 +156,79 @@ def dequantize(codes, scales, signs=None, lam=None, group=16, bits=4, rot="srft"
     _check(lib().oracle_dequantize(B, T, H, d, group, bits, ROT[rot], _ptr(c4),
                                    _ptr(scales), _ptr(s), _ptr(l), _ptr(x), _ptr(x64)),
            "dequantize")
+    if codes.ndim == 3:
+        x = x[0]
+        x64 = None if x64 is None else x64[0]
+    return (x, x64) if return_f64 else x
+
+
+def householder_matrix(V) -> np.ndarray:
+    """Product of Householder reflections, fp64: Q = H_1 H_2 ... H_k with
+    H_i = I - 2 v_i v_i^T / (v_i^T v_i) for the rows v_i of V [..., k, d]
+    (a zero row is the identity).  The Householder rotations of "When
+    Quantization Is Free" (Metodologia 3, Householder rotations: k = d/2
+    reflectors at d = 256) parametrize an orthogonal d x d matrix this way.
+    Returns [..., d, d]."""
+    V = np.asarray(V, dtype=np.float64)
+    lead, (k, d) = V.shape[:-2], V.shape[-2:]
+    Vs = V.reshape(-1, k, d)
+    out = np.empty((Vs.shape[0], d, d), dtype=np.float64)
+    for m in range(Vs.shape[0]):
+        Q = np.eye(d)
+        for i in range(k):
+            v = Vs[m, i]
+            n2 = float(v @ v)
+            if n2 == 0.0:
+                continue
+            # Q <- Q H_i = Q - (2 / v.v) (Q v) v^T
+            Q = Q - np.outer(Q @ v, v) * (2.0 / n2)
+        out[m] = Q
+    return out.reshape(lead + (d, d))
+
+
+def _dense_q(Q, B, H, d):
+    """Q as fp32 [d, d] (one matrix, stride 0) or [B, H, d, d] (stride d*d)."""
+    Q = np.ascontiguousarray(np.asarray(Q, dtype=np.float32))
+    if Q.shape == (d, d):
+        return Q, 0
+    return Q.reshape(B, H, d, d), d * d
+
+
+def quantize_dense(x16, Q, signs=None, lam=None, group=16, bits=4, return_z=False):
+    """As quantize() with the rotation y = Q (s . x) for a given fp32 matrix
+    Q (a learned or Householder rotation, "When Quantization Is Free",
+    Metodologia 3): Q [d, d] for every head or [B, H, d, d] per head."""
+    x, B, T, H, d = _as4(_bits(x16))
+    s = _signs(signs, B, H, d)
+    l = _lam(lam, B, H, d)
+    q, qs = _dense_q(Q, B, H, d)
+    codes = np.empty((B, H, T, d * bits // 8), dtype=np.uint8)
+    scales = np.empty((B, H, T, d // group), dtype=np.uint16)
+    z = np.empty((B, H, T, d), dtype=np.float32) if return_z else None
+    _check(lib().oracle_quantize_dense(B, T, H, d, group, bits, _ptr(q), qs, _ptr(x), _ptr(s), _ptr(l),
+                                       _ptr(codes), _ptr(scales), _ptr(z)), "quantize_dense")
+    out = (codes, scales) + ((z,) if return_z else ())
+    if x16.ndim == 3:
+        out = tuple(a[0] for a in out)
+    return out
+
+
+def dequantize_dense(codes, scales, Q, signs=None, lam=None, group=16, bits=4, d=None,
+                     return_f64=False):
+    """As dequantize() with x = s . (Q^T yhat)."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint16)
+    if d is None:
+        d = codes.shape[-1] * 8 // bits
+    c4 = codes if codes.ndim == 4 else codes[None]
+    B, H, T = c4.shape[:3]
+    s = _signs(signs, B, H, d)
+    l = _lam(lam, B, H, d)
+    q, qs = _dense_q(Q, B, H, d)
+    x = np.empty((B, T, H, d), dtype=np.uint16)
+    x64 = np.empty((B, T, H, d), dtype=np.float64) if return_f64 else None
+    _check(lib().oracle_dequantize_dense(B, T, H, d, group, bits, _ptr(q), qs, _ptr(c4), _ptr(scales),
+                                         _ptr(s), _ptr(l), _ptr(x), _ptr(x64)), "dequantize_dense")
     if codes.ndim == 3:
         x = x[0]
         x64 = None if x64 is None else x64[0]

@@ -20,7 +20,10 @@
  *   - the DFT is an O(d^2) direct sum in fp64 (no FFT);
  *   - the Walsh-Hadamard transform is a direct +-1 sum in fp64, Sylvester
  *     (natural) order, entry (j,k) = (-1)^popcount(j & k);
- *   - the quantizer is a scalar loop.
+ *   - the quantizer is a scalar loop;
+ *   - a rotation given as a matrix (the learned and Householder rotations
+ *     of section 3) is a direct fp64 matrix-vector sum over its fp32
+ *     entries, y = Q (s . x), and its transpose for the inverse.
  *
  * Readings where the pages are silent (each listed in the design notes):
  *   - DFT sign e^{-2 pi i jk/d}; unitary 1/sqrt(d).
@@ -52,6 +55,7 @@
  *   codes      uint8      [B, H, T, d*bits/8]
  *   scales     fp16 bits  [B, H, T, d/group]
  *   z_out      fp32       [B, H, T, d]   (rows aligned with codes)
+ *   Q          fp32       row-major d x d at Q + (b*H + h) * q_stride
  */
 #include <math.h>
 #include <stdint.h>
@@ -318,13 +322,39 @@ static size_t cache_row(int64_t b, int64_t t, int h, int64_t T, int H)
 }
 
 /*
- * Quantize every vector.  z_out (optional, fp32 [B,H,T,d]) receives the fp32
- * values the decision was taken on.
+ * A rotation given as a matrix (the learned or Householder rotations of
+ * "When Quantization Is Free", Metodologia 3): y = Q xs and its transpose
+ * xs = Q^T y, plain fp64 sums over the fp32 entries of Q (row-major d x d).
  */
-int oracle_quantize(int64_t B, int64_t T, int H, int d, int group, int bits,
-                    int rot, const uint16_t *x, const int8_t *signs,
-                    const float *lambda, uint8_t *codes, uint16_t *scales,
-                    float *z_out)
+static void dense_apply(int d, const float *Q, const double *xs, double *y)
+{
+    for (int i = 0; i < d; ++i) {
+        double acc = 0.0;
+        for (int j = 0; j < d; ++j)
+            acc += (double)Q[(size_t)i * d + j] * xs[j];
+        y[i] = acc;
+    }
+}
+
+static void dense_apply_t(int d, const float *Q, const double *y, double *xs)
+{
+    for (int j = 0; j < d; ++j) {
+        double acc = 0.0;
+        for (int i = 0; i < d; ++i)
+            acc += (double)Q[(size_t)i * d + j] * y[i];
+        xs[j] = acc;
+    }
+}
+
+/*
+ * Quantize every vector.  z_out (optional, fp32 [B,H,T,d]) receives the fp32
+ * values the decision was taken on.  Q (optional) replaces the rotation.
+ */
+static int quantize_impl(int64_t B, int64_t T, int H, int d, int group, int bits,
+                         int rot, const float *Q, int64_t q_stride, const uint16_t *x,
+                         const int8_t *signs,
+                         const float *lambda, uint8_t *codes, uint16_t *scales,
+                         float *z_out)
 {
     int st = check_shape(B, T, H, d, rot);
     if (!st)
@@ -353,7 +383,10 @@ int oracle_quantize(int64_t B, int64_t T, int H, int d, int group, int bits,
             for (int j = 0; j < d; ++j)
                 xs[j] = sign_of(signs, b, H, h, d, j) *
                         oracle_f16_to_f64(x[(size_t)v * d + j]);
-            rotate_one(d, rot, xs, y, cs, sn);
+            if (Q)
+                dense_apply(d, Q + ((size_t)b * H + h) * (size_t)q_stride, xs, y);
+            else
+                rotate_one(d, rot, xs, y, cs, sn);
             for (int j = 0; j < d; ++j) {
                 double lam = lambda ? (double)lambda[((size_t)b * H + h) * d + j] : 1.0;
                 z[j] = (float)(lam * y[j]);
@@ -411,15 +444,42 @@ int oracle_quantize(int64_t B, int64_t T, int H, int d, int group, int bits,
     return 0;
 }
 
+int oracle_quantize(int64_t B, int64_t T, int H, int d, int group, int bits,
+                    int rot, const uint16_t *x, const int8_t *signs,
+                    const float *lambda, uint8_t *codes, uint16_t *scales,
+                    float *z_out)
+{
+    return quantize_impl(B, T, H, d, group, bits, rot, NULL, 0, x, signs, lambda, codes, scales, z_out);
+}
+
+/*
+ * Quantize with the rotation y = Q_bh (s . x): Q_bh = Q + (b*H + h) * q_stride,
+ * row-major d x d fp32 (q_stride 0: one matrix for every head).
+ */
+int oracle_quantize_dense(int64_t B, int64_t T, int H, int d, int group, int bits,
+                          const float *Q, int64_t q_stride, const uint16_t *x, const int8_t *signs,
+                          const float *lambda, uint8_t *codes, uint16_t *scales,
+                          float *z_out)
+{
+    if (!Q)
+        return 1;
+    if (q_stride < 0)
+        return 2;
+    return quantize_impl(B, T, H, d, group, bits, ORACLE_ROT_NONE, Q, q_stride, x, signs, lambda,
+                         codes, scales, z_out);
+}
+
 /*
  * Dequantize every vector: yhat_j = q_j * sigma_G / lambda_j (fp64), then
- * x = s (.) M^T yhat.  x_out receives fp16 (RNE from fp64); x64_out
- * (optional) receives the fp64 values before that rounding.
+ * x = s (.) M^T yhat (M^T = Q^T when Q is given).  x_out receives fp16 (RNE
+ * from fp64); x64_out (optional) receives the fp64 values before that
+ * rounding.
  */
-int oracle_dequantize(int64_t B, int64_t T, int H, int d, int group, int bits,
-                      int rot, const uint8_t *codes, const uint16_t *scales,
-                      const int8_t *signs, const float *lambda,
-                      uint16_t *x_out, double *x64_out)
+static int dequantize_impl(int64_t B, int64_t T, int H, int d, int group, int bits,
+                           int rot, const float *Q, int64_t q_stride, const uint8_t *codes,
+                           const uint16_t *scales,
+                           const int8_t *signs, const float *lambda,
+                           uint16_t *x_out, double *x64_out)
 {
     int st = check_shape(B, T, H, d, rot);
     if (!st)
@@ -454,7 +514,10 @@ int oracle_dequantize(int64_t B, int64_t T, int H, int d, int group, int bits,
                 double lam = lambda ? (double)lambda[((size_t)b * H + h) * d + j] : 1.0;
                 yh[j] = (double)qj * sg / lam;
             }
-            unrotate_one(d, rot, yh, xs, cs, sn);
+            if (Q)
+                dense_apply_t(d, Q + ((size_t)b * H + h) * (size_t)q_stride, yh, xs);
+            else
+                unrotate_one(d, rot, yh, xs, cs, sn);
             for (int j = 0; j < d; ++j) {
                 double val = sign_of(signs, b, H, h, d, j) * xs[j];
                 if (x64_out)
@@ -469,6 +532,30 @@ int oracle_dequantize(int64_t B, int64_t T, int H, int d, int group, int bits,
     free(cs);
     free(sn);
     return 0;
+}
+
+int oracle_dequantize(int64_t B, int64_t T, int H, int d, int group, int bits,
+                      int rot, const uint8_t *codes, const uint16_t *scales,
+                      const int8_t *signs, const float *lambda,
+                      uint16_t *x_out, double *x64_out)
+{
+    return dequantize_impl(B, T, H, d, group, bits, rot, NULL, 0, codes, scales, signs, lambda, x_out,
+                           x64_out);
+}
+
+/* Dequantize with the rotation x = s (.) Q_bh^T yhat (Q_bh as above). */
+int oracle_dequantize_dense(int64_t B, int64_t T, int H, int d, int group, int bits,
+                            const float *Q, int64_t q_stride, const uint8_t *codes,
+                            const uint16_t *scales,
+                            const int8_t *signs, const float *lambda,
+                            uint16_t *x_out, double *x64_out)
+{
+    if (!Q)
+        return 1;
+    if (q_stride < 0)
+        return 2;
+    return dequantize_impl(B, T, H, d, group, bits, ORACLE_ROT_NONE, Q, q_stride, codes, scales, signs,
+                           lambda, x_out, x64_out);
 }
 
 /*

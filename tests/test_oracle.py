@@ -551,3 +551,130 @@ def test_attention_scores_in_the_rotated_domain():
     sig = np.repeat(K[1].view(np.float16).astype(np.float64)[0, 0], g, axis=-1)
     yh = c * sig / K[3][0, 0].astype(np.float64)
     assert np.allclose(yh @ u, direct, rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# Rotations given as matrices: learned and Householder rotations ("When
+# Quantization Is Free", Metodologia 3: a learnable rotation R with lambda,
+# and Householder rotations with k = d/2 reflectors at d = 256).
+# --------------------------------------------------------------------------
+
+def _srft_matrix(d):
+    """Columns M e_i from the oracle's FFT-based rotation of the basis."""
+    return oracle.rotate(np.eye(d, dtype=np.float16).reshape(d, 1, d), None, "srft")[:, 0, :].T
+
+
+def test_householder_single_reflector_invariants():
+    """k = 1: H v = -v, H w = w for w orthogonal to v, H symmetric and H^2 = I."""
+    rng = np.random.default_rng(40)
+    d = 64
+    v = rng.standard_normal(d)
+    H = oracle.householder_matrix(v[None])
+    assert np.allclose(H @ v, -v, atol=1e-13)
+    w = rng.standard_normal(d)
+    w -= (w @ v) / (v @ v) * v
+    assert np.allclose(H @ w, w, atol=1e-13)
+    assert np.allclose(H, H.T, atol=1e-15)
+    assert np.allclose(H @ H, np.eye(d), atol=1e-13)
+
+
+def test_householder_product_matches_lapack_qr():
+    """LAPACK's QR stores Q as H_1 H_2 ... H_n with H_i = I - tau_i v_i v_i^T,
+    v_i = (0 .. 0, 1, below-diagonal of column i); for real reflections
+    tau_i = 2 / (v_i . v_i).  Rebuilding Q from those vectors must give
+    numpy's Q (an independent library routine)."""
+    rng = np.random.default_rng(41)
+    n = 48
+    A = rng.standard_normal((n, n))
+    Qref = np.linalg.qr(A)[0]
+    h, tau = np.linalg.qr(A, mode="raw")
+    F = h.T                                     # LAPACK's column-major factor
+    V = np.zeros((n, n))
+    for i in range(n):
+        V[i, i] = 1.0
+        V[i, i + 1:] = F[i + 1:, i]
+        if tau[i] != 0.0:
+            assert np.isclose(tau[i], 2.0 / (V[i] @ V[i]), rtol=1e-12)
+        else:
+            V[i] = 0.0
+    assert np.allclose(oracle.householder_matrix(V), Qref, atol=1e-12)
+
+
+@pytest.mark.parametrize("k", [128, 127])
+def test_householder_rotation_orthogonal_d256(k):
+    """k reflectors at d = 256: Q^T Q = I and det Q = (-1)^k; zero rows are
+    the identity."""
+    rng = np.random.default_rng(42 + k)
+    V = rng.standard_normal((k, 256))
+    Q = oracle.householder_matrix(V)
+    assert np.abs(Q.T @ Q - np.eye(256)).max() < 1e-12
+    sign, _ = np.linalg.slogdet(Q)
+    assert sign == (-1) ** k
+    V2 = np.concatenate([V[:5], np.zeros((3, 256)), V[5:]])
+    assert np.allclose(oracle.householder_matrix(V2), Q, atol=1e-14)
+
+
+@pytest.mark.parametrize("bits,group", [(4, 16), (8, 32)])
+def test_dense_special_cases_reduce_to_the_transforms(bits, group):
+    """Q = I is rot none; Q = the packed SRFT matrix is rot srft; Q = H_d /
+    sqrt(d) from scipy is rot srht (quantize bit-exact, dequantize to fp64
+    rounding)."""
+    d = 64
+    rng = np.random.default_rng(43)
+    x = _rand_x(rng, (2, 30, 3, d))
+    s = _rand_signs(rng, 2, 3, d)
+    lam = rng.uniform(0.5, 2.0, size=(2, 3, d)).astype(np.float32)
+    mats = {"none": np.eye(d), "srft": _srft_matrix(d),
+            "srht": scipy.linalg.hadamard(d).astype(np.float64) / math.sqrt(d)}
+    for rot, M in mats.items():
+        c0, s0 = oracle.quantize(x, s, lam, group, bits, rot)
+        c1, s1 = oracle.quantize_dense(x, M.astype(np.float32), s, lam, group, bits)
+        assert np.array_equal(c0, c1) and np.array_equal(s0, s1), rot
+        _, a = oracle.dequantize(c0, s0, s, lam, group, bits, rot, d=d, return_f64=True)
+        _, b = oracle.dequantize_dense(c0, s0, M.astype(np.float32), s, lam, group, bits, d=d,
+                                       return_f64=True)
+        assert np.allclose(a, b, rtol=1e-6, atol=1e-6 * np.abs(a).max()), rot
+
+
+def test_dense_per_head_matrices_index_by_tensor_and_head():
+    """Q [B, H, d, d]: each head uses its own matrix (checked head by head
+    against single-matrix calls)."""
+    d, B, H, T = 64, 2, 3, 17
+    rng = np.random.default_rng(44)
+    x = _rand_x(rng, (B, T, H, d))
+    Q = oracle.householder_matrix(rng.standard_normal((B, H, d // 2, d))).astype(np.float32)
+    codes, scales = oracle.quantize_dense(x, Q, None, None, 16, 4)
+    xr = oracle.dequantize_dense(codes, scales, Q, None, None, 16, 4)
+    for b in range(B):
+        for h in range(H):
+            c1, s1 = oracle.quantize_dense(x[b:b + 1, :, h:h + 1], Q[b, h], None, None, 16, 4)
+            assert np.array_equal(c1[0, 0], codes[b, h]) and np.array_equal(s1[0, 0], scales[b, h])
+            x1 = oracle.dequantize_dense(c1, s1, Q[b, h], None, None, 16, 4)
+            assert np.array_equal(x1[0, :, 0], xr[b, :, h])
+
+
+def test_dense_roundtrip_error_identity_and_bound():
+    """A Householder rotation (not symmetric, so a transposed operand shows):
+    ||x_hat - x|| = ||y_hat - y|| (orthogonality of Q), within half a
+    quantization step per coordinate."""
+    d, g, bits = 128, 16, 4
+    rng = np.random.default_rng(45)
+    x = _rand_x(rng, (1, 40, 2, d))
+    s = _rand_signs(rng, 1, 2, d)
+    lam = rng.uniform(0.5, 2.0, size=(1, 2, d)).astype(np.float32)
+    Q = oracle.householder_matrix(rng.standard_normal((d // 2, d))).astype(np.float32)
+    assert np.abs(Q - Q.T).max() > 0.1
+    codes, scales = oracle.quantize_dense(x, Q, s, lam, g, bits)
+    _, x64 = oracle.dequantize_dense(codes, scales, Q, s, lam, g, bits, d=d, return_f64=True)
+    from oracle.compare import decode_codes
+    q = decode_codes(codes, bits, d).astype(np.float64)
+    sig = np.repeat(scales.view(np.float16).astype(np.float64), g, axis=-1)
+    yhat = (q * sig / lam[:, :, None]).transpose(0, 2, 1, 3)
+    sig = sig.transpose(0, 2, 1, 3)
+    y = np.einsum("ij,bthj->bthi", Q.astype(np.float64), s[:, None] * x.astype(np.float64))
+    e_x = np.linalg.norm(x64 - x.astype(np.float64), axis=-1)
+    e_y = np.linalg.norm(yhat - y, axis=-1)
+    # fp32 rounding of Q makes it orthogonal to ~1e-7 only
+    assert np.allclose(e_x, e_y, rtol=1e-5, atol=1e-5)
+    bound = np.sqrt(np.sum((sig / (2 * lam[:, None])) ** 2, axis=-1))
+    assert np.all(e_x <= bound * (1 + 1e-4) + 1e-5)
