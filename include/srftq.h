@@ -242,6 +242,48 @@ srftq_status srftq_decode_attention(const srftq_shape* shape, int64_t t_cap, int
                                     float scale, float* out, void* workspace,
                                     size_t workspace_bytes, void* stream);
 
+/*
+ * Rotations given as a matrix.  "When Quantization Is Free", Metodologia 3,
+ * studies replacing or extending the fixed SRFT by a learned rotation R
+ * (calibrated together with lambda) and by Householder rotations, k = d/2
+ * reflectors at d = 256.  Either is an orthogonal d x d matrix Q, and the
+ * quantizer is then the one above applied to y = Q (s . x):
+ *   z_j = lambda_j y_j, per-group sigma and rounding exactly as srftq_quantize,
+ *   and dequantize: x = s . (Q^T yhat), yhat_j = q_j sigma_G / lambda_j.
+ * (The SRFT itself is the matrix whose columns are srftq_rotate of the unit
+ * vectors; a learned R on top of it is the product R M.)
+ *
+ * srftq_householder_matrix: Q_m = H_1 H_2 ... H_k for m < n, with
+ *   H_i = I - 2 v_i v_i^T / (v_i . v_i) (a zero v_i is the identity),
+ *   computed in fp64 and rounded to fp32.
+ *   d     1..256;  k  0..1024;  n  0..65535 matrices.
+ *   V     in   fp32 [n, k, d] device, 4-B aligned (may be NULL when k = 0)
+ *   Q     out  fp32 [n, d, d] device, 4-B aligned, row-major
+ *
+ * srftq_quantize_dense / srftq_dequantize_dense: as srftq_quantize /
+ * srftq_dequantize (same layouts, alignment and errors) with
+ *   Q         in  fp32 row-major d x d matrices, 16-B aligned; head h of
+ *                 tensor b uses Q + (b*H + h) * q_stride
+ *   q_stride  0 (one matrix for every head) or >= d*d, a multiple of 4
+ *             (else SRFTQ_ERR_SHAPE)
+ * Supported: d in {64, 128, 256}, group in {8, 16, 32}, bits in {4, 8};
+ * shape.rot and shape.variant are ignored.  Q is used as given: dequantize
+ * inverts quantize only when Q is orthogonal.  The product runs on the
+ * matrix cores with Q split into two fp16 parts (about 22 significant bits),
+ * x exact in fp16 and fp32 sums; dequantize splits yhat the same way.
+ */
+srftq_status srftq_householder_matrix(int32_t d, int32_t k, int64_t n, const float* V, float* Q,
+                                     void* stream);
+
+srftq_status srftq_quantize_dense(const srftq_shape* shape, const float* Q, int64_t q_stride,
+                                  const uint16_t* x, const int8_t* signs, const float* lambda,
+                                  uint8_t* codes, uint16_t* scales, void* stream);
+
+srftq_status srftq_dequantize_dense(const srftq_shape* shape, const float* Q, int64_t q_stride,
+                                    const uint8_t* codes, const uint16_t* scales,
+                                    const int8_t* signs, const float* lambda, uint16_t* x_out,
+                                    void* stream);
+
 /* Static description of a status code. */
 const char* srftq_status_string(srftq_status status);
 

@@ -198,6 +198,39 @@ bool attn_plan(const srftq_shape* s, int32_t R, AttnPlan* p) {
 const srftq::RunAttnFn kAttention[3] = {srftq::run_attention_d64, srftq::run_attention_d128,
                                         srftq::run_attention_d256};
 
+// Rotation given as a matrix: the sizes of validate(); d in {64, 128, 256},
+// group in {8, 16, 32}; rot and variant are not used.  q_stride 0 (one
+// matrix) or at least d*d, a multiple of 4 (16-byte aligned matrices).
+srftq_status validate_dense(const srftq_shape* s, int64_t q_stride) {
+  if (!s) return SRFTQ_ERR_NULL;
+  srftq_shape t = *s;
+  t.rot = SRFTQ_ROT_NONE;
+  t.variant = 0;
+  srftq_status st = validate(&t);
+  if (st != SRFTQ_OK) return st;
+  if (s->d != 64 && s->d != 128 && s->d != 256) return SRFTQ_ERR_UNSUPPORTED;
+  if (s->group != 8 && s->group != 16 && s->group != 32) return SRFTQ_ERR_UNSUPPORTED;
+  if (q_stride < 0 || (q_stride != 0 && (q_stride < (int64_t)s->d * s->d || q_stride % 4 != 0)))
+    return SRFTQ_ERR_SHAPE;
+  if (q_stride > 0 && s->B * (int64_t)s->H > (int64_t)0x7fffffffffffLL / q_stride) return SRFTQ_ERR_SHAPE;
+  return SRFTQ_OK;
+}
+
+const srftq::RunDenseFn kDense[3] = {srftq::run_dense_d64, srftq::run_dense_d128, srftq::run_dense_d256};
+
+srftq_status run_dense(srftq::DenseArgs& a, const srftq_shape* s, const int8_t* signs, void* stream) {
+  a.group = s->group;
+  a.bits = s->bits;
+  a.T = s->T;
+  a.H = s->H;
+  a.BH = (int32_t)(s->B * s->H);
+  a.signs = signs ? signs : srftq::plus_ones_ptr();
+  a.sign_stride = signs ? s->d : 0;
+  if (!a.signs) return SRFTQ_ERR_HIP;
+  const int di = s->d == 64 ? 0 : s->d == 128 ? 1 : 2;
+  return from_hip(kDense[di](a, (hipStream_t)stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -373,6 +406,55 @@ srftq_status srftq_calibrate_lambda(const srftq_shape* s, const uint16_t* x, con
   if (!p.signs) return SRFTQ_ERR_HIP;
   p.lambda_out = lambda;
   return run_misc(srftq::Op::Calibrate, s, p, stream);
+}
+
+srftq_status srftq_householder_matrix(int32_t d, int32_t k, int64_t n, const float* V, float* Q,
+                                     void* stream) {
+  if (d < 1 || d > 256 || k < 0 || k > 1024 || n < 0 || n > 65535) return SRFTQ_ERR_SHAPE;
+  if (n == 0) return SRFTQ_OK;
+  if (!Q || (k > 0 && !V)) return SRFTQ_ERR_NULL;
+  if (!aligned4(Q) || (V && !aligned4(V))) return SRFTQ_ERR_ALIGN;
+  return from_hip(srftq::run_householder(d, k, n, V, Q, (hipStream_t)stream));
+}
+
+srftq_status srftq_quantize_dense(const srftq_shape* s, const float* Q, int64_t q_stride, const uint16_t* x,
+                                  const int8_t* signs, const float* lambda, uint8_t* codes, uint16_t* scales,
+                                  void* stream) {
+  srftq_status st = validate_dense(s, q_stride);
+  if (st != SRFTQ_OK) return st;
+  if (nvec(s) == 0) return SRFTQ_OK;
+  if (!Q || !x || !codes || !scales) return SRFTQ_ERR_NULL;
+  if (!aligned16(Q) || !aligned16(x) || !aligned16(codes) || !aligned16(scales)) return SRFTQ_ERR_ALIGN;
+  if ((st = check_side(signs, lambda)) != SRFTQ_OK) return st;
+  srftq::DenseArgs a = {};
+  a.quantize = true;
+  a.Q = Q;
+  a.q_stride = q_stride;
+  a.lambda = lambda;
+  a.x = x;
+  a.codes_out = codes;
+  a.scales_out = scales;
+  return run_dense(a, s, signs, stream);
+}
+
+srftq_status srftq_dequantize_dense(const srftq_shape* s, const float* Q, int64_t q_stride,
+                                    const uint8_t* codes, const uint16_t* scales, const int8_t* signs,
+                                    const float* lambda, uint16_t* x_out, void* stream) {
+  srftq_status st = validate_dense(s, q_stride);
+  if (st != SRFTQ_OK) return st;
+  if (nvec(s) == 0) return SRFTQ_OK;
+  if (!Q || !codes || !scales || !x_out) return SRFTQ_ERR_NULL;
+  if (!aligned16(Q) || !aligned16(codes) || !aligned16(scales) || !aligned16(x_out)) return SRFTQ_ERR_ALIGN;
+  if ((st = check_side(signs, lambda)) != SRFTQ_OK) return st;
+  srftq::DenseArgs a = {};
+  a.quantize = false;
+  a.Q = Q;
+  a.q_stride = q_stride;
+  a.lambda = lambda;
+  a.codes_in = codes;
+  a.scales_in = scales;
+  a.x_out = x_out;
+  return run_dense(a, s, signs, stream);
 }
 
 const char* srftq_status_string(srftq_status status) {

@@ -92,6 +92,31 @@ hipError_t run_attention_d64(const AttnArgs&, hipStream_t);
 hipError_t run_attention_d128(const AttnArgs&, hipStream_t);
 hipError_t run_attention_d256(const AttnArgs&, hipStream_t);
 
+// Quantize / dequantize with a rotation given as a matrix (dense.h).
+struct DenseArgs {
+  bool quantize;
+  int group, bits;
+  int64_t T;
+  int32_t H, BH;
+  const float* Q;          // [., d, d] fp32, matrix of head bh at Q + bh * q_stride
+  int64_t q_stride;
+  const int8_t* signs;     // never null (shared +1 row when the caller passes none)
+  int32_t sign_stride;     // d, or 0
+  const float* lambda;     // [B, H, d] or null
+  const uint16_t* x;
+  uint8_t* codes_out;
+  uint16_t* scales_out;
+  const uint8_t* codes_in;
+  const uint16_t* scales_in;
+  uint16_t* x_out;
+};
+using RunDenseFn = hipError_t (*)(const DenseArgs&, hipStream_t);
+hipError_t run_dense_d64(const DenseArgs&, hipStream_t);
+hipError_t run_dense_d128(const DenseArgs&, hipStream_t);
+hipError_t run_dense_d256(const DenseArgs&, hipStream_t);
+// Q_m = H_1 ... H_k from V [n, k, d] into Q [n, d, d] (d <= 256, k <= 1024).
+hipError_t run_householder(int d, int k, int64_t n, const float* V, float* Q, hipStream_t st);
+
 // Number of compute units of the current device (cached per device).
 int device_cu_count();
 

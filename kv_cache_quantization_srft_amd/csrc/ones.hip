@@ -7,7 +7,7 @@
 
 namespace srftq {
 
-__device__ int8_t g_plus_ones[256] = {
+__device__ __attribute__((aligned(16))) int8_t g_plus_ones[256] = {
 #define SRFTQ_ONE8 1, 1, 1, 1, 1, 1, 1, 1
 #define SRFTQ_ONE64 SRFTQ_ONE8, SRFTQ_ONE8, SRFTQ_ONE8, SRFTQ_ONE8, SRFTQ_ONE8, SRFTQ_ONE8, SRFTQ_ONE8, SRFTQ_ONE8
     SRFTQ_ONE64, SRFTQ_ONE64, SRFTQ_ONE64, SRFTQ_ONE64

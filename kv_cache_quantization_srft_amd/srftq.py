@@ -82,12 +82,16 @@ def lib() -> ctypes.CDLL:
         L.srftq_attention_workspace_bytes.restype = ctypes.c_size_t
         L.srftq_decode_attention.argtypes = [sp, ctypes.c_int64, ctypes.c_int32, vp, cv, cv, vp,
                                              ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
+        L.srftq_householder_matrix.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, vp, vp, vp]
+        L.srftq_quantize_dense.argtypes = [sp, vp, ctypes.c_int64, vp, vp, vp, vp, vp, vp]
+        L.srftq_dequantize_dense.argtypes = [sp, vp, ctypes.c_int64, vp, vp, vp, vp, vp, vp]
         L.srftq_status_string.argtypes = [ctypes.c_int]
         L.srftq_status_string.restype = ctypes.c_char_p
         L.srftq_version.argtypes = []
         for f in ("srftq_validate", "srftq_quantize", "srftq_dequantize", "srftq_rotate",
                   "srftq_unrotate", "srftq_calibrate_lambda", "srftq_cache_append",
-                  "srftq_cache_read", "srftq_decode_attention", "srftq_version"):
+                  "srftq_cache_read", "srftq_decode_attention", "srftq_householder_matrix",
+                  "srftq_quantize_dense", "srftq_dequantize_dense", "srftq_version"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -168,6 +172,20 @@ def srftq_decode_attention(shape, t_cap, q_per_kv, q, k_view, v_view, lengths, s
                                         None if v_view is None else ctypes.byref(v_view), _dp(lengths),
                                         float(scale), _dp(out), _dp(workspace), int(workspace_bytes),
                                         _stream(stream))
+
+
+def srftq_householder_matrix(d, k, n, V, Q, stream=None) -> int:
+    return lib().srftq_householder_matrix(int(d), int(k), int(n), _dp(V), _dp(Q), _stream(stream))
+
+
+def srftq_quantize_dense(shape, Q, q_stride, x, signs, lam, codes, scales, stream=None) -> int:
+    return lib().srftq_quantize_dense(ctypes.byref(shape), _dp(Q), int(q_stride), _dp(x), _dp(signs),
+                                      _dp(lam), _dp(codes), _dp(scales), _stream(stream))
+
+
+def srftq_dequantize_dense(shape, Q, q_stride, codes, scales, signs, lam, x_out, stream=None) -> int:
+    return lib().srftq_dequantize_dense(ctypes.byref(shape), _dp(Q), int(q_stride), _dp(codes), _dp(scales),
+                                        _dp(signs), _dp(lam), _dp(x_out), _stream(stream))
 
 
 def srftq_rotate(shape, x, signs, y, stream=None) -> int:
@@ -408,3 +426,68 @@ def calibrate_lambda(x, signs=None, rot="srft", variant="default", out=None, str
     sh = make_shape(B, T, H, d, 8, 4, rot, variant)
     _check(srftq_calibrate_lambda(sh, x, signs, out, stream), "srftq_calibrate_lambda")
     return out if x.dim() == 4 else out[0]
+
+
+def householder_matrix(V, out=None, stream=None):
+    """Products of Householder reflections: V fp32 [..., k, d] (device) ->
+    Q fp32 [..., d, d], Q = H_1 ... H_k with H_i = I - 2 v_i v_i^T / |v_i|^2."""
+    import torch
+    _req(V, torch.float32, "V")
+    *lead, k, d = V.shape
+    n = 1
+    for m in lead:
+        n *= m
+    out = _out(out, tuple(lead) + (d, d), torch.float32, V.device, "out")
+    _check(srftq_householder_matrix(d, k, n, V, out, stream), "srftq_householder_matrix")
+    return out
+
+
+def _q_stride(Q, B, H, d):
+    if tuple(Q.shape) == (d, d):
+        return 0
+    if tuple(Q.shape) == (B, H, d, d):
+        return d * d
+    raise ValueError(f"Q must be [d, d] or [B, H, d, d] = [{B}, {H}, {d}, {d}], got {tuple(Q.shape)}")
+
+
+def quantize_dense(x, Q, signs=None, lam=None, group=16, bits=4, codes=None, scales=None, stream=None):
+    """As quantize() with the rotation y = Q (s . x): Q fp32 [d, d] (every
+    head) or [B, H, d, d] (per head), e.g. from householder_matrix()."""
+    import torch
+    B, T, H, d = _dims(x)
+    _req(x, torch.float16, "x")
+    _req(Q, torch.float32, "Q")
+    _req(signs, torch.int8, "signs")
+    _req(lam, torch.float32, "lambda")
+    qs = _q_stride(Q, B, H, d)
+    lead = _cache_lead(x)
+    codes = _out(codes, lead + (d * bits // 8,), torch.uint8, x.device, "codes")
+    scales = _out(scales, lead + (max(d // max(group, 1), 1),), torch.float16, x.device, "scales")
+    sh = make_shape(B, T, H, d, group, bits, "none")
+    _check(srftq_quantize_dense(sh, Q, qs, x, signs, lam, codes, scales, stream), "srftq_quantize_dense")
+    return codes, scales
+
+
+def dequantize_dense(codes, scales, Q, signs=None, lam=None, group=16, bits=4, d=None, out=None, stream=None):
+    """As dequantize() with x = s . (Q^T yhat)."""
+    import torch
+    _req(codes, torch.uint8, "codes")
+    _req(scales, torch.float16, "scales")
+    _req(Q, torch.float32, "Q")
+    _req(signs, torch.int8, "signs")
+    _req(lam, torch.float32, "lambda")
+    if d is None:
+        d = codes.shape[-1] * 8 // bits
+    if codes.dim() == 3:
+        H, T = codes.shape[:2]
+        B, oshape = 1, (T, H, d)
+    elif codes.dim() == 4:
+        B, H, T = codes.shape[:3]
+        oshape = (B, T, H, d)
+    else:
+        raise ValueError("codes must be [H,T,*] or [B,H,T,*]")
+    qs = _q_stride(Q, B, H, d)
+    out = _out(out, oshape, torch.float16, codes.device, "out")
+    sh = make_shape(B, T, H, d, group, bits, "none")
+    _check(srftq_dequantize_dense(sh, Q, qs, codes, scales, signs, lam, out, stream), "srftq_dequantize_dense")
+    return out

@@ -27,6 +27,14 @@ sub-stream per quantity):
               lambda calibrated per rotated coordinate; group 16; int4.
   roundtrip   [T=131072, H=8, d=128]; x ~ Student-t(nu=3); lambda = 1;
               group 16; int4.
+  householder the Householder rotation at d = 256 ("When Quantization Is
+              Free", Metodologia 3: k = d/2 reflectors at d = 256, the head
+              size of Gemma-3 1B, one of the pages' models): 26 layers x
+              {K, V} = B=52 tensors of [T=32768, H=1, d=256];
+              x = N(0,1) * sigma[b,h,c], sigma ~ LogNormal(0,1),
+              round(0.01*H*d) = 3 channels x 30; lambda = 1; group 16;
+              int4; per (tensor, head) k = 128 reflector vectors ~ N(0, I)
+              in fp32 (``reflectors``), standing in for learned ones.
 
 Signs: one +-1 vector per (tensor, head), int8, drawn uniformly.
 
@@ -42,7 +50,7 @@ import numpy as np
 
 MASTER_SEED = 20260508
 
-_STREAM = {"x": 1, "signs": 2, "sigma": 3, "outlier": 4, "query": 5}
+_STREAM = {"x": 1, "signs": 2, "sigma": 3, "outlier": 4, "query": 5, "reflectors": 6}
 
 
 @dataclass(frozen=True)
@@ -62,6 +70,7 @@ class Workload:
     calibrated_lambda: bool = False
     rots: tuple = field(default=("srft",))
     steps: int = 1
+    reflectors: int = 0        # householder: reflector vectors per (tensor, head)
 
     @property
     def seed(self) -> int:
@@ -86,6 +95,8 @@ WORKLOADS = {
                      outlier_frac=0.01, outlier_gain=30.0, calibrated_lambda=True,
                      rots=("srft", "srht")),
     "roundtrip": Workload("roundtrip", 4, 1, 131072, 8, 128, 16, 4, "student_t3"),
+    "householder": Workload("householder", 5, 52, 32768, 1, 256, 16, 4, "lognormal",
+                            outlier_frac=0.01, outlier_gain=30.0, rots=(), reflectors=128),
 }
 
 
@@ -147,6 +158,13 @@ def values(w: Workload, B: int | None = None, T: int | None = None,
             v *= g[b][None]
             out[b, t0:t1] = v.astype(np.float16)
     return out
+
+
+def reflectors(w: Workload, B: int | None = None) -> np.ndarray:
+    """Householder reflector vectors, fp32 [B, H, k, d] ~ N(0, I)."""
+    B = w.B if B is None else B
+    r = _rng(w.seed, "reflectors")
+    return r.standard_normal((B, w.H, w.reflectors, w.d), dtype=np.float32)
 
 
 def attention_queries(w: Workload, R: int) -> np.ndarray:

@@ -181,6 +181,50 @@ def test_attention_workspace_and_argument_errors():
     assert call(shape=S.make_shape(0, 1000, 2, 128, 16, 4), q=None, out=None, ws=None) == S.SRFTQ_OK
 
 
+def test_dense_argument_errors_return_before_launch():
+    a, mis = _Fake(0x10000), _Fake(0x10008)
+    sh = S.make_shape(2, 64, 4, 256, 16, 4)
+    q = lambda shape=sh, Q=a, qs=0, x=a, signs=None, lam=None, codes=a, scales=a: \
+        S.srftq_quantize_dense(shape, Q, qs, x, signs, lam, codes, scales, stream=0)
+    dq = lambda shape=sh, Q=a, qs=0, codes=a, scales=a, signs=None, lam=None, out=a: \
+        S.srftq_dequantize_dense(shape, Q, qs, codes, scales, signs, lam, out, stream=0)
+    # supported sizes: d 64 / 128 / 256, groups 8 / 16 / 32; rot and variant unused
+    assert q(shape=S.make_shape(2, 64, 4, 96, 16, 4)) == S.SRFTQ_ERR_UNSUPPORTED
+    assert q(shape=S.make_shape(2, 64, 4, 256, 64, 4)) == S.SRFTQ_ERR_UNSUPPORTED
+    assert dq(shape=S.make_shape(2, 64, 4, 128, 128, 8)) == S.SRFTQ_ERR_UNSUPPORTED
+    assert q(shape=S.make_shape(2, 64, 4, 128, 16, 3)) == S.SRFTQ_ERR_UNSUPPORTED
+    assert q(shape=S.make_shape(-1, 64, 4, 128, 16, 4)) == S.SRFTQ_ERR_SHAPE
+    # matrix stride: 0, or at least d*d and a multiple of 4
+    assert q(qs=-1) == S.SRFTQ_ERR_SHAPE
+    assert q(qs=256 * 256 - 4) == S.SRFTQ_ERR_SHAPE
+    assert dq(qs=256 * 256 + 2) == S.SRFTQ_ERR_SHAPE
+    # NULL and misaligned pointers
+    assert q(Q=None) == S.SRFTQ_ERR_NULL
+    assert q(x=None) == S.SRFTQ_ERR_NULL
+    assert dq(out=None) == S.SRFTQ_ERR_NULL
+    assert q(Q=mis) == S.SRFTQ_ERR_ALIGN
+    assert q(codes=mis) == S.SRFTQ_ERR_ALIGN
+    assert dq(scales=mis) == S.SRFTQ_ERR_ALIGN
+    assert q(signs=_Fake(0x10001)) == S.SRFTQ_ERR_ALIGN
+    assert dq(lam=_Fake(0x10002)) == S.SRFTQ_ERR_ALIGN
+    # empty problem
+    empty = S.make_shape(2, 0, 4, 256, 16, 4)
+    assert q(shape=empty, Q=None, x=None, codes=None, scales=None) == S.SRFTQ_OK
+    assert dq(shape=empty, Q=None, codes=None, scales=None, out=None) == S.SRFTQ_OK
+    # Householder products: d 1..256, k 0..1024, n 0..65535
+    hh = lambda d=256, k=128, n=3, V=a, Q=a: S.srftq_householder_matrix(d, k, n, V, Q, stream=0)
+    assert hh(d=0) == S.SRFTQ_ERR_SHAPE
+    assert hh(d=257) == S.SRFTQ_ERR_SHAPE
+    assert hh(k=-1) == S.SRFTQ_ERR_SHAPE
+    assert hh(k=1025) == S.SRFTQ_ERR_SHAPE
+    assert hh(n=-1) == S.SRFTQ_ERR_SHAPE
+    assert hh(n=65536) == S.SRFTQ_ERR_SHAPE
+    assert hh(V=None) == S.SRFTQ_ERR_NULL
+    assert hh(Q=None) == S.SRFTQ_ERR_NULL
+    assert hh(Q=_Fake(0x10002)) == S.SRFTQ_ERR_ALIGN
+    assert hh(n=0, V=None, Q=None) == S.SRFTQ_OK
+
+
 def test_empty_problem_is_a_no_op():
     sh = S.make_shape(1, 0, 8, 128, 16, 4)
     assert S.srftq_quantize(sh, None, None, None, None, None, stream=0) == S.SRFTQ_OK
