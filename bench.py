@@ -327,6 +327,75 @@ def non_pow2_timing(steps: int) -> dict:
             "vectors_per_s_step": n / ((q_ms + dq_ms) * 1e-3)}
 
 
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix-core peak
+
+
+def householder_timing(steps: int) -> dict:
+    """Quantize + dequantize with a Householder rotation (k = d/2 reflectors
+    at d = 256): the 'householder' workload, 52 tensors of fp16 [T=32768,
+    H=1, d=256], group 16, int4, one matrix per tensor built on the device
+    from the workload's seeded reflectors.  The product is a dense
+    contraction on the matrix cores: algorithmic 2 d^2 flops per vector (the
+    kernels execute it as 2 (quantize) / 3 (dequantize) fp16 passes)."""
+    import torch
+
+    from kv_cache_quantization_srft_amd import srftq as S
+    from kv_cache_quantization_srft_amd import workloads as W
+
+    w = W.WORKLOADS["householder"]
+    x, s = W.generate(w)
+    V = W.reflectors(w)
+    dev = torch.device("cuda:0")
+    xd = torch.from_numpy(x).to(dev)
+    sd = torch.from_numpy(s).to(dev)
+    Vd = torch.from_numpy(V).to(dev)
+    del x
+    Q = S.householder_matrix(Vd)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    S.householder_matrix(Vd, out=Q)
+    e1.record()
+    torch.cuda.synchronize()
+    build_ms = e0.elapsed_time(e1)
+    codes, scales = S.quantize_dense(xd, Q, sd, None, w.group, w.bits)
+    xhat = S.dequantize_dense(codes, scales, Q, sd, None, w.group, w.bits)
+    for _ in range(5):
+        S.quantize_dense(xd, Q, sd, None, w.group, w.bits, codes=codes, scales=scales)
+        S.dequantize_dense(codes, scales, Q, sd, None, w.group, w.bits, out=xhat)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    tq = tdq = 0.0
+    for _ in range(steps):
+        ev[0].record()
+        S.quantize_dense(xd, Q, sd, None, w.group, w.bits, codes=codes, scales=scales)
+        ev[1].record()
+        S.dequantize_dense(codes, scales, Q, sd, None, w.group, w.bits, out=xhat)
+        ev[2].record()
+        torch.cuda.synchronize()
+        tq += ev[0].elapsed_time(ev[1])
+        tdq += ev[1].elapsed_time(ev[2])
+    rel = (torch.linalg.vector_norm(xhat.float() - xd.float()) / torch.linalg.vector_norm(xd.float())).item()
+    n = w.nvec
+    q_ms, dq_ms = tq / steps, tdq / steps
+    flops = 2.0 * w.d * w.d * n
+    bpv = algorithmic_bytes_per_vector(w.d, w.group, w.bits)
+    tq_tf, tdq_tf = flops / (q_ms * 1e-3) / 1e12, flops / (dq_ms * 1e-3) / 1e12
+    return {"workload": f"householder: {w.B} x fp16 [T={w.T}, H={w.H}, d={w.d}], k={w.reflectors} "
+                        f"reflectors per tensor, group {w.group}, int{w.bits}",
+            "householder_build_ms": build_ms,
+            "quantize_ms": q_ms, "dequantize_ms": dq_ms,
+            "vectors_per_s_step": n / ((q_ms + dq_ms) * 1e-3),
+            "algorithmic_flops_per_vector": 2 * w.d * w.d,
+            "quantize_TFLOPs": tq_tf, "dequantize_TFLOPs": tdq_tf,
+            "quantize_mfma_frac": tq_tf / MFMA_F16_PEAK_TFLOPS,
+            "dequantize_mfma_frac": tdq_tf / MFMA_F16_PEAK_TFLOPS,
+            "executed_fp16_passes": {"quantize": 2, "dequantize": 3},
+            "quantize_hbm_frac": bpv * n / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "dequantize_hbm_frac": bpv * n / (dq_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "reconstruction_rel_l2": rel}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -454,6 +523,8 @@ def main():
     dec = None if args.no_decode else decode_append_latency()
     attn = None if args.no_decode else decode_attention_timing(w, codes, scales, sd, lam, args.steps)
     d96 = None if args.no_decode else non_pow2_timing(min(args.steps, 50))
+    del xhat
+    hh = None if args.no_decode else householder_timing(min(args.steps, 20))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -490,6 +561,7 @@ def main():
         "decode_append": dec,
         "decode_attention": attn,
         "non_pow2_d96": d96,
+        "householder_d256": hh,
         "device": torch.cuda.get_device_name(0),
         "input_generation_s": gen_s,
     }
