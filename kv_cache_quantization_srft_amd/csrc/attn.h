@@ -118,25 +118,6 @@ __device__ __forceinline__ void wait_blocks(int k) {
   });
 }
 
-// Sign masks of one lane's own head, held in registers (a sign source for
-// forward() when the lanes of a wave belong to different heads).
-// The sign diagonal applied to a lane's own fp16 words (each lane may belong
-// to a different head), before a transform that then takes no signs.
-template <int D>
-__device__ __forceinline__ void apply_lane_signs(const int8_t* row, uint32_t (&w)[D / 2]) {
-  const uint32_t* r = (const uint32_t*)row;   // 4-byte aligned
-  static_for<D / 4>([&](auto ii) {
-    constexpr int i = decltype(ii)::value;
-    const uint32_t sb = r[i];
-    w[2 * i] ^= sign_mask_of(sb);
-    w[2 * i + 1] ^= sign_mask_of(sb >> 16);
-  });
-}
-struct NoSigns {
-  __device__ __forceinline__ uint32_t mask(int) const { return 0u; }
-  __device__ __forceinline__ uint4 mask4(int) const { return make_uint4(0u, 0u, 0u, 0u); }
-};
-
 // Two fp16 lanes holding 0x6400 | n (= 1024 + n), minus the bias: exact small
 // integers.
 __device__ __forceinline__ uint32_t f16x2_minus(uint32_t w, float bias) {

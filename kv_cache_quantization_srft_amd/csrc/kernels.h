@@ -88,6 +88,23 @@ struct Cursor {
   }
 };
 
+// The sign diagonal applied to a lane's own fp16 words (each lane may belong
+// to a different head), before a transform that then takes no signs.
+template <int D>
+__device__ __forceinline__ void apply_lane_signs(const int8_t* row, uint32_t (&w)[D / 2]) {
+  const uint32_t* r = (const uint32_t*)row;   // 4-byte aligned
+  static_for<D / 4>([&](auto ii) {
+    constexpr int i = decltype(ii)::value;
+    const uint32_t sb = r[i];
+    w[2 * i] ^= sign_mask_of(sb);
+    w[2 * i + 1] ^= sign_mask_of(sb >> 16);
+  });
+}
+struct NoSigns {
+  __device__ __forceinline__ uint32_t mask(int) const { return 0u; }
+  __device__ __forceinline__ uint4 mask4(int) const { return make_uint4(0u, 0u, 0u, 0u); }
+};
+
 // Row of token t of head bh in x [B,T,H,D]: ((b*T + t)*H + h).
 __device__ __forceinline__ int64_t row_index(const Geo& a, int bh, int64_t t) {
   const int b = bh / a.H, h = bh - b * a.H;

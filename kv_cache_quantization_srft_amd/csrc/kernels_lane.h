@@ -87,6 +87,46 @@ __global__ __launch_bounds__(64) void quantize_lane_kernel(const uint16_t* __res
   store_row_bytes<SB>((uint8_t*)scales_out + row * SB, scales);
 }
 
+// Quantize a few tokens per tensor (decode steps: T = 1 .. 8), one vector per
+// lane over the flattened (tensor, token, head) index, so every lane of the
+// grid is live; the tiled kernels give each (tensor, head) a 64-token tile,
+// which for one token leaves 63 of its 64 lanes idle.  Each lane applies its
+// own head's signs and lambda; the transform and the quantizer tail are the
+// same code.  Cache rows follow the tiled kernels: row pos[b] + t of head
+// (b, h) (or t), dropped outside [0, pitch).
+template <int D, int G, int BITS, int ROT, int VAR, bool LAM>
+__global__ __launch_bounds__(64) void quantize_flat_kernel(const uint16_t* __restrict__ x,
+                                                           const int8_t* __restrict__ signs,
+                                                           const float* __restrict__ lambda,
+                                                           uint8_t* __restrict__ codes_out,
+                                                           uint16_t* __restrict__ scales_out, Geo a) {
+  constexpr int CB = D * BITS / 8;
+  constexpr int SB = 2 * D / G;
+  const int64_t v = (int64_t)blockIdx.x * 64 + threadIdx.x;   // ((b*T + t)*H + h)
+  if (v >= (int64_t)a.BH * a.T) return;
+  const int64_t bt = v / a.H;
+  const int h = (int)(v - bt * a.H);
+  const int64_t b = bt / a.T;
+  const int64_t t = bt - b * a.T;
+  const int64_t bh = b * a.H + h;
+  uint32_t w[D / 2];
+  load_words<D / 2>((const uint8_t*)x + v * (2 * D), w);
+  apply_lane_signs<D>(signs + bh * a.sign_stride, w);
+  float y[D];
+  forward<D, ROT, VAR>(w, NoSigns{}, y);
+  uint32_t codes[CodeWords<D, BITS>::kWords];
+  uint32_t scales[ScaleWords<D, G>::kWords];
+  quantize_tail<D, G, BITS, ROT, VAR, LAM>(y, LAM ? lambda + bh * D : nullptr, codes, scales);
+  int64_t tc = t;
+  if (a.pos) {
+    tc += a.pos[b];
+    if (tc < 0 || tc >= a.pitch) return;
+  }
+  const int64_t row = bh * a.pitch + tc;
+  store_row_bytes<CB>(codes_out + row * CB, codes);
+  store_row_bytes<SB>((uint8_t*)scales_out + row * SB, scales);
+}
+
 template <int D, int G, int BITS, int ROT, int VAR, bool LAM>
 __global__ __launch_bounds__(64) void dequantize_lane_kernel(const uint8_t* __restrict__ codes_in,
                                                              const uint16_t* __restrict__ scales_in,

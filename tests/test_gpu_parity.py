@@ -305,3 +305,50 @@ def test_many_tensors_single_token():
     x, s, _ = rand_case(4343, 4096, 1, 2, 128)
     print(f"[B=4096, T=1] {x.shape}", flush=True)
     print(run_and_check(x, s, None, 16, 4, "srht", "default"))
+
+
+@pytest.mark.parametrize("T", [1, 2, 5, 8, 9])
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_few_tokens_one_vector_per_lane(T, d):
+    """Up to 8 tokens per tensor quantize one vector per lane over the
+    flattened (tensor, token, head) index (decode steps); 9 takes the tiled
+    kernel.  Many tensors and heads, every rotation path, lambda on and off."""
+    B, H = 37, 3
+    for i, (rot, variant) in enumerate(ROTS):
+        lam = (i + T) % 2 == 0
+        g, bits = [(16, 4), (32, 8), (8, 4), (64, 8)][i]
+        x, s, l = rand_case(8000 + 10 * T + d + i, B, T, H, d, lam=lam)
+        print(f"[few tokens T={T} d={d} {rot}/{variant} g={g} b={bits} lam={lam}]", flush=True)
+        run_and_check(x, s, l, g, bits, rot, variant, dequant=False)
+
+
+def test_few_tokens_append_ragged_positions():
+    """One-vector-per-lane appends at ragged positions, some rows past the
+    capacity or negative (dropped), against the oracle's cache."""
+    B, T, H, d, cap, g, bits = 9, 3, 4, 128, 20, 16, 4
+    x, s, l = rand_case(8100, B, T, H, d, lam=True)
+    pos = np.array([0, 5, 17, 18, 19, -1, -3, 10, 100], dtype=np.int32)
+    cc = torch.full((B, H, cap, d * bits // 8), 0x5A, dtype=torch.uint8, device="cuda")
+    cs = torch.full((B, H, cap, d // g), 7.0, dtype=torch.float16, device="cuda")
+    S.cache_append(dev(x), cc, cs, dev(pos), dev(s), dev(l), g, bits)
+    torch.cuda.synchronize()
+    co = np.full((B, H, cap, d * bits // 8), 0x5A, dtype=np.uint8)
+    so = np.full((B, H, cap, d // g), np.float16(7.0).view(np.uint16), dtype=np.uint16)
+    co, so = oracle.cache_append(co, so, x, pos, s, l, g, bits, "srft")
+    _, _, z = oracle.quantize(x, s, l, g, bits, "srft", return_z=True)
+    cg, sg = host(cc), host(cs).view(np.uint16)
+    # rows the oracle leaves untouched must be untouched; written rows pass the parity bar
+    written = np.zeros((B, H, cap), dtype=bool)
+    for b in range(B):
+        for t in range(T):
+            r = pos[b] + t
+            if 0 <= r < cap:
+                written[b, :, r] = True
+    assert np.array_equal(cg[~written], co[~written]) and np.array_equal(sg[~written], so[~written])
+    zc = np.zeros((B, H, cap, d), dtype=np.float32)
+    for b in range(B):
+        for t in range(T):
+            r = pos[b] + t
+            if 0 <= r < cap:
+                zc[b, :, r] = z[b, :, t]
+    print(compare.check_quantize(cg[written], sg[written], co[written], so[written], zc[written], bits, g, d))
