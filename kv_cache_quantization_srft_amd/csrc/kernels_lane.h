@@ -2,10 +2,15 @@
 // not cover (d = 96: the SRFT of any even d is defined, "When Quantization Is
 // Free", Metodologia 1, and d = 3 * 2^k takes a radix-3 step, xform.h).
 //
-// One 64-token tile of one (tensor, head) per block, one vector per lane as
-// in kernels.h, but each lane loads and stores its own rows directly: the
-// LDS row tiles of the streaming kernels assume power-of-two row sizes.  The
-// transform, the quantizer tail and the dequantizer head are the same code.
+// One 64-token tile of one (tensor, head) per block (one wave), one vector
+// per lane as in kernels.h.  The fp16 rows (2D bytes, D/8 16-byte chunks;
+// 192 bytes at d = 96) pass through LDS so that global memory sees whole
+// rows: quantize fetches its tile by LDS-DMA, dequantize writes its output
+// tile from LDS.  Chunk c of row v sits at chunk position c ^ ((v >> 2) & 3)
+// (the chunk count is a multiple of 4, so this stays inside the row), which
+// keeps the 16 rows of a read phase in different banks.  Code and scale rows
+// (48 and 6/12/24 bytes at d = 96) are stored per lane.  The transform, the
+// quantizer tail and the dequantizer head are the same code.
 #pragma once
 
 #include "kernels.h"
@@ -55,6 +60,9 @@ __device__ __forceinline__ void load_row_bytes(const uint8_t* src, uint32_t (&v)
   }
 }
 
+// Chunk position of chunk c of tile row v (and back: the same XOR).
+__device__ __forceinline__ int lane_swz(int v) { return (v >> 2) & 3; }
+
 template <int D, int G, int BITS, int ROT, int VAR, bool LAM>
 __global__ __launch_bounds__(64) void quantize_lane_kernel(const uint16_t* __restrict__ x,
                                                            const int8_t* __restrict__ signs,
@@ -63,28 +71,92 @@ __global__ __launch_bounds__(64) void quantize_lane_kernel(const uint16_t* __res
                                                            uint16_t* __restrict__ scales_out, Geo a) {
   constexpr int CB = D * BITS / 8;
   constexpr int SB = 2 * D / G;
+  constexpr int CH = 2 * D / 16;   // 16-byte chunks per fp16 row
+  static_assert(CH % 4 == 0, "chunk swizzle stays inside the row");
+  __shared__ __attribute__((aligned(16))) uint8_t xt[64 * 2 * D];
   const int lane = threadIdx.x;
   const int tile = blockIdx.x;
   const int k = tile / a.BH, bh = tile - k * a.BH;
-  const int64_t t = (int64_t)k * 64 + lane;
-  if (t >= a.T) return;
+  const int64_t t0 = (int64_t)k * 64;
+  const int nv = a.T - t0 < 64 ? (int)(a.T - t0) : 64;
+  // the tile by LDS-DMA: slot p = 64 i + lane holds chunk (p % CH) ^ swz of
+  // row p / CH (rows past T re-read the last row)
+  {
+    const uint8_t* base = (const uint8_t*)x + row_index(a, bh, t0) * (2 * D);
+    const uint32_t stride = (uint32_t)a.H * (2 * D);
+    static_for<CH>([&](auto ii) {
+      constexpr int i = decltype(ii)::value;
+      const int p = 64 * i + lane;
+      const int v = p / CH;
+      const int c = (p % CH) ^ lane_swz(v);
+      const int vv = v < nv ? v : nv - 1;
+      dma_to_lds<16>(base, (uint32_t)vv * stride + 16u * (uint32_t)c, lds_addr(xt) + 1024u * i);
+    });
+    wait_vm<0>();
+    wave_fence();
+  }
   uint32_t w[D / 2];
-  load_words<D / 2>((const uint8_t*)x + row_index(a, bh, t) * (2 * D), w);
+  {
+    const int sw = lane_swz(lane);
+    static_for<CH>([&](auto cc) {
+      constexpr int c = decltype(cc)::value;
+      const uint4 q = *(const uint4*)(xt + lane * (2 * D) + 16 * (c ^ sw));
+      w[4 * c + 0] = q.x;
+      w[4 * c + 1] = q.y;
+      w[4 * c + 2] = q.z;
+      w[4 * c + 3] = q.w;
+    });
+  }
   const HeadSigns sg(signs + (int64_t)bh * a.sign_stride);
   float y[D];
   forward<D, ROT, VAR>(w, sg, y);
   uint32_t codes[CodeWords<D, BITS>::kWords];
   uint32_t scales[ScaleWords<D, G>::kWords];
   quantize_tail<D, G, BITS, ROT, VAR, LAM>(y, LAM ? lambda + (int64_t)bh * D : nullptr, codes, scales);
-  // cache row: token t, or the tensor's append position + t (dropped outside [0, pitch))
-  int64_t tc = t;
-  if (a.pos) {
-    tc += a.pos[bh / a.H];
-    if (tc < 0 || tc >= a.pitch) return;
+  // The tile's code and scale rows through LDS (the x tile is no longer
+  // read: every lane has its row), then out as two contiguous runs: cache
+  // row r0 + v for tile row v, r0 = t0 or the tensor's append position + t0;
+  // rows past T, and rows outside [0, pitch), are not written.
+  static_assert(CB % 16 == 0, "code rows are whole 16-byte chunks");
+  constexpr int SE = SB % 16 == 0 ? 16 : SB % 4 == 0 ? 4 : 2;   // scale store granule
+  uint8_t* oc = xt;
+  uint8_t* osc = xt + 64 * CB;
+  static_for<CB / 16>([&](auto cc) {
+    constexpr int c = decltype(cc)::value;
+    *(uint4*)(oc + lane * CB + 16 * c) = make_uint4(codes[4 * c], codes[4 * c + 1], codes[4 * c + 2], codes[4 * c + 3]);
+  });
+  if constexpr (SB % 4 == 0) {
+    static_for<SB / 4>([&](auto ii) { *(uint32_t*)(osc + lane * SB + 4 * decltype(ii)::value) = scales[decltype(ii)::value]; });
+  } else {
+    static_for<SB / 2>([&](auto ii) {
+      constexpr int i = decltype(ii)::value;
+      *(uint16_t*)(osc + lane * SB + 2 * i) = (uint16_t)(scales[i / 2] >> (16 * (i % 2)));
+    });
   }
-  const int64_t row = cache_row(a, bh, tc);
-  store_row_bytes<CB>(codes_out + row * CB, codes);
-  store_row_bytes<SB>((uint8_t*)scales_out + row * SB, scales);
+  wait_lgkm0();
+  wave_fence();
+  const int64_t r0 = t0 + (a.pos ? (int64_t)a.pos[bh / a.H] : 0);
+  uint8_t* cbase = codes_out + cache_row(a, bh, 0) * CB;
+  uint8_t* sbase = (uint8_t*)scales_out + cache_row(a, bh, 0) * SB;
+  auto row_ok = [&](int v) { return v < nv && r0 + v >= 0 && r0 + v < a.pitch; };
+  static_for<(64 * CB / 16 + 63) / 64>([&](auto ii) {
+    constexpr int i = decltype(ii)::value;
+    const int q = 64 * i + lane;   // 16-byte chunk of the tile's code rows
+    const int v = q * 16 / CB;
+    if (q < 64 * CB / 16 && row_ok(v))
+      *(uint4*)(cbase + (r0 + v) * CB + (q * 16 - v * CB)) = *(const uint4*)(oc + 16 * q);
+  });
+  static_for<(64 * SB / SE + 63) / 64>([&](auto ii) {
+    constexpr int i = decltype(ii)::value;
+    const int e = 64 * i + lane;   // granule of the tile's scale rows
+    const int v = e * SE / SB;
+    if (e < 64 * SB / SE && row_ok(v)) {
+      uint8_t* dst = sbase + (r0 + v) * SB + (e * SE - v * SB);
+      if constexpr (SE == 16) *(uint4*)dst = *(const uint4*)(osc + SE * e);
+      else if constexpr (SE == 4) *(uint32_t*)dst = *(const uint32_t*)(osc + SE * e);
+      else *(uint16_t*)dst = *(const uint16_t*)(osc + SE * e);
+    }
+  });
 }
 
 // Quantize a few tokens per tensor (decode steps: T = 1 .. 8), one vector per
@@ -136,7 +208,10 @@ __global__ __launch_bounds__(64) void dequantize_lane_kernel(const uint8_t* __re
   using Sc = Scales<D, ROT, VAR>;
   constexpr int CB = D * BITS / 8;
   constexpr int SB = 2 * D / G;
+  constexpr int CH = 2 * D / 16;   // 16-byte chunks per fp16 row
+  static_assert(CH % 4 == 0, "chunk swizzle stays inside the row");
   __shared__ float lt[LAM ? D : 1];
+  __shared__ __attribute__((aligned(16))) uint8_t xo[64 * 2 * D];
   const int lane = threadIdx.x;
   const int tile = blockIdx.x;
   const int k = tile / a.BH, bh = tile - k * a.BH;
@@ -149,9 +224,11 @@ __global__ __launch_bounds__(64) void dequantize_lane_kernel(const uint8_t* __re
     }
     __syncthreads();
   }
-  const int64_t t = (int64_t)k * 64 + lane;
-  if (t >= a.T) return;
-  const int64_t row = cache_row(a, bh, t);
+  const int64_t t0 = (int64_t)k * 64;
+  const int nv = a.T - t0 < 64 ? (int)(a.T - t0) : 64;
+  const int64_t t = t0 + lane;
+  const bool live = lane < nv;
+  const int64_t row = cache_row(a, bh, live ? t : t0);
   uint32_t codes[CodeWords<D, BITS>::kWords];
   uint32_t scales[ScaleWords<D, G>::kWords];
   load_row_bytes<CB>(codes_in + row * CB, codes);
@@ -166,7 +243,27 @@ __global__ __launch_bounds__(64) void dequantize_lane_kernel(const uint8_t* __re
     constexpr int m = decltype(mm)::value;
     o[m] = pack_f16x2(xr[2 * m], xr[2 * m + 1]) ^ sg.mask(m);
   });
-  store_words<D / 2>((uint8_t*)x_out + row_index(a, bh, t) * (2 * D), o);
+  // the output tile through LDS: lane writes its row, then every lane stores
+  // slot p = 64 i + lane (chunk (p % CH) ^ swz of row p / CH), whole rows at a time
+  {
+    const int sw = lane_swz(lane);
+    static_for<CH>([&](auto cc) {
+      constexpr int c = decltype(cc)::value;
+      *(uint4*)(xo + lane * (2 * D) + 16 * (c ^ sw)) =
+          make_uint4(o[4 * c + 0], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]);
+    });
+    wait_lgkm0();
+    wave_fence();
+    uint8_t* base = (uint8_t*)x_out + row_index(a, bh, t0) * (2 * D);
+    const int64_t stride = (int64_t)a.H * (2 * D);
+    static_for<CH>([&](auto ii) {
+      constexpr int i = decltype(ii)::value;
+      const int p = 64 * i + lane;
+      const int v = p / CH;
+      const int c = (p % CH) ^ lane_swz(v);
+      if (v < nv) *(uint4*)(base + v * stride + 16 * c) = *(const uint4*)(xo + 16 * p);
+    });
+  }
 }
 
 }  // namespace srftq
