@@ -16,9 +16,10 @@
 //                        stored as 2^-e_r u_r with e_r putting max |u_r| in
 //                        [2^10, 2^11) (so that its fp16 parts neither
 //                        overflow nor go subnormal) plus the factor 2^e_r
-//                        (one lane per query head).
-//   attn_partial_kernel  one block of 4 waves per chunk of 4 * span tokens of
-//                        one (tensor, KV head); per 16-token block a wave
+//                        (one wave per query head).
+//   attn_partial_kernel  one block of 4 waves per chunk of one (tensor, KV
+//                        head) (the tensor's 16-token blocks split evenly
+//                        over its chunks' waves); per 16-token block a wave
 //                        computes the scores of 16 query heads (R used, the
 //                        rest zero) with v_mfma_f32_16x16x16_f16 -- the codes
 //                        are exact in fp16 (A), the query coordinates are
@@ -164,8 +165,86 @@ __device__ __forceinline__ uint32_t scale_pair(uint32_t tile, int row, int g) {
 }
 
 // ----------------------------------------------------------------------------
-// u = M (s_k . q) * scale * log2(e) / lambda_k, one lane per query head
-// v = b*H*R + h*R + r (KV head bh = v / R).
+// Transforms of single vectors spread over a wave (the query rotation and the
+// output unrotation, one vector per query head): cooperative, so that their
+// latency is a few hundred instructions rather than a whole transform on one
+// lane.
+// ----------------------------------------------------------------------------
+
+// (cos, -sin)(2 pi m / D) for m in [0, D), interleaved: the DFT kernel
+// exp(-2 pi i m / D) rounded to fp32 from the compile-time series.
+template <int D>
+struct DftTwiddles {
+  float v[2 * D];
+  constexpr DftTwiddles() : v{} {
+    for (int m = 0; m < D; ++m) {
+      const int mm = 2 * m <= D ? m : m - D;   // angle in (-pi, pi]
+      const double ang = 2.0 * kPi * mm / D;
+      v[2 * m] = (float)ccos(ang);
+      v[2 * m + 1] = -(float)csin(ang);
+    }
+  }
+};
+template <int D>
+__device__ __forceinline__ const float* dft_twiddles() {
+  static constexpr DftTwiddles<D> kTab{};
+  return kTab.v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  static_for<6>([&](auto ii) { v += __shfl_xor(v, 1 << decltype(ii)::value); });
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+  static_for<6>([&](auto ii) { v = __builtin_fmaxf(v, __shfl_xor(v, 1 << decltype(ii)::value)); });
+  return v;
+}
+
+// A d-vector spread over one wave: lane l holds elements P l .. P l + P - 1
+// (d = 64: lanes 0..31 hold two each, the rest none).
+template <int D>
+struct WaveVec {
+  static constexpr int P = D >= 128 ? D / 64 : 2;
+  static constexpr int NL = D / P;   // lanes holding elements
+};
+
+// Unnormalized Walsh-Hadamard transform in natural (Sylvester) order,
+// y_j = sum_m (-1)^popcount(j & m) x_m, of a vector laid out as in WaveVec:
+// butterflies over the in-lane index bits, then over the lane bits through
+// lane exchanges.
+template <int D>
+__device__ __forceinline__ void wave_fwht(float (&x)[WaveVec<D>::P], int lane) {
+  constexpr int P = WaveVec<D>::P, NL = WaveVec<D>::NL;
+  static_for<P>([&](auto hh) {
+    constexpr int h = decltype(hh)::value;
+    static_for<P>([&](auto tt) {
+      constexpr int t = decltype(tt)::value;
+      if constexpr ((h & (h - 1)) == 0 && h > 0 && (t & h) == 0 && t + h < P) {
+        const float a = x[t], b = x[t + h];
+        x[t] = a + b;
+        x[t + h] = a - b;
+      }
+    });
+  });
+  static_for<6>([&](auto bb) {
+    constexpr int msk = 1 << decltype(bb)::value;
+    if constexpr (msk < NL) {
+      static_for<P>([&](auto tt) {
+        constexpr int t = decltype(tt)::value;
+        const float o = __shfl_xor(x[t], msk);
+        x[t] = (lane & msk) ? o - x[t] : x[t] + o;
+      });
+    }
+  });
+}
+
+// ----------------------------------------------------------------------------
+// u = M (s_k . q) * scale * log2(e) / lambda_k for one query head per wave,
+// v = b*H*R + h*R + r (KV head bh = v / R).  SRFT: lane k accumulates the
+// DFT bin X_k = sum_m x_m exp(-2 pi i k m / d) from the LDS copy of x and the
+// twiddle table (two bins per lane at d = 256), and the bin X_{d/2} is the
+// alternating sum of x; the packed coordinates are Re X_0..Re X_{d/2},
+// Im X_1..Im X_{d/2-1} with the orthonormal scales.  SRHT: wave_fwht.
 // ----------------------------------------------------------------------------
 template <int D, int ROT>
 __global__ __launch_bounds__(64) void attn_qprep_kernel(const uint16_t* __restrict__ q,
@@ -174,46 +253,117 @@ __global__ __launch_bounds__(64) void attn_qprep_kernel(const uint16_t* __restri
                                                         float* __restrict__ uq,
                                                         float* __restrict__ uexp, AttnGeo a) {
   using Sc = Scales<D, ROT, VAR_REAL>;
-  const int64_t v = (int64_t)blockIdx.x * 64 + threadIdx.x;
-  if (v >= (int64_t)a.BH * a.R) return;
+  constexpr int P = WaveVec<D>::P, NL = WaveVec<D>::NL;
+  constexpr int N = D / 2;
+  constexpr int KPL = N >= 64 ? N / 64 : 1;                   // SRFT bins per lane
+  constexpr int NO = ROT == ROT_SRFT ? 2 * KPL : P;            // outputs per lane
+  __shared__ __attribute__((aligned(16))) float xs[ROT == ROT_SRFT ? D : 4];
+  __shared__ __attribute__((aligned(16))) float tw[ROT == ROT_SRFT ? 2 * D : 4];
+  const int lane = threadIdx.x;
+  const int64_t v = blockIdx.x;
   const int64_t bh = v / a.R;
-  uint32_t w[D / 2];
-  load_words<D / 2>((const uint8_t*)q + v * (2 * D), w);
-  apply_lane_signs<D>(signs_k + bh * a.sign_stride_k, w);
-  float y[D];
-  forward<D, ROT, VAR_REAL>(w, NoSigns{}, y);
-  const float* lam = lam_k ? lam_k + bh * D : nullptr;
-  const bool lam16 = ((uintptr_t)lam & 15u) == 0;   // rows of 16-byte aligned lambda load as float4
-  float mx = 0.0f;
-  static_for<D / 4>([&](auto kk) {
-    constexpr int k = decltype(kk)::value;
-    float li[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-    if (lam) {
-      if (lam16) {
-        const float4 l4 = *(const float4*)(lam + 4 * k);
-        li[0] = l4.x, li[1] = l4.y, li[2] = l4.z, li[3] = l4.w;
-      } else {
-        static_for<4>([&](auto ee) { li[decltype(ee)::value] = lam[4 * k + decltype(ee)::value]; });
-      }
+
+  // x = s_k (.) q, elements P lane .. P lane + P - 1
+  float x[P];
+  static_for<P>([&](auto tt) { x[decltype(tt)::value] = 0.0f; });
+  if (lane < NL) {
+    const uint16_t* src = q + v * D + P * lane;
+    if constexpr (P == 2) {
+      const uint32_t w = *(const uint32_t*)src;
+      x[0] = hlo(w), x[1] = hhi(w);
+    } else {
+      static_for<P / 4>([&](auto ii) {
+        constexpr int i = decltype(ii)::value;
+        const uint2 w = *(const uint2*)(src + 4 * i);
+        x[4 * i] = hlo(w.x), x[4 * i + 1] = hhi(w.x), x[4 * i + 2] = hlo(w.y), x[4 * i + 3] = hhi(w.y);
+      });
     }
-    static_for<4>([&](auto ee) {
-      constexpr int e = decltype(ee)::value;
-      constexpr int j = 4 * k + e;
-      float u = y[j] * (float)(Sc::is_edge(j) ? Sc::kFwdEdge : Sc::kFwdBulk) * a.scale_log2e;
-      if (lam) u = u * __builtin_amdgcn_rcpf(li[e]);
-      y[j] = u;
-      mx = __builtin_fmaxf(mx, __builtin_fabsf(u));
+    const int8_t* sg = signs_k + bh * a.sign_stride_k + P * lane;
+    static_for<P>([&](auto tt) {
+      constexpr int t = decltype(tt)::value;
+      if (sg[t] < 0) x[t] = -x[t];
     });
+  }
+
+  float y[NO];
+  int jo[NO];   // coordinate of each output, -1 where the lane has none
+  static_for<NO>([&](auto oo) {
+    constexpr int o = decltype(oo)::value;
+    if constexpr (ROT == ROT_SRFT) {
+      const int k = lane + 64 * (o / 2);
+      jo[o] = k >= N ? -1 : (o & 1) ? (k == 0 ? N : N + k) : k;
+    } else {
+      jo[o] = lane < NL ? P * lane + o : -1;
+    }
   });
+  // 1 / lambda_k of the lane's outputs, loaded before the transform
+  float rl[NO];
+  static_for<NO>([&](auto oo) {
+    constexpr int o = decltype(oo)::value;
+    rl[o] = (lam_k && jo[o] >= 0) ? __builtin_amdgcn_rcpf(lam_k[bh * D + jo[o]]) : 1.0f;
+  });
+  if constexpr (ROT == ROT_SRFT) {
+    if (lane < NL) static_for<P>([&](auto tt) { xs[P * lane + decltype(tt)::value] = x[decltype(tt)::value]; });
+    const float* twg = dft_twiddles<D>();
+    static_for<(2 * D + 63) / 64>([&](auto ii) {
+      const int i = lane + 64 * decltype(ii)::value;
+      if (i < 2 * D) tw[i] = twg[i];
+    });
+    // X_{d/2} = sum_m (-1)^m x_m (P is even: element P l + t has the sign of t)
+    float alt = 0.0f;
+    static_for<P>([&](auto tt) {
+      constexpr int t = decltype(tt)::value;
+      alt += (t & 1) ? -x[t] : x[t];
+    });
+    alt = wave_sum(alt);
+    __syncthreads();
+    static_for<KPL>([&](auto kk) {
+      constexpr int i = decltype(kk)::value;
+      const int k = lane + 64 * i;
+      float re[4] = {0.f, 0.f, 0.f, 0.f}, im[4] = {0.f, 0.f, 0.f, 0.f};
+      if (k < N) {
+        int idx = 0;   // k m mod d
+#pragma unroll 4
+        for (int m = 0; m < D; m += 4) {
+          const float4 xv = *(const float4*)&xs[m];
+          const float xe[4] = {xv.x, xv.y, xv.z, xv.w};
+          static_for<4>([&](auto ee) {
+            constexpr int e = decltype(ee)::value;
+            const float2 w = *(const float2*)&tw[2 * idx];
+            re[e] = __builtin_fmaf(xe[e], w.x, re[e]);
+            im[e] = __builtin_fmaf(xe[e], w.y, im[e]);
+            idx = (idx + k) & (D - 1);
+          });
+        }
+      }
+      y[2 * i] = (re[0] + re[1]) + (re[2] + re[3]);
+      y[2 * i + 1] = k == 0 ? alt : (im[0] + im[1]) + (im[2] + im[3]);
+    });
+  } else {
+    if constexpr (ROT == ROT_SRHT) wave_fwht<D>(x, lane);
+    static_for<P>([&](auto tt) { y[decltype(tt)::value] = x[decltype(tt)::value]; });
+  }
+
+  float mx = 0.0f;
+  static_for<NO>([&](auto oo) {
+    constexpr int o = decltype(oo)::value;
+    const int j = jo[o];
+    if (j >= 0) {
+      float u = y[o] * (float)(Sc::is_edge(j) ? Sc::kFwdEdge : Sc::kFwdBulk) * a.scale_log2e;
+      if (lam_k) u = u * rl[o];
+      y[o] = u;
+      mx = __builtin_fmaxf(mx, __builtin_fabsf(u));
+    }
+  });
+  mx = wave_max(mx);
   // power of two 2^e with max |u| / 2^e in [2^10, 2^11) (e = 0 for u = 0)
   const int e = mx > 0.0f ? __builtin_amdgcn_frexp_expf(mx) - 11 : 0;
   const float down = __builtin_ldexpf(1.0f, -e);
-  float4* dst = (float4*)(uq + v * D);
-  static_for<D / 4>([&](auto kk) {
-    constexpr int k = decltype(kk)::value;
-    dst[k] = make_float4(y[4 * k] * down, y[4 * k + 1] * down, y[4 * k + 2] * down, y[4 * k + 3] * down);
+  static_for<NO>([&](auto oo) {
+    constexpr int o = decltype(oo)::value;
+    if (jo[o] >= 0) uq[v * D + jo[o]] = y[o] * down;
   });
-  uexp[v] = __builtin_ldexpf(1.0f, e);
+  if (lane == 0) uexp[v] = __builtin_ldexpf(1.0f, e);
 }
 
 // ----------------------------------------------------------------------------
@@ -255,8 +405,11 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const uint8_t* __rest
     const int64_t lb = lengths[b];
     len = lb < 0 ? 0 : (lb < a.T ? lb : a.T);
   }
-  const int64_t t_begin = ((int64_t)c * 4 + wave) * a.span;
-  int64_t t_end = t_begin + a.span;
+  // this tensor's 16-token blocks split evenly over the 4 * n_chunks waves of
+  // (tensor, KV head): wave w takes blocks [w nb / nw, (w + 1) nb / nw)
+  const int64_t nb16 = (len + 15) / 16, nw = 4 * (int64_t)a.n_chunks, w = (int64_t)c * 4 + wave;
+  const int64_t t_begin = 16 * (w * nb16 / nw);
+  int64_t t_end = 16 * ((w + 1) * nb16 / nw);
   t_end = t_end < len ? t_end : len;
   const int nblk = t_end > t_begin ? (int)((t_end - t_begin + 15) / 16) : 0;
 
@@ -497,8 +650,9 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const uint8_t* __rest
 // One query head: merge its chunks, w = acc / (l * lambda_v), o = s_v . M^T w.
 // Block = (tensor, query head), 4 waves: the threads split the chunks for
 // the maxima and sums, each wave accumulates every fourth chunk with its
-// lanes splitting the coordinates, the waves add up through LDS, and lane 0
-// unrotates.
+// lanes splitting the coordinates, the waves add up through LDS, and the
+// unrotation runs on all threads: SRFT one output coordinate per thread (a
+// direct inverse DFT from the LDS twiddle table), SRHT wave_fwht on wave 0.
 // ----------------------------------------------------------------------------
 template <int D, int ROT>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ ws_ml,
@@ -509,6 +663,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
   using Sc = Scales<D, ROT, VAR_REAL>;
   constexpr int PER = D / 64;
   __shared__ __attribute__((aligned(16))) float part[4][D];
+  __shared__ __attribute__((aligned(16))) float tw[ROT == ROT_SRFT ? 2 * D : 4];
   __shared__ float red[2][4];
   const int64_t v = blockIdx.x;               // b*H*R + h*R + r
   const int bh = (int)(v / a.R);
@@ -517,6 +672,16 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int NC = a.n_chunks;
   const int64_t s0 = (int64_t)bh * NC * a.R + r;   // slot of chunk 0; chunk c at s0 + c*R
+  if constexpr (ROT == ROT_SRFT) {
+    const float* twg = dft_twiddles<D>();
+    for (int i = t; i < 2 * D; i += 256) tw[i] = twg[i];   // read after the barriers below
+  }
+  constexpr int JPT = (D + 255) / 256;   // coordinates j = t + 256 i per thread
+  float rlv[JPT];
+  static_for<JPT>([&](auto ii) {
+    const int j = t + 256 * decltype(ii)::value;
+    rlv[decltype(ii)::value] = (lam_v && j < D) ? __builtin_amdgcn_rcpf(lam_v[(int64_t)bh * D + j]) : 1.0f;
+  });
 
   // largest chunk maximum and the weighted sum of the chunk sums
   float m = -__builtin_inff();
@@ -554,31 +719,74 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
   __syncthreads();
   l = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
   const float inv_l = l > 0.0f ? 1.0f / l : 0.0f;
-  for (int j = t; j < D; j += 256) {
-    float y = ((part[0][j] + part[1][j]) + (part[2][j] + part[3][j])) * inv_l;
-    if (lam_v) y = y * __builtin_amdgcn_rcpf(lam_v[(int64_t)bh * D + j]);
-    part[0][j] = y * (float)(Sc::is_edge(j) ? Sc::kInvEdge : Sc::kInvBulk);
-  }
+  // z_j = acc_j / (l lambda_j) times the orthonormal scale of coordinate j:
+  // x = M^T (acc / (l lambda)) below takes the unscaled transform of z
+  static_for<JPT>([&](auto ii) {
+    const int j = t + 256 * decltype(ii)::value;
+    if (j < D) {
+      float y = ((part[0][j] + part[1][j]) + (part[2][j] + part[3][j])) * inv_l;
+      if (lam_v) y = y * rlv[decltype(ii)::value];
+      part[0][j] = y * (float)(Sc::is_edge(j) ? Sc::kFwdEdge : Sc::kFwdBulk);
+    }
+  });
   __syncthreads();
-  if (t != 0) return;
-  float y[D];
-  static_for<D / 4>([&](auto kk) {
-    constexpr int k = decltype(kk)::value;
-    const float4 q4 = *(const float4*)(&part[0][4 * k]);
-    y[4 * k] = q4.x;
-    y[4 * k + 1] = q4.y;
-    y[4 * k + 2] = q4.z;
-    y[4 * k + 3] = q4.w;
-  });
-  float x[D];
-  inverse<D, ROT, VAR_REAL>(y, x);
-  const HeadSigns sg(signs_v + (int64_t)bh * a.sign_stride_v);
-  uint32_t o[D];
-  static_for<D>([&](auto jj) {
-    constexpr int j = decltype(jj)::value;
-    o[j] = as_u32(x[j]) ^ (sg.sbit(j) << 31);
-  });
-  store_words<D>((uint8_t*)out + v * (4 * D), o);
+  const int8_t* sg = signs_v + (int64_t)bh * a.sign_stride_v;
+  float* dst = out + v * D;
+  if constexpr (ROT == ROT_SRFT) {
+    // x_m = z_0 + (-1)^m z_{d/2} + sum_{0<k<d/2} (cos(2 pi k m/d) z_k - sin(2 pi k m/d) z_{d/2+k}),
+    // one output per thread
+    constexpr int N = D / 2;
+    if (t < D) {
+      const int m = t;
+      const float* z = part[0];
+      float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+      int idx = 0;   // k m mod d
+#pragma unroll 2
+      for (int k = 0; k < N; k += 4) {
+        const float4 zr = *(const float4*)&z[k];
+        const float4 zi = *(const float4*)&z[N + k];
+        float2 w = *(const float2*)&tw[2 * idx];
+        s0 = __builtin_fmaf(zr.x, w.x, s0);
+        s0 = __builtin_fmaf(zi.x, w.y, s0);
+        idx = (idx + m) & (D - 1);
+        w = *(const float2*)&tw[2 * idx];
+        s1 = __builtin_fmaf(zr.y, w.x, s1);
+        s1 = __builtin_fmaf(zi.y, w.y, s1);
+        idx = (idx + m) & (D - 1);
+        w = *(const float2*)&tw[2 * idx];
+        s2 = __builtin_fmaf(zr.z, w.x, s2);
+        s2 = __builtin_fmaf(zi.z, w.y, s2);
+        idx = (idx + m) & (D - 1);
+        w = *(const float2*)&tw[2 * idx];
+        s3 = __builtin_fmaf(zr.w, w.x, s3);
+        s3 = __builtin_fmaf(zi.w, w.y, s3);
+        idx = (idx + m) & (D - 1);
+      }
+      // the k = 0 term above is z_0 (its sine is 0)
+      float xm = ((s0 + s1) + (s2 + s3)) + ((m & 1) ? -z[N] : z[N]);
+      if (sg[m] < 0) xm = -xm;
+      dst[m] = xm;
+    }
+  } else if constexpr (ROT == ROT_SRHT) {
+    constexpr int P = WaveVec<D>::P, NL = WaveVec<D>::NL;
+    if (wave == 0) {
+      float x[P];
+      static_for<P>([&](auto tt) {
+        constexpr int i = decltype(tt)::value;
+        x[i] = lane < NL ? part[0][P * lane + i] : 0.0f;
+      });
+      wave_fwht<D>(x, lane);
+      if (lane < NL) {
+        static_for<P>([&](auto tt) {
+          constexpr int i = decltype(tt)::value;
+          const int m = P * lane + i;
+          dst[m] = sg[m] < 0 ? -x[i] : x[i];
+        });
+      }
+    }
+  } else {
+    for (int m = t; m < D; m += 256) dst[m] = sg[m] < 0 ? -part[0][m] : part[0][m];
+  }
 }
 
 }  // namespace srftq

@@ -61,8 +61,8 @@ struct AttnGeo {
   int32_t H;             // KV heads per tensor
   int32_t R;             // query heads per KV head, 1..16
   int32_t BH;            // B * H
-  int32_t span;          // tokens per wave, a multiple of 16
-  int32_t n_chunks;      // chunks per (tensor, KV head); a chunk is 4 * span tokens
+  int32_t n_chunks;      // chunks per (tensor, KV head), 4 waves each; a tensor's
+                         // 16-token blocks are split evenly over its 4 * n_chunks waves
   int32_t sign_stride_k; // elements between K heads' sign rows: d, or 0 (shared row)
   int32_t sign_stride_v;
   float scale_log2e;     // softmax scale * log2(e)

@@ -106,12 +106,13 @@ def check(c, got, lengths=None, scale=None):
 @pytest.mark.parametrize("g,bits", [(16, 4), (32, 8), (64, 4)])
 @pytest.mark.parametrize("rot", ["srft", "srht", "none"])
 def test_attention_matrix(d, g, bits, rot):
-    """Several chunks per head, a ragged tail, two tensors of different
-    lengths, grouped query heads; lambda on for half the cases."""
+    """Several chunks per head (1100 tokens: 4 chunks of 4 waves), a ragged
+    tail, two tensors of different lengths, grouped query heads; lambda on
+    for half the cases."""
     R = {64: 1, 128: 6, 256: 16}[d]
     lam = (d + g) % 2 == 0 and rot != "none"
-    c = make_case(7000 + d + g + bits, 2, 300, 2, R, d, g, bits, rot, lam=lam)
-    lengths = np.array([300, 181], dtype=np.int32)
+    c = make_case(7000 + d + g + bits, 2, 1100, 2, R, d, g, bits, rot, lam=lam)
+    lengths = np.array([1100, 681], dtype=np.int32)
     print(f"[attention d={d} g={g} b={bits} {rot} R={R} lam={lam}]", flush=True)
     print(check(c, run_gpu(c, lengths), lengths))
 
@@ -123,6 +124,14 @@ def test_attention_lengths():
     lengths = np.array([0, 1, 15, 16, 17, 64, 80, 500], dtype=np.int32)
     print(check(c, run_gpu(c, lengths), lengths))
     print(check(c, run_gpu(c, None), None))     # every tensor attends T tokens
+
+
+def test_attention_more_heads_than_resident_blocks():
+    """1,200 (tensor, KV head) pairs: one chunk each, a grid of more blocks
+    than the chip holds at once, short ragged lengths."""
+    c = make_case(7150, 300, 40, 4, 2, 64, 16, 4, "srft")
+    lengths = (np.arange(300, dtype=np.int32) * 7) % 45
+    print(check(c, run_gpu(c, lengths), lengths))
 
 
 def test_attention_scale_and_large_scores():
