@@ -500,12 +500,14 @@ def _attn(q, K, V, g, bits, rot, **kw):
                                    lam_v=V[3], group=g, bits=bits, rot=rot, **kw)
 
 
-def test_attention_matches_torch_sdpa():
+@pytest.mark.parametrize("d,g", [(64, 16), (96, 32)])
+def test_attention_matches_torch_sdpa(d, g):
     """Against torch's scaled_dot_product_attention (fp64, CPU) on the
-    oracle's own reconstructions, with grouped query heads and a length mask."""
+    oracle's own reconstructions, with grouped query heads and a length mask
+    (d = 96: the SRFT with its radix-3 step)."""
     import torch
-    B, T, H, R, d, g, bits = 2, 37, 2, 3, 64, 16, 4
-    q, K, V = _attn_case(61, B, T, H, R, d, g, bits, "srft")
+    B, T, H, R, bits = 2, 37, 2, 3, 4
+    q, K, V = _attn_case(61 + d, B, T, H, R, d, g, bits, "srft")
     lengths = np.array([37, 20], dtype=np.int32)
     got = _attn(q, K, V, g, bits, "srft", lengths=lengths)
     _, kh = oracle.dequantize(K[0], K[1], K[2], K[3], g, bits, "srft", d=d, return_f64=True)
@@ -538,12 +540,13 @@ def test_attention_special_cases():
     assert np.array_equal(a, b)
 
 
-def test_attention_scores_in_the_rotated_domain():
+@pytest.mark.parametrize("d", [128, 96])
+def test_attention_scores_in_the_rotated_domain(d):
     """The identity the GPU path relies on: q . k^ = (M (s_k . q)) . y^ with
     y^_j = c_j sigma_G / lambda_j, since M is orthonormal."""
     from oracle.compare import decode_codes
-    B, T, H, R, d, g, bits = 1, 9, 1, 1, 128, 16, 4
-    q, K, _ = _attn_case(63, B, T, H, R, d, g, bits, "srft")
+    B, T, H, R, g, bits = 1, 9, 1, 1, 16, 4
+    q, K, _ = _attn_case(63 + d, B, T, H, R, d, g, bits, "srft")
     _, kh = oracle.dequantize(K[0], K[1], K[2], K[3], g, bits, "srft", d=d, return_f64=True)
     direct = kh[0, :, 0] @ q[0, 0].astype(np.float64)
     u = oracle.rotate(q[:, None], K[2], "srft")[0, 0, 0]                       # M (s . q)
