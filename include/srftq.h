@@ -93,7 +93,7 @@ typedef enum {
  * the Walsh-Hadamard transform) takes the real-input transform with one
  * radix-3 step, for rot SRFT (variants 0 and 1) and NONE; SRHT and variant 2
  * need a power of two and return SRFTQ_ERR_UNSUPPORTED.  Decode attention
- * supports d in {64, 128, 256}.
+ * supports every d above, with the same rotations.
  */
 typedef struct {
     int64_t B;
@@ -223,8 +223,9 @@ srftq_status srftq_cache_read(const srftq_shape* shape, int64_t t_cap, const uin
  *   workspace  device memory of at least srftq_attention_workspace_bytes
  *              (16-B aligned), owned by the caller; contents on entry are
  *              ignored.  Calls that share a workspace must not overlap.
- * The P.V product takes p * sigma_v rounded once to fp16 (as attention
- * kernels round P); every other step is fp32.  Errors as for
+ * The P.V product multiplies fp16(c_v * sigma_v) by fp16(2^14 p) (two
+ * fp16 roundings per term, as attention kernels round P); every other step
+ * is fp32.  Errors as for
  * srftq_quantize; a short workspace is SRFTQ_ERR_SHAPE.
  */
 typedef struct {

@@ -177,7 +177,7 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 bool attn_plan(const srftq_shape* s, int32_t R, AttnPlan* p) {
   if (validate(s) != SRFTQ_OK || R < 1 || R > 16 || s->group < 16) return false;
-  if (s->d != 64 && s->d != 128 && s->d != 256) return false;
+  if (s->d != 64 && s->d != 96 && s->d != 128 && s->d != 256) return false;
   const int64_t BH = s->B * (int64_t)s->H;
   constexpr int64_t kResidentBlocks = 1024;
   const int64_t blocks16 = (s->T + 15) / 16;
@@ -196,8 +196,8 @@ bool attn_plan(const srftq_shape* s, int32_t R, AttnPlan* p) {
   return true;
 }
 
-const srftq::RunAttnFn kAttention[3] = {srftq::run_attention_d64, srftq::run_attention_d128,
-                                        srftq::run_attention_d256};
+const srftq::RunAttnFn kAttention[4] = {srftq::run_attention_d64, srftq::run_attention_d96,
+                                        srftq::run_attention_d128, srftq::run_attention_d256};
 
 // Rotation given as a matrix: the sizes of validate(); d in {64, 128, 256},
 // group in {8, 16, 32}; rot and variant are not used.  q_stride 0 (one
@@ -250,7 +250,7 @@ srftq_status srftq_decode_attention(const srftq_shape* s, int64_t t_cap, int32_t
   srftq_status st = validate(s);
   if (st != SRFTQ_OK) return st;
   if (R < 1 || R > 16) return SRFTQ_ERR_SHAPE;
-  if (s->group < 16 || (s->d != 64 && s->d != 128 && s->d != 256)) return SRFTQ_ERR_UNSUPPORTED;
+  if (s->group < 16) return SRFTQ_ERR_UNSUPPORTED;
   if ((st = validate_cache(s, t_cap)) != SRFTQ_OK) return st;
   if (t_cap < s->T) return SRFTQ_ERR_SHAPE;
   if (!(scale == scale) || scale > 3.0e38f || scale < -3.0e38f) return SRFTQ_ERR_SHAPE;
@@ -296,7 +296,7 @@ srftq_status srftq_decode_attention(const srftq_shape* s, int64_t t_cap, int32_t
   a.uexp = (float*)((char*)workspace + plan.off_exp);
   a.ws_ml = (float*)((char*)workspace + plan.off_ml);
   a.ws_acc = (float*)((char*)workspace + plan.off_acc);
-  const int di = s->d == 64 ? 0 : s->d == 128 ? 1 : 2;
+  const int di = s->d == 64 ? 0 : s->d == 96 ? 1 : s->d == 128 ? 2 : 3;
   return from_hip(kAttention[di](a, (hipStream_t)stream));
 }
 

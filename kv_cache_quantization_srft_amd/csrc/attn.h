@@ -67,8 +67,10 @@ struct AttnTile {
   static constexpr int KC_INST = (CT + 1023) / 1024;   // K codes: 16 B per lane
   static constexpr int KC_BYTES = 1024 * KC_INST;
   static constexpr int VC_INST = CT / 256;             // V codes: 4 B per lane, transposed
-  static constexpr int SE = SRB >= 4 ? 4 : 2;          // scale rows: 4 B (2 B) per lane
-  // LDS-DMA fills a whole dword slot per lane: 2-byte rows sit 4 bytes apart
+  // scale rows move in 4-byte pieces when a row is a whole number of dwords,
+  // else in 2-byte pieces (d = 96, group 32: 6-byte rows)
+  static constexpr int SE = SRB % 4 == 0 ? 4 : 2;
+  // LDS-DMA fills a whole dword slot per lane: 2-byte pieces sit 4 bytes apart
   static constexpr int SSLOT = SE < 4 ? 4 : SE;
   static constexpr int S_INST = (ST + 64 * SE - 1) / (64 * SE);
   static constexpr int S_BYTES = 64 * SSLOT * S_INST;
@@ -140,27 +142,29 @@ __device__ __forceinline__ half4_t half4_of(uint32_t lo, uint32_t hi) {
 // fp16 value of a scale: half `hi` of a dword.
 __device__ __forceinline__ float f16_half(uint32_t w, int hi) { return hi ? hhi(w) : hlo(w); }
 
-// Scale sigma of group g of row `row` in an LDS scale tile (rows of SRB
-// bytes; 2-byte rows sit in 4-byte slots).
+// Scale sigma of group g of row `row` in an LDS scale tile: rows of SRB
+// bytes back to back when SRB is a multiple of 4, else moved in 2-byte
+// pieces that sit in 4-byte slots (scale (row, g) is piece row SRB/2 + g).
 template <int SRB>
 __device__ __forceinline__ float tile_scale(uint32_t tile, int row, int g) {
-  if constexpr (SRB >= 4) {
+  if constexpr (SRB % 4 == 0) {
     const uint32_t w = lds_u32(tile + (uint32_t)(row * SRB + 4 * (g >> 1)));
     return f16_half(w, g & 1);
   } else {
-    return hlo(lds_u16(tile + (uint32_t)(row * 4)));
+    return hlo(lds_u16(tile + (uint32_t)(2 * row * SRB + 4 * g)));
   }
 }
 
 // The fp16 scales of group g of rows `row` and `row + 1`, packed (low, high).
 template <int SRB>
 __device__ __forceinline__ uint32_t scale_pair(uint32_t tile, int row, int g) {
-  if constexpr (SRB >= 4) {
+  if constexpr (SRB % 4 == 0) {
     const uint32_t w0 = lds_u32(tile + (uint32_t)(row * SRB + 4 * (g >> 1)));
     const uint32_t w1 = lds_u32(tile + (uint32_t)((row + 1) * SRB + 4 * (g >> 1)));
     return __builtin_amdgcn_perm(w1, w0, (g & 1) ? 0x07060302u : 0x05040100u);
   } else {
-    return lds_u16(tile + (uint32_t)(row * 4)) | (lds_u16(tile + (uint32_t)((row + 1) * 4)) << 16);
+    return lds_u16(tile + (uint32_t)(2 * row * SRB + 4 * g)) |
+           (lds_u16(tile + (uint32_t)(2 * (row + 1) * SRB + 4 * g)) << 16);
   }
 }
 
@@ -189,6 +193,15 @@ template <int D>
 __device__ __forceinline__ const float* dft_twiddles() {
   static constexpr DftTwiddles<D> kTab{};
   return kTab.v;
+}
+
+// i mod D for 0 <= i < 2D
+template <int D>
+__device__ __forceinline__ int wrap(int i) {
+  if constexpr ((D & (D - 1)) == 0)
+    return i & (D - 1);
+  else
+    return i >= D ? i - D : i;
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -332,7 +345,7 @@ __global__ __launch_bounds__(64) void attn_qprep_kernel(const uint16_t* __restri
             const float2 w = *(const float2*)&tw[2 * idx];
             re[e] = __builtin_fmaf(xe[e], w.x, re[e]);
             im[e] = __builtin_fmaf(xe[e], w.y, im[e]);
-            idx = (idx + k) & (D - 1);
+            idx = wrap<D>(idx + k);
           });
         }
       }
@@ -661,7 +674,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
                                                            const float* __restrict__ lam_v,
                                                            float* __restrict__ out, AttnGeo a) {
   using Sc = Scales<D, ROT, VAR_REAL>;
-  constexpr int PER = D / 64;
+  constexpr int PER = (D + 63) / 64;   // coordinates lane + 64 k per lane (d = 96: the second for lanes < 32)
   __shared__ __attribute__((aligned(16))) float part[4][D];
   __shared__ __attribute__((aligned(16))) float tw[ROT == ROT_SRFT ? 2 * D : 4];
   __shared__ float red[2][4];
@@ -709,12 +722,12 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
     const float* src = ws_acc + s * D + lane;
     static_for<PER>([&](auto kk) {
       constexpr int k = decltype(kk)::value;
-      w[k] += f * src[64 * k];
+      if (D % 64 == 0 || lane + 64 * k < D) w[k] += f * src[64 * k];
     });
   }
   static_for<PER>([&](auto kk) {
     constexpr int k = decltype(kk)::value;
-    part[wave][lane + 64 * k] = w[k];
+    if (D % 64 == 0 || lane + 64 * k < D) part[wave][lane + 64 * k] = w[k];
   });
   __syncthreads();
   l = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
@@ -748,19 +761,19 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
         float2 w = *(const float2*)&tw[2 * idx];
         s0 = __builtin_fmaf(zr.x, w.x, s0);
         s0 = __builtin_fmaf(zi.x, w.y, s0);
-        idx = (idx + m) & (D - 1);
+        idx = wrap<D>(idx + m);
         w = *(const float2*)&tw[2 * idx];
         s1 = __builtin_fmaf(zr.y, w.x, s1);
         s1 = __builtin_fmaf(zi.y, w.y, s1);
-        idx = (idx + m) & (D - 1);
+        idx = wrap<D>(idx + m);
         w = *(const float2*)&tw[2 * idx];
         s2 = __builtin_fmaf(zr.z, w.x, s2);
         s2 = __builtin_fmaf(zi.z, w.y, s2);
-        idx = (idx + m) & (D - 1);
+        idx = wrap<D>(idx + m);
         w = *(const float2*)&tw[2 * idx];
         s3 = __builtin_fmaf(zr.w, w.x, s3);
         s3 = __builtin_fmaf(zi.w, w.y, s3);
-        idx = (idx + m) & (D - 1);
+        idx = wrap<D>(idx + m);
       }
       // the k = 0 term above is z_0 (its sine is 0)
       float xm = ((s0 + s1) + (s2 + s3)) + ((m & 1) ? -z[N] : z[N]);

@@ -89,6 +89,7 @@ struct AttnArgs {
 };
 using RunAttnFn = hipError_t (*)(const AttnArgs&, hipStream_t);
 hipError_t run_attention_d64(const AttnArgs&, hipStream_t);
+hipError_t run_attention_d96(const AttnArgs&, hipStream_t);
 hipError_t run_attention_d128(const AttnArgs&, hipStream_t);
 hipError_t run_attention_d256(const AttnArgs&, hipStream_t);
 

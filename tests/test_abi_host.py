@@ -165,7 +165,9 @@ def test_attention_workspace_and_argument_errors():
     assert call(R=0) == S.SRFTQ_ERR_SHAPE
     assert call(R=17) == S.SRFTQ_ERR_SHAPE
     assert call(shape=S.make_shape(2, 1000, 2, 128, 8, 4)) == S.SRFTQ_ERR_UNSUPPORTED
-    assert call(shape=S.make_shape(2, 1000, 2, 96, 16, 4)) == S.SRFTQ_ERR_UNSUPPORTED
+    # d = 96 is supported with the SRFT; the Walsh-Hadamard rotation needs a power of two
+    assert S.srftq_attention_workspace_bytes(S.make_shape(2, 1000, 2, 96, 32, 4), 6) > 0
+    assert call(shape=S.make_shape(2, 1000, 2, 96, 16, 4, rot="srht")) == S.SRFTQ_ERR_UNSUPPORTED
     assert call(t_cap=999) == S.SRFTQ_ERR_SHAPE
     assert call(scale=float("nan")) == S.SRFTQ_ERR_SHAPE
     assert call(scale=float("inf")) == S.SRFTQ_ERR_SHAPE

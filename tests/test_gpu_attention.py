@@ -117,6 +117,27 @@ def test_attention_matrix(d, g, bits, rot):
     print(check(c, run_gpu(c, lengths), lengths))
 
 
+@pytest.mark.parametrize("g,bits", [(16, 4), (32, 4), (16, 8), (32, 8)])
+@pytest.mark.parametrize("rot", ["srft", "none"])
+def test_attention_d96(g, bits, rot):
+    """d = 96 (the SRFT with its radix-3 step): the direct-DFT query rotation
+    and unrotation at a head size that is not a power of two, and 6-byte
+    scale rows at group 32; four chunks, ragged lengths."""
+    lam = bits == 4 and rot == "srft"
+    c = make_case(7050 + g + bits, 2, 1100, 2, 6, 96, g, bits, rot, lam=lam)
+    lengths = np.array([1100, 681], dtype=np.int32)
+    print(f"[attention d=96 g={g} b={bits} {rot} lam={lam}]", flush=True)
+    print(check(c, run_gpu(c, lengths), lengths))
+
+
+def test_attention_d96_lengths():
+    """Odd token counts in the last block (2-byte scale pieces, clamped to the
+    last valid row), zero and one token, lengths past T."""
+    c = make_case(7060, 8, 80, 1, 4, 96, 32, 4, "srft", cap=96)
+    lengths = np.array([0, 1, 15, 16, 17, 63, 80, 500], dtype=np.int32)
+    print(check(c, run_gpu(c, lengths), lengths))
+
+
 def test_attention_lengths():
     """Zero, one, and block-boundary lengths, lengths past T (clamped), and a
     cache with spare rows past T holding junk."""
