@@ -278,15 +278,39 @@ def decode_attention(q16, k_codes, k_scales, v_codes, v_scales, T=None, lengths=
     scale = 1/sqrt(d) by default.  A tensor with no tokens gives zeros.
     q16: fp16 [B, H*R, d]; caches [B, H, t_cap, .]."""
     q = f16_to_f64(_bits(np.asarray(q16)))
-    B, HR, d = q.shape
-    H, t_cap = k_codes.shape[1], k_codes.shape[2]
-    R = HR // H
-    T = t_cap if T is None else int(T)
-    scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    d = q.shape[2]
+    T = k_codes.shape[2] if T is None else int(T)
     _, k = dequantize(k_codes[:, :, :T], k_scales[:, :, :T], signs_k, lam_k, group, bits, rot, d=d,
                       return_f64=True)
     _, v = dequantize(v_codes[:, :, :T], v_scales[:, :, :T], signs_v, lam_v, group, bits, rot, d=d,
                       return_f64=True)                                    # [B, T, H, d]
+    return _attend(q, k, v, T, lengths, scale)
+
+
+def decode_attention_dense(q16, k_codes, k_scales, v_codes, v_scales, Qk, Qv, T=None, lengths=None,
+                           signs_k=None, lam_k=None, signs_v=None, lam_v=None, group=16, bits=4,
+                           scale=None):
+    """decode_attention over caches written with a rotation given as a matrix
+    (a learned or Householder rotation, "When Quantization Is Free",
+    Metodologia 3): k^ and v^ are the fp64 reconstructions of
+    ``dequantize_dense`` with Qk and Qv ([d, d] or [B, H, d, d])."""
+    q = f16_to_f64(_bits(np.asarray(q16)))
+    d = q.shape[2]
+    T = k_codes.shape[2] if T is None else int(T)
+    _, k = dequantize_dense(k_codes[:, :, :T], k_scales[:, :, :T], Qk, signs_k, lam_k, group, bits, d=d,
+                            return_f64=True)
+    _, v = dequantize_dense(v_codes[:, :, :T], v_scales[:, :, :T], Qv, signs_v, lam_v, group, bits, d=d,
+                            return_f64=True)                              # [B, T, H, d]
+    return _attend(q, k, v, T, lengths, scale)
+
+
+def _attend(q, k, v, T, lengths, scale):
+    """softmax(scale q . k) v per tensor b and query head r over the first
+    L_b = clamp(lengths[b], 0, T) tokens of KV head r // R; zeros when L_b = 0."""
+    B, HR, d = q.shape
+    H = k.shape[2]
+    R = HR // H
+    scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
     out = np.zeros((B, HR, d), dtype=np.float64)
     for b in range(B):
         L = T if lengths is None else min(max(int(lengths[b]), 0), T)

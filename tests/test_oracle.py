@@ -681,3 +681,79 @@ def test_dense_roundtrip_error_identity_and_bound():
     assert np.allclose(e_x, e_y, rtol=1e-5, atol=1e-5)
     bound = np.sqrt(np.sum((sig / (2 * lam[:, None])) ** 2, axis=-1))
     assert np.all(e_x <= bound * (1 + 1e-4) + 1e-5)
+
+
+# --------------------------------------------------------------------------
+# Decode attention over caches written with a rotation matrix.
+# --------------------------------------------------------------------------
+
+def _attn_case_dense(seed, B, T, H, R, d, g, bits, Q, lam=True):
+    rng = np.random.default_rng(seed)
+    k = _rand_x(rng, (B, T, H, d))
+    v = _rand_x(rng, (B, T, H, d), 2.0)
+    sk, sv = _rand_signs(rng, B, H, d), _rand_signs(rng, B, H, d)
+    lk = rng.uniform(0.5, 2.0, size=(B, H, d)).astype(np.float32) if lam else None
+    lv = rng.uniform(0.5, 2.0, size=(B, H, d)).astype(np.float32) if lam else None
+    kc, ks = oracle.quantize_dense(k, Q, sk, lk, g, bits)
+    vc, vs = oracle.quantize_dense(v, Q, sv, lv, g, bits)
+    q = _rand_x(rng, (B, H * R, d))
+    return q, (kc, ks, sk, lk), (vc, vs, sv, lv)
+
+
+@pytest.mark.parametrize("which", ["srft", "none"])
+def test_attention_dense_reduces_to_the_transforms(which):
+    """With Q the packed SRFT matrix (or the identity) the caches, and so the
+    attention, are those of rot = srft (none): the dense path adds nothing
+    but the matrix."""
+    B, T, H, R, d, g, bits = 2, 29, 2, 3, 64, 16, 4
+    Q = (_srft_matrix(d) if which == "srft" else np.eye(d)).astype(np.float32)
+    q, K, V = _attn_case(64, B, T, H, R, d, g, bits, which)
+    lengths = np.array([29, 11], dtype=np.int32)
+    ref = _attn(q, K, V, g, bits, which, lengths=lengths)
+    got = oracle.decode_attention_dense(q, K[0], K[1], V[0], V[1], Q, Q, lengths=lengths, signs_k=K[2],
+                                        lam_k=K[3], signs_v=V[2], lam_v=V[3], group=g, bits=bits)
+    # the SRFT matrix is the FFT's output rounded to fp32 (2^-24 relative per entry)
+    tol = 1e-6 if which == "srft" else 1e-13
+    assert np.allclose(got, ref, rtol=tol, atol=tol)
+
+
+def test_attention_dense_matches_torch_sdpa():
+    """Per-head Householder rotations for K and different ones for V, against
+    torch's scaled_dot_product_attention (fp64, CPU) on the dense
+    reconstructions, grouped query heads and a length mask."""
+    import torch
+    B, T, H, R, d, g, bits = 2, 31, 2, 2, 64, 32, 8
+    rng = np.random.default_rng(65)
+    Qk = oracle.householder_matrix(rng.standard_normal((B, H, d // 2, d))).astype(np.float32)
+    Qv = oracle.householder_matrix(rng.standard_normal((B, H, d // 2, d))).astype(np.float32)
+    q, K, _ = _attn_case_dense(66, B, T, H, R, d, g, bits, Qk)
+    _, _, V = _attn_case_dense(67, B, T, H, R, d, g, bits, Qv)
+    lengths = np.array([31, 7], dtype=np.int32)
+    got = oracle.decode_attention_dense(q, K[0], K[1], V[0], V[1], Qk, Qv, lengths=lengths, signs_k=K[2],
+                                        lam_k=K[3], signs_v=V[2], lam_v=V[3], group=g, bits=bits)
+    _, kh = oracle.dequantize_dense(K[0], K[1], Qk, K[2], K[3], g, bits, d=d, return_f64=True)
+    _, vh = oracle.dequantize_dense(V[0], V[1], Qv, V[2], V[3], g, bits, d=d, return_f64=True)
+    kt = torch.from_numpy(kh).permute(0, 2, 1, 3).repeat_interleave(R, dim=1)
+    vt = torch.from_numpy(vh).permute(0, 2, 1, 3).repeat_interleave(R, dim=1)
+    qt = torch.from_numpy(q.astype(np.float64))[:, :, None]
+    mask = torch.from_numpy(np.arange(T)[None, :] < lengths[:, None])[:, None, None]
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask)[:, :, 0]
+    assert np.allclose(got, ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_attention_dense_scores_in_the_rotated_domain():
+    """q . k^ = (Q (s_k . q)) . y^ for an orthonormal Q: the identity that lets
+    the GPU score the codes directly under a Householder rotation."""
+    from oracle.compare import decode_codes
+    B, T, H, R, d, g, bits = 1, 9, 1, 1, 128, 16, 4
+    rng = np.random.default_rng(68)
+    Q = oracle.householder_matrix(rng.standard_normal((d // 2, d))).astype(np.float32)
+    q, K, _ = _attn_case_dense(69, B, T, H, R, d, g, bits, Q)
+    _, kh = oracle.dequantize_dense(K[0], K[1], Q, K[2], K[3], g, bits, d=d, return_f64=True)
+    direct = kh[0, :, 0] @ q[0, 0].astype(np.float64)
+    xs = q[0, 0].astype(np.float64) * K[2][0, 0]
+    u = Q.astype(np.float64) @ xs
+    c = decode_codes(K[0], bits, d)[0, 0].astype(np.float64)
+    sig = np.repeat(K[1].view(np.float16).astype(np.float64)[0, 0], g, axis=-1)
+    yh = c * sig / K[3][0, 0].astype(np.float64)
+    assert np.allclose(yh @ u, direct, rtol=1e-12, atol=1e-12)
