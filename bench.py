@@ -376,6 +376,33 @@ def householder_timing(steps: int) -> dict:
         tq += ev[0].elapsed_time(ev[1])
         tdq += ev[1].elapsed_time(ev[2])
     rel = (torch.linalg.vector_norm(xhat.float() - xd.float()) / torch.linalg.vector_norm(xd.float())).item()
+    del xhat
+    # decode attention over these caches read as 26 layers' K (even tensors)
+    # and V (odd tensors), each with its own matrix, 8 query heads per KV head
+    R = 8
+    L = w.B // 2
+    kc, vc = codes[0::2].contiguous(), codes[1::2].contiguous()
+    ks, vs = scales[0::2].contiguous(), scales[1::2].contiguous()
+    sk, sv = sd[0::2].contiguous(), sd[1::2].contiguous()
+    Qk, Qv = Q[0::2].contiguous(), Q[1::2].contiguous()
+    qa = torch.from_numpy(W.attention_queries(w, R)).to(dev)
+    ws = torch.empty((S.srftq_attention_workspace_bytes(S.make_shape(L, w.T, w.H, w.d, w.group, w.bits), R),),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty((L, w.H * R, w.d), dtype=torch.float32, device=dev)
+    attend = lambda: S.decode_attention_dense(qa, kc, ks, vc, vs, Qk, Qv, sk, None, sv, None, group=w.group,
+                                              bits=w.bits, workspace=ws, out=out)
+    for _ in range(10):
+        attend()
+    torch.cuda.synchronize()
+    ta = 0.0
+    for _ in range(steps):
+        ev[0].record()
+        attend()
+        ev[1].record()
+        torch.cuda.synchronize()
+        ta += ev[0].elapsed_time(ev[1])
+    attn_ms = ta / steps
+    attn_bytes = 2 * L * w.H * w.T * (w.d * w.bits // 8 + 2 * (w.d // w.group))
     n = w.nvec
     q_ms, dq_ms = tq / steps, tdq / steps
     flops = 2.0 * w.d * w.d * n
@@ -393,7 +420,12 @@ def householder_timing(steps: int) -> dict:
             "executed_fp16_passes": {"quantize": 2, "dequantize": 3},
             "quantize_hbm_frac": bpv * n / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
             "dequantize_hbm_frac": bpv * n / (dq_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-            "reconstruction_rel_l2": rel}
+            "reconstruction_rel_l2": rel,
+            "decode_attention": {"step": f"srftq_decode_attention_dense: {L} layers x K+V caches, {R} query "
+                                         "heads per KV head, one query token, each cache with its own matrix",
+                                 "ms": attn_ms, "algorithmic_bytes": attn_bytes,
+                                 "GBps": attn_bytes / (attn_ms * 1e-3) / 1e9,
+                                 "hbm_frac": attn_bytes / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}}
 
 
 def main():

@@ -285,6 +285,27 @@ srftq_status srftq_dequantize_dense(const srftq_shape* shape, const float* Q, in
                                     const int8_t* signs, const float* lambda, uint16_t* x_out,
                                     void* stream);
 
+/*
+ * srftq_decode_attention_dense: srftq_decode_attention over K and V caches
+ * written by srftq_quantize_dense (a learned or Householder rotation,
+ * Metodologia 3): k^ = s_k . (Qk^T yhat_k), v^ = s_v . (Qv^T yhat_v).  The
+ * scores are taken against Qk (s_k . q) and the output is unrotated by Qv^T
+ * once per query head; the scoring kernel is the same as for the transforms.
+ *   Qk, Qv     fp32 row-major d x d matrices (16-B aligned; may be the same),
+ *              head h of tensor b at Q + (b*H + h) * q_stride
+ *   q_stride   as for srftq_quantize_dense
+ * Every other argument, the workspace (srftq_attention_workspace_bytes of
+ * the same shape) and the errors as for srftq_decode_attention; the sizes of
+ * srftq_quantize_dense with group >= 16; shape.rot and shape.variant are
+ * ignored.  The query rotation and the unrotation run in fp32.
+ */
+srftq_status srftq_decode_attention_dense(const srftq_shape* shape, int64_t t_cap, int32_t q_per_kv,
+                                          const float* Qk, const float* Qv, int64_t q_stride,
+                                          const uint16_t* q, const srftq_cache_view* k,
+                                          const srftq_cache_view* v, const int32_t* lengths,
+                                          float scale, float* out, void* workspace,
+                                          size_t workspace_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* srftq_status_string(srftq_status status);
 

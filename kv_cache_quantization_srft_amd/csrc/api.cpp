@@ -184,7 +184,7 @@ bool attn_plan(const srftq_shape* s, int32_t R, AttnPlan* p) {
   int64_t nc = BH > 0 ? kResidentBlocks / BH : 1;
   if (nc > blocks16 / 16) nc = blocks16 / 16;
   if (nc < 1) nc = 1;
-  if (BH * nc > 0x7fffffffLL || BH * R > 0x7fffffffLL) return false;
+  if (BH * nc > 0x7fffffffLL || BH * R > 0x7ffffff0LL) return false;   // grids of up to BH * R + 7 blocks
   p->n_chunks = (int)nc;
   const size_t uq = (size_t)BH * R * s->d * 4;
   const size_t ml = (size_t)BH * nc * R * 2 * 4;
@@ -232,6 +232,71 @@ srftq_status run_dense(srftq::DenseArgs& a, const srftq_shape* s, const int8_t* 
   return from_hip(kDense[di](a, (hipStream_t)stream));
 }
 
+// The kernels read a sign row for every head: the shared +1 row where the
+// caller passes none (a device lookup, so after every argument check).
+srftq_status set_plus_ones(srftq::AttnArgs& a) {
+  if (a.signs_k && a.signs_v) return SRFTQ_OK;
+  const int8_t* ones = srftq::plus_ones_ptr();
+  if (!ones) return SRFTQ_ERR_HIP;
+  if (!a.signs_k) a.signs_k = ones;
+  if (!a.signs_v) a.signs_v = ones;
+  return SRFTQ_OK;
+}
+
+// Checks and launch arguments shared by the decode-attention entry points
+// (the shape already validated); `empty` when there is nothing to launch.
+srftq_status attention_args(const srftq_shape* s, int64_t t_cap, int32_t R, const uint16_t* q,
+                            const srftq_cache_view* k, const srftq_cache_view* v, const int32_t* lengths,
+                            float scale, float* out, void* workspace, size_t workspace_bytes,
+                            srftq::AttnArgs& a, bool& empty) {
+  srftq_status st;
+  if (R < 1 || R > 16) return SRFTQ_ERR_SHAPE;
+  if (s->group < 16) return SRFTQ_ERR_UNSUPPORTED;
+  if ((st = validate_cache(s, t_cap)) != SRFTQ_OK) return st;
+  if (t_cap < s->T) return SRFTQ_ERR_SHAPE;
+  if (!(scale == scale) || scale > 3.0e38f || scale < -3.0e38f) return SRFTQ_ERR_SHAPE;
+  AttnPlan plan;
+  if (!attn_plan(s, R, &plan)) return SRFTQ_ERR_SHAPE;
+  empty = s->B * (int64_t)s->H == 0;
+  if (empty) return SRFTQ_OK;
+  if (!q || !k || !v || !out || !workspace) return SRFTQ_ERR_NULL;
+  if (!k->codes || !k->scales || !v->codes || !v->scales) return SRFTQ_ERR_NULL;
+  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace) || !aligned16(k->codes) ||
+      !aligned16(k->scales) || !aligned16(v->codes) || !aligned16(v->scales))
+    return SRFTQ_ERR_ALIGN;
+  if (lengths && !aligned4(lengths)) return SRFTQ_ERR_ALIGN;
+  if ((st = check_side(k->signs, k->lambda)) != SRFTQ_OK) return st;
+  if ((st = check_side(v->signs, v->lambda)) != SRFTQ_OK) return st;
+  if (workspace_bytes < plan.bytes) return SRFTQ_ERR_SHAPE;
+  a.geo.T = s->T;
+  a.geo.pitch = t_cap;
+  a.geo.H = s->H;
+  a.geo.R = R;
+  a.geo.BH = (int32_t)(s->B * s->H);
+  a.geo.n_chunks = plan.n_chunks;
+  a.geo.sign_stride_k = k->signs ? s->d : 0;
+  a.geo.sign_stride_v = v->signs ? s->d : 0;
+  a.geo.scale_log2e = (float)((double)scale * 1.4426950408889634);
+  a.group = s->group;
+  a.bits = s->bits;
+  a.q = q;
+  a.codes_k = k->codes;
+  a.scales_k = k->scales;
+  a.signs_k = k->signs;   // NULL: the shared +1 row, set by set_plus_ones
+  a.lam_k = k->lambda;
+  a.codes_v = v->codes;
+  a.scales_v = v->scales;
+  a.signs_v = v->signs;
+  a.lam_v = v->lambda;
+  a.lengths = lengths;
+  a.out = out;
+  a.uq = (float*)workspace;
+  a.uexp = (float*)((char*)workspace + plan.off_exp);
+  a.ws_ml = (float*)((char*)workspace + plan.off_ml);
+  a.ws_acc = (float*)((char*)workspace + plan.off_acc);
+  return SRFTQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -249,54 +314,40 @@ srftq_status srftq_decode_attention(const srftq_shape* s, int64_t t_cap, int32_t
                                     size_t workspace_bytes, void* stream) {
   srftq_status st = validate(s);
   if (st != SRFTQ_OK) return st;
-  if (R < 1 || R > 16) return SRFTQ_ERR_SHAPE;
-  if (s->group < 16) return SRFTQ_ERR_UNSUPPORTED;
-  if ((st = validate_cache(s, t_cap)) != SRFTQ_OK) return st;
-  if (t_cap < s->T) return SRFTQ_ERR_SHAPE;
-  if (!(scale == scale) || scale > 3.0e38f || scale < -3.0e38f) return SRFTQ_ERR_SHAPE;
-  AttnPlan plan;
-  if (!attn_plan(s, R, &plan)) return SRFTQ_ERR_SHAPE;
-  if (s->B * (int64_t)s->H == 0) return SRFTQ_OK;
-  if (!q || !k || !v || !out || !workspace) return SRFTQ_ERR_NULL;
-  if (!k->codes || !k->scales || !v->codes || !v->scales) return SRFTQ_ERR_NULL;
-  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace) || !aligned16(k->codes) ||
-      !aligned16(k->scales) || !aligned16(v->codes) || !aligned16(v->scales))
-    return SRFTQ_ERR_ALIGN;
-  if (lengths && !aligned4(lengths)) return SRFTQ_ERR_ALIGN;
-  if ((st = check_side(k->signs, k->lambda)) != SRFTQ_OK) return st;
-  if ((st = check_side(v->signs, v->lambda)) != SRFTQ_OK) return st;
-  if (workspace_bytes < plan.bytes) return SRFTQ_ERR_SHAPE;
-  const int8_t* ones = srftq::plus_ones_ptr();
-  if (!ones) return SRFTQ_ERR_HIP;
   srftq::AttnArgs a = {};
-  a.geo.T = s->T;
-  a.geo.pitch = t_cap;
-  a.geo.H = s->H;
-  a.geo.R = R;
-  a.geo.BH = (int32_t)(s->B * s->H);
-  a.geo.n_chunks = plan.n_chunks;
-  a.geo.sign_stride_k = k->signs ? s->d : 0;
-  a.geo.sign_stride_v = v->signs ? s->d : 0;
-  a.geo.scale_log2e = (float)((double)scale * 1.4426950408889634);
+  bool empty = false;
+  if ((st = attention_args(s, t_cap, R, q, k, v, lengths, scale, out, workspace, workspace_bytes, a,
+                           empty)) != SRFTQ_OK || empty)
+    return st;
   a.rot = s->rot;
-  a.group = s->group;
-  a.bits = s->bits;
-  a.q = q;
-  a.codes_k = k->codes;
-  a.scales_k = k->scales;
-  a.signs_k = k->signs ? k->signs : ones;
-  a.lam_k = k->lambda;
-  a.codes_v = v->codes;
-  a.scales_v = v->scales;
-  a.signs_v = v->signs ? v->signs : ones;
-  a.lam_v = v->lambda;
-  a.lengths = lengths;
-  a.out = out;
-  a.uq = (float*)workspace;
-  a.uexp = (float*)((char*)workspace + plan.off_exp);
-  a.ws_ml = (float*)((char*)workspace + plan.off_ml);
-  a.ws_acc = (float*)((char*)workspace + plan.off_acc);
+  if ((st = set_plus_ones(a)) != SRFTQ_OK) return st;
   const int di = s->d == 64 ? 0 : s->d == 96 ? 1 : s->d == 128 ? 2 : 3;
+  return from_hip(kAttention[di](a, (hipStream_t)stream));
+}
+
+srftq_status srftq_decode_attention_dense(const srftq_shape* s, int64_t t_cap, int32_t R, const float* Qk,
+                                          const float* Qv, int64_t q_stride, const uint16_t* q,
+                                          const srftq_cache_view* k, const srftq_cache_view* v,
+                                          const int32_t* lengths, float scale, float* out, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  srftq_status st = validate_dense(s, q_stride);
+  if (st != SRFTQ_OK) return st;
+  srftq_shape t = *s;   // rot and variant are not used
+  t.rot = SRFTQ_ROT_NONE;
+  t.variant = 0;
+  srftq::AttnArgs a = {};
+  bool empty = false;
+  if ((st = attention_args(&t, t_cap, R, q, k, v, lengths, scale, out, workspace, workspace_bytes, a,
+                           empty)) != SRFTQ_OK || empty)
+    return st;
+  if (!Qk || !Qv) return SRFTQ_ERR_NULL;
+  if (!aligned16(Qk) || !aligned16(Qv)) return SRFTQ_ERR_ALIGN;
+  a.dense = true;
+  a.Qk = Qk;
+  a.Qv = Qv;
+  a.q_stride = q_stride;
+  if ((st = set_plus_ones(a)) != SRFTQ_OK) return st;
+  const int di = s->d == 64 ? 0 : s->d == 128 ? 2 : 3;
   return from_hip(kAttention[di](a, (hipStream_t)stream));
 }
 

@@ -51,6 +51,11 @@
 
 namespace srftq {
 
+// A rotation given as a matrix (learned or Householder, row-major fp32
+// [d, d] per (tensor, KV head)): the query rotation and the unrotation are
+// dense products; the scoring kernel is the same for every rotation.
+enum : int { ROT_DENSE = 3 };
+
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -195,6 +200,30 @@ __device__ __forceinline__ const float* dft_twiddles() {
   return kTab.v;
 }
 
+// Query head of this block for the per-query-head kernels, launched on
+// xcd_grid(n) blocks: the chip deals consecutive blocks to its 8 XCDs in
+// turn, so block i takes head (i mod 8) ceil(n / 8) + i / 8 and each XCD
+// (its own L2) gets a contiguous range of heads -- the R heads of a KV head
+// read that head's matrix through one L2 instead of eight.  -1: no head.
+__device__ __forceinline__ int64_t xcd_head(int64_t n) {
+  const int64_t per = (n + 7) / 8;
+  const int64_t v = (int64_t)(blockIdx.x % 8u) * per + blockIdx.x / 8u;
+  return v < n ? v : -1;
+}
+inline unsigned xcd_grid(int64_t n) { return (unsigned)(8 * ((n + 7) / 8)); }
+
+// Orthonormal scale of rotated coordinate j: the transforms run unscaled,
+// a matrix is orthonormal as given.
+template <int D, int ROT>
+__device__ __forceinline__ float coord_scale(int j) {
+  if constexpr (ROT == ROT_DENSE) {
+    return 1.0f;
+  } else {
+    using Sc = Scales<D, ROT, VAR_REAL>;
+    return (float)(Sc::is_edge(j) ? Sc::kFwdEdge : Sc::kFwdBulk);
+  }
+}
+
 // i mod D for 0 <= i < 2D
 template <int D>
 __device__ __forceinline__ int wrap(int i) {
@@ -252,34 +281,44 @@ __device__ __forceinline__ void wave_fwht(float (&x)[WaveVec<D>::P], int lane) {
 }
 
 // ----------------------------------------------------------------------------
-// u = M (s_k . q) * scale * log2(e) / lambda_k for one query head per wave,
-// v = b*H*R + h*R + r (KV head bh = v / R).  SRFT: lane k accumulates the
-// DFT bin X_k = sum_m x_m exp(-2 pi i k m / d) from the LDS copy of x and the
-// twiddle table (two bins per lane at d = 256), and the bin X_{d/2} is the
-// alternating sum of x; the packed coordinates are Re X_0..Re X_{d/2},
-// Im X_1..Im X_{d/2-1} with the orthonormal scales.  SRHT: wave_fwht.
+// u = M (s_k . q) * scale * log2(e) / lambda_k for one query head per block
+// of four waves, v = b*H*R + h*R + r (KV head bh = v / R).  SRFT: lane k
+// accumulates the DFT bin X_k = sum_m x_m exp(-2 pi i k m / d) from the LDS
+// copy of x and the twiddle table (two bins per lane at d = 256), each wave
+// over a quarter of m, and the bin X_{d/2} is the alternating sum of x; the
+// packed coordinates are Re X_0..Re X_{d/2}, Im X_1..Im X_{d/2-1} with the
+// orthonormal scales.  Matrix: lane j forms rows j, j + 64, ... of Q with x,
+// each wave over a quarter of the columns.  Wave 0 adds the quarters and
+// finishes; SRHT and no rotation run on wave 0 alone (wave_fwht).
 // ----------------------------------------------------------------------------
 template <int D, int ROT>
-__global__ __launch_bounds__(64) void attn_qprep_kernel(const uint16_t* __restrict__ q,
-                                                        const int8_t* __restrict__ signs_k,
-                                                        const float* __restrict__ lam_k,
-                                                        float* __restrict__ uq,
-                                                        float* __restrict__ uexp, AttnGeo a) {
-  using Sc = Scales<D, ROT, VAR_REAL>;
+__global__ __launch_bounds__(256) void attn_qprep_kernel(const uint16_t* __restrict__ q,
+                                                         const int8_t* __restrict__ signs_k,
+                                                         const float* __restrict__ lam_k,
+                                                         const float* __restrict__ Qk, int64_t q_stride,
+                                                         float* __restrict__ uq,
+                                                         float* __restrict__ uexp, AttnGeo a) {
   constexpr int P = WaveVec<D>::P, NL = WaveVec<D>::NL;
   constexpr int N = D / 2;
   constexpr int KPL = N >= 64 ? N / 64 : 1;                   // SRFT bins per lane
-  constexpr int NO = ROT == ROT_SRFT ? 2 * KPL : P;            // outputs per lane
-  __shared__ __attribute__((aligned(16))) float xs[ROT == ROT_SRFT ? D : 4];
+  constexpr int NO = ROT == ROT_SRFT    ? 2 * KPL              // outputs per lane
+                   : ROT == ROT_DENSE ? (D + 63) / 64          // matrix rows lane + 64 o
+                                      : P;
+  constexpr int MQ = D / 4;                                    // sum terms per wave (SRFT, matrix)
+  constexpr bool kSplit = ROT == ROT_SRFT || ROT == ROT_DENSE;
+  __shared__ __attribute__((aligned(16))) float xs[kSplit ? D : 4];
   __shared__ __attribute__((aligned(16))) float tw[ROT == ROT_SRFT ? 2 * D : 4];
-  const int lane = threadIdx.x;
-  const int64_t v = blockIdx.x;
+  __shared__ __attribute__((aligned(16))) float red[kSplit ? 4 * NO * 64 : 4];   // [wave][o][lane]
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int64_t v = xcd_head((int64_t)a.BH * a.R);
+  if (v < 0) return;
   const int64_t bh = v / a.R;
 
-  // x = s_k (.) q, elements P lane .. P lane + P - 1
+  // wave 0: x = s_k (.) q, elements P lane .. P lane + P - 1
   float x[P];
   static_for<P>([&](auto tt) { x[decltype(tt)::value] = 0.0f; });
-  if (lane < NL) {
+  if (wave == 0 && lane < NL) {
     const uint16_t* src = q + v * D + P * lane;
     if constexpr (P == 2) {
       const uint32_t w = *(const uint32_t*)src;
@@ -298,71 +337,116 @@ __global__ __launch_bounds__(64) void attn_qprep_kernel(const uint16_t* __restri
     });
   }
 
-  float y[NO];
-  int jo[NO];   // coordinate of each output, -1 where the lane has none
+  int jo[NO];   // coordinate of each output of a wave-0 lane, -1 where it has none
   static_for<NO>([&](auto oo) {
     constexpr int o = decltype(oo)::value;
     if constexpr (ROT == ROT_SRFT) {
       const int k = lane + 64 * (o / 2);
       jo[o] = k >= N ? -1 : (o & 1) ? (k == 0 ? N : N + k) : k;
+    } else if constexpr (ROT == ROT_DENSE) {
+      jo[o] = lane + 64 * o < D ? lane + 64 * o : -1;
     } else {
       jo[o] = lane < NL ? P * lane + o : -1;
     }
   });
-  // 1 / lambda_k of the lane's outputs, loaded before the transform
+  // 1 / lambda_k of the outputs, loaded before the transform
   float rl[NO];
   static_for<NO>([&](auto oo) {
     constexpr int o = decltype(oo)::value;
-    rl[o] = (lam_k && jo[o] >= 0) ? __builtin_amdgcn_rcpf(lam_k[bh * D + jo[o]]) : 1.0f;
+    rl[o] = (wave == 0 && lam_k && jo[o] >= 0) ? __builtin_amdgcn_rcpf(lam_k[bh * D + jo[o]]) : 1.0f;
   });
-  if constexpr (ROT == ROT_SRFT) {
-    if (lane < NL) static_for<P>([&](auto tt) { xs[P * lane + decltype(tt)::value] = x[decltype(tt)::value]; });
-    const float* twg = dft_twiddles<D>();
-    static_for<(2 * D + 63) / 64>([&](auto ii) {
-      const int i = lane + 64 * decltype(ii)::value;
-      if (i < 2 * D) tw[i] = twg[i];
-    });
-    // X_{d/2} = sum_m (-1)^m x_m (P is even: element P l + t has the sign of t)
-    float alt = 0.0f;
-    static_for<P>([&](auto tt) {
-      constexpr int t = decltype(tt)::value;
-      alt += (t & 1) ? -x[t] : x[t];
-    });
-    alt = wave_sum(alt);
+
+  float y[NO];
+  static_for<NO>([&](auto oo) { y[decltype(oo)::value] = 0.0f; });
+  if constexpr (kSplit) {
+    // the four waves split the sum over m into quarters; wave 0 adds them up
+    if (wave == 0 && lane < NL) static_for<P>([&](auto tt) { xs[P * lane + decltype(tt)::value] = x[decltype(tt)::value]; });
+    if constexpr (ROT == ROT_SRFT) {
+      const float* twg = dft_twiddles<D>();
+      for (int i = (int)threadIdx.x; i < 2 * D; i += 256) tw[i] = twg[i];
+    }
     __syncthreads();
-    static_for<KPL>([&](auto kk) {
-      constexpr int i = decltype(kk)::value;
-      const int k = lane + 64 * i;
-      float re[4] = {0.f, 0.f, 0.f, 0.f}, im[4] = {0.f, 0.f, 0.f, 0.f};
-      if (k < N) {
-        int idx = 0;   // k m mod d
+    const int m0 = wave * MQ;
+    float part[NO];
+    if constexpr (ROT == ROT_SRFT) {
+      static_for<KPL>([&](auto kk) {
+        constexpr int i = decltype(kk)::value;
+        const int k = lane + 64 * i;
+        float re[4] = {0.f, 0.f, 0.f, 0.f}, im[4] = {0.f, 0.f, 0.f, 0.f};
+        if (k < N) {
+          int idx = (k * m0) % D;   // k m mod d
 #pragma unroll 4
-        for (int m = 0; m < D; m += 4) {
-          const float4 xv = *(const float4*)&xs[m];
-          const float xe[4] = {xv.x, xv.y, xv.z, xv.w};
-          static_for<4>([&](auto ee) {
-            constexpr int e = decltype(ee)::value;
-            const float2 w = *(const float2*)&tw[2 * idx];
-            re[e] = __builtin_fmaf(xe[e], w.x, re[e]);
-            im[e] = __builtin_fmaf(xe[e], w.y, im[e]);
-            idx = wrap<D>(idx + k);
+          for (int m = m0; m < m0 + MQ; m += 4) {
+            const float4 xv = *(const float4*)&xs[m];
+            const float xe[4] = {xv.x, xv.y, xv.z, xv.w};
+            static_for<4>([&](auto ee) {
+              constexpr int e = decltype(ee)::value;
+              const float2 w = *(const float2*)&tw[2 * idx];
+              re[e] = __builtin_fmaf(xe[e], w.x, re[e]);
+              im[e] = __builtin_fmaf(xe[e], w.y, im[e]);
+              idx = wrap<D>(idx + k);
+            });
+          }
+        }
+        part[2 * i] = (re[0] + re[1]) + (re[2] + re[3]);
+        part[2 * i + 1] = (im[0] + im[1]) + (im[2] + im[3]);
+      });
+    } else {
+      // u_j = sum_m Q[j][m] x_m, rows j = lane + 64 o of this head's matrix
+      const float* Qh = Qk + bh * q_stride;
+      static_for<NO>([&](auto oo) {
+        constexpr int o = decltype(oo)::value;
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        if (jo[o] >= 0) {
+          const float4* row = (const float4*)(Qh + (int64_t)jo[o] * D + m0);
+          float4 w[MQ / 4];
+          static_for<MQ / 4>([&](auto mm) { w[decltype(mm)::value] = row[decltype(mm)::value]; });
+          static_for<MQ / 4>([&](auto mm) {
+            constexpr int m = decltype(mm)::value;
+            const float4 xv = *(const float4*)&xs[m0 + 4 * m];
+            acc[0] = __builtin_fmaf(w[m].x, xv.x, acc[0]);
+            acc[1] = __builtin_fmaf(w[m].y, xv.y, acc[1]);
+            acc[2] = __builtin_fmaf(w[m].z, xv.z, acc[2]);
+            acc[3] = __builtin_fmaf(w[m].w, xv.w, acc[3]);
           });
         }
-      }
-      y[2 * i] = (re[0] + re[1]) + (re[2] + re[3]);
-      y[2 * i + 1] = k == 0 ? alt : (im[0] + im[1]) + (im[2] + im[3]);
+        part[o] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+      });
+    }
+    static_for<NO>([&](auto oo) {
+      constexpr int o = decltype(oo)::value;
+      red[(wave * NO + o) * 64 + lane] = part[o];
     });
+    __syncthreads();
+    if (wave != 0) return;
+    static_for<NO>([&](auto oo) {
+      constexpr int o = decltype(oo)::value;
+      y[o] = (red[o * 64 + lane] + red[(NO + o) * 64 + lane]) +
+             (red[(2 * NO + o) * 64 + lane] + red[(3 * NO + o) * 64 + lane]);
+    });
+    if constexpr (ROT == ROT_SRFT) {
+      // X_{d/2} = sum_m (-1)^m x_m (P is even: element P l + t has the sign of t)
+      float alt = 0.0f;
+      static_for<P>([&](auto tt) {
+        constexpr int t = decltype(tt)::value;
+        alt += (t & 1) ? -x[t] : x[t];
+      });
+      alt = wave_sum(alt);
+      if (lane == 0) y[1] = alt;   // bin 0 has no imaginary part: its slot holds X_{d/2}
+    }
   } else {
+    if (wave != 0) return;
     if constexpr (ROT == ROT_SRHT) wave_fwht<D>(x, lane);
     static_for<P>([&](auto tt) { y[decltype(tt)::value] = x[decltype(tt)::value]; });
   }
 
+  // wave 0: scales, the power-of-two normalization, the stores
   float mx = 0.0f;
   static_for<NO>([&](auto oo) {
     constexpr int o = decltype(oo)::value;
     const int j = jo[o];
     if (j >= 0) {
-      float u = y[o] * (float)(Sc::is_edge(j) ? Sc::kFwdEdge : Sc::kFwdBulk) * a.scale_log2e;
+      float u = y[o] * coord_scale<D, ROT>(j) * a.scale_log2e;
       if (lam_k) u = u * rl[o];
       y[o] = u;
       mx = __builtin_fmaxf(mx, __builtin_fabsf(u));
@@ -672,13 +756,15 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
                                                            const float* __restrict__ ws_acc,
                                                            const int8_t* __restrict__ signs_v,
                                                            const float* __restrict__ lam_v,
+                                                           const float* __restrict__ Qv, int64_t q_stride,
                                                            float* __restrict__ out, AttnGeo a) {
-  using Sc = Scales<D, ROT, VAR_REAL>;
   constexpr int PER = (D + 63) / 64;   // coordinates lane + 64 k per lane (d = 96: the second for lanes < 32)
   __shared__ __attribute__((aligned(16))) float part[4][D];
   __shared__ __attribute__((aligned(16))) float tw[ROT == ROT_SRFT ? 2 * D : 4];
+  __shared__ __attribute__((aligned(16))) float pacc[ROT == ROT_DENSE ? 1024 : 4];   // matrix: [part][d]
   __shared__ float red[2][4];
-  const int64_t v = blockIdx.x;               // b*H*R + h*R + r
+  const int64_t v = xcd_head((int64_t)a.BH * a.R);   // b*H*R + h*R + r
+  if (v < 0) return;
   const int bh = (int)(v / a.R);
   const int r = (int)(v - (int64_t)bh * a.R);
   const int t = threadIdx.x, lane = t & 63;
@@ -739,7 +825,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
     if (j < D) {
       float y = ((part[0][j] + part[1][j]) + (part[2][j] + part[3][j])) * inv_l;
       if (lam_v) y = y * rlv[decltype(ii)::value];
-      part[0][j] = y * (float)(Sc::is_edge(j) ? Sc::kFwdEdge : Sc::kFwdBulk);
+      part[0][j] = y * coord_scale<D, ROT>(j);
     }
   });
   __syncthreads();
@@ -777,6 +863,40 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
       }
       // the k = 0 term above is z_0 (its sine is 0)
       float xm = ((s0 + s1) + (s2 + s3)) + ((m & 1) ? -z[N] : z[N]);
+      if (sg[m] < 0) xm = -xm;
+      dst[m] = xm;
+    }
+  } else if constexpr (ROT == ROT_DENSE) {
+    // x_m = sum_j Q[j][m] z_j: thread t takes columns 4c .. 4c + 3 (c = t mod
+    // d/4) over rows [p JR, (p + 1) JR) (p = t / (d/4); NP = 1024/d parts of
+    // JR = d/NP rows), reading 16-byte pieces of the rows; the parts add up
+    // through LDS
+    constexpr int C4 = D / 4, NP = 256 / C4, JR = D / NP, JB = JR < 16 ? JR : 16;
+    const int c = t % C4, pr = t / C4;
+    const float* Qh = Qv + (int64_t)bh * q_stride + 4 * c;
+    const float* z = part[0];
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j0 = pr * JR; j0 < (pr + 1) * JR; j0 += JB) {
+      float4 w[JB];
+      static_for<JB>([&](auto ii) {
+        constexpr int i = decltype(ii)::value;
+        w[i] = *(const float4*)(Qh + (int64_t)(j0 + i) * D);
+      });
+      static_for<JB>([&](auto ii) {
+        constexpr int i = decltype(ii)::value;
+        const float zj = z[j0 + i];
+        acc.x = __builtin_fmaf(w[i].x, zj, acc.x);
+        acc.y = __builtin_fmaf(w[i].y, zj, acc.y);
+        acc.z = __builtin_fmaf(w[i].z, zj, acc.z);
+        acc.w = __builtin_fmaf(w[i].w, zj, acc.w);
+      });
+    }
+    *(float4*)&pacc[pr * D + 4 * c] = acc;
+    __syncthreads();
+    if (t < D) {
+      const int m = t;
+      float xm = 0.0f;
+      static_for<NP>([&](auto pp) { xm += pacc[decltype(pp)::value * D + m]; });
       if (sg[m] < 0) xm = -xm;
       dst[m] = xm;
     }

@@ -71,6 +71,10 @@ struct AttnGeo {
 struct AttnArgs {
   AttnGeo geo;
   int rot, group, bits;
+  bool dense;              // rotation given as matrices Qk, Qv (rot ignored)
+  const float* Qk;         // [., d, d] fp32, matrix of head bh at Qk + bh * q_stride
+  const float* Qv;
+  int64_t q_stride;
   const uint16_t* q;
   const uint8_t* codes_k;
   const uint16_t* scales_k;

@@ -85,13 +85,16 @@ def lib() -> ctypes.CDLL:
         L.srftq_householder_matrix.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, vp, vp, vp]
         L.srftq_quantize_dense.argtypes = [sp, vp, ctypes.c_int64, vp, vp, vp, vp, vp, vp]
         L.srftq_dequantize_dense.argtypes = [sp, vp, ctypes.c_int64, vp, vp, vp, vp, vp, vp]
+        L.srftq_decode_attention_dense.argtypes = [sp, ctypes.c_int64, ctypes.c_int32, vp, vp, ctypes.c_int64,
+                                                   vp, cv, cv, vp, ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
         L.srftq_status_string.argtypes = [ctypes.c_int]
         L.srftq_status_string.restype = ctypes.c_char_p
         L.srftq_version.argtypes = []
         for f in ("srftq_validate", "srftq_quantize", "srftq_dequantize", "srftq_rotate",
                   "srftq_unrotate", "srftq_calibrate_lambda", "srftq_cache_append",
                   "srftq_cache_read", "srftq_decode_attention", "srftq_householder_matrix",
-                  "srftq_quantize_dense", "srftq_dequantize_dense", "srftq_version"):
+                  "srftq_quantize_dense", "srftq_dequantize_dense", "srftq_decode_attention_dense",
+                  "srftq_version"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -172,6 +175,16 @@ def srftq_decode_attention(shape, t_cap, q_per_kv, q, k_view, v_view, lengths, s
                                         None if v_view is None else ctypes.byref(v_view), _dp(lengths),
                                         float(scale), _dp(out), _dp(workspace), int(workspace_bytes),
                                         _stream(stream))
+
+
+def srftq_decode_attention_dense(shape, t_cap, q_per_kv, Qk, Qv, q_stride, q, k_view, v_view, lengths, scale,
+                                 out, workspace, workspace_bytes, stream=None) -> int:
+    return lib().srftq_decode_attention_dense(ctypes.byref(shape), int(t_cap), int(q_per_kv), _dp(Qk), _dp(Qv),
+                                              int(q_stride), _dp(q),
+                                              None if k_view is None else ctypes.byref(k_view),
+                                              None if v_view is None else ctypes.byref(v_view), _dp(lengths),
+                                              float(scale), _dp(out), _dp(workspace), int(workspace_bytes),
+                                              _stream(stream))
 
 
 def srftq_householder_matrix(d, k, n, V, Q, stream=None) -> int:
@@ -353,6 +366,21 @@ def decode_attention(q, k_codes, k_scales, v_codes, v_scales, k_signs=None, k_la
     q fp16 [B, H*R, d]; caches [B, H, t_cap, .] (srftq_cache_append layout);
     lengths int32 [B] (device) or None (= T, default t_cap); scale defaults
     to 1/sqrt(d).  Returns fp32 [B, H*R, d]."""
+    return _attention(None, q, k_codes, k_scales, v_codes, v_scales, k_signs, k_lam, v_signs, v_lam, lengths,
+                      T, scale, group, bits, rot, workspace, out, stream)
+
+
+def decode_attention_dense(q, k_codes, k_scales, v_codes, v_scales, Qk, Qv, k_signs=None, k_lam=None,
+                           v_signs=None, v_lam=None, lengths=None, T=None, scale=None, group=16, bits=4,
+                           workspace=None, out=None, stream=None):
+    """decode_attention over caches written by quantize_dense: Qk, Qv fp32
+    [d, d] (one matrix) or [B, H, d, d] (one per head)."""
+    return _attention((Qk, Qv), q, k_codes, k_scales, v_codes, v_scales, k_signs, k_lam, v_signs, v_lam,
+                      lengths, T, scale, group, bits, "none", workspace, out, stream)
+
+
+def _attention(mats, q, k_codes, k_scales, v_codes, v_scales, k_signs, k_lam, v_signs, v_lam, lengths, T,
+               scale, group, bits, rot, workspace, out, stream):
     import math
 
     import torch
@@ -383,9 +411,19 @@ def decode_attention(q, k_codes, k_scales, v_codes, v_scales, k_signs=None, k_la
     out = _out(out, (B, HR, d), torch.float32, q.device, "out")
     kv = cache_view(k_codes, k_scales, k_signs, k_lam)
     vv = cache_view(v_codes, v_scales, v_signs, v_lam)
-    _check(srftq_decode_attention(sh, t_cap, R, q, kv, vv, lengths, scale, out, workspace,
-                                  workspace.numel() * workspace.element_size(), stream),
-           "srftq_decode_attention")
+    nbytes = workspace.numel() * workspace.element_size()
+    if mats is None:
+        _check(srftq_decode_attention(sh, t_cap, R, q, kv, vv, lengths, scale, out, workspace, nbytes, stream),
+               "srftq_decode_attention")
+    else:
+        Qk, Qv = mats
+        _req(Qk, torch.float32, "Qk")
+        _req(Qv, torch.float32, "Qv")
+        qs = _q_stride(Qk, B, H, d)
+        if _q_stride(Qv, B, H, d) != qs:
+            raise ValueError("Qk and Qv must both be [d, d] or both [B, H, d, d]")
+        _check(srftq_decode_attention_dense(sh, t_cap, R, Qk, Qv, qs, q, kv, vv, lengths, scale, out, workspace,
+                                            nbytes, stream), "srftq_decode_attention_dense")
     return out
 
 

@@ -183,6 +183,32 @@ def test_attention_workspace_and_argument_errors():
     assert call(shape=S.make_shape(0, 1000, 2, 128, 16, 4), q=None, out=None, ws=None) == S.SRFTQ_OK
 
 
+def test_dense_attention_argument_errors_return_before_launch():
+    sh = S.make_shape(2, 1000, 2, 128, 16, 4)
+    need = S.srftq_attention_workspace_bytes(sh, 6)
+    a, mis = _Fake(0x10000), _Fake(0x10008)
+    kv = S.CacheView(0x10000, 0x10000, None, None)
+    call = lambda shape=sh, Qk=a, Qv=a, qs=0, t_cap=1000, R=6, q=a, k=kv, v=kv, scale=0.1, out=a, ws=a, \
+        nbytes=need: S.srftq_decode_attention_dense(shape, t_cap, R, Qk, Qv, qs, q, k, v, None, scale, out, ws,
+                                                    nbytes, stream=0)
+    # the sizes of the rotation-matrix quantizer with group >= 16
+    assert call(shape=S.make_shape(2, 1000, 2, 96, 16, 4)) == S.SRFTQ_ERR_UNSUPPORTED
+    assert call(shape=S.make_shape(2, 1000, 2, 128, 8, 4)) == S.SRFTQ_ERR_UNSUPPORTED
+    assert call(shape=S.make_shape(2, 1000, 2, 128, 64, 4)) == S.SRFTQ_ERR_UNSUPPORTED
+    assert call(qs=-1) == S.SRFTQ_ERR_SHAPE
+    assert call(qs=128 * 128 - 4) == S.SRFTQ_ERR_SHAPE
+    assert call(qs=128 * 128 + 2) == S.SRFTQ_ERR_SHAPE
+    assert call(R=17) == S.SRFTQ_ERR_SHAPE
+    assert call(Qk=None) == S.SRFTQ_ERR_NULL
+    assert call(Qv=None) == S.SRFTQ_ERR_NULL
+    assert call(Qv=mis) == S.SRFTQ_ERR_ALIGN
+    assert call(q=None) == S.SRFTQ_ERR_NULL
+    assert call(out=mis) == S.SRFTQ_ERR_ALIGN
+    assert call(nbytes=need - 1) == S.SRFTQ_ERR_SHAPE
+    assert call(shape=S.make_shape(0, 1000, 2, 128, 16, 4), Qk=None, Qv=None, q=None, out=None,
+                ws=None) == S.SRFTQ_OK
+
+
 def test_dense_argument_errors_return_before_launch():
     a, mis = _Fake(0x10000), _Fake(0x10008)
     sh = S.make_shape(2, 64, 4, 256, 16, 4)

@@ -55,12 +55,31 @@ def make_case(seed, B, T, H, R, d, g, bits, rot, lam=True, scale_k=1.0, scale_v=
     return dict(q=q, K=(kc, ks, sk, lk), V=(vc, vs, sv, lv), g=g, bits=bits, rot=rot, T=T)
 
 
+def make_case_dense(seed, B, T, H, R, d, g, bits, Qk, Qv, lam=True):
+    """Caches written by the oracle's rotation-matrix quantizer: Qk, Qv fp32
+    [d, d] or [B, H, d, d]."""
+    r = np.random.default_rng(seed)
+    k = r.standard_normal((B, T, H, d)).astype(np.float16)
+    v = (r.standard_normal((B, T, H, d)) * 2.0).astype(np.float16)
+    sk = (1 - 2 * r.integers(0, 2, (B, H, d))).astype(np.int8)
+    sv = (1 - 2 * r.integers(0, 2, (B, H, d))).astype(np.int8)
+    lk = r.uniform(0.5, 2.0, (B, H, d)).astype(np.float32) if lam else None
+    lv = r.uniform(0.5, 2.0, (B, H, d)).astype(np.float32) if lam else None
+    q = (r.standard_normal((B, H * R, d)) * 1.5).astype(np.float16)
+    kc, ks = oracle.quantize_dense(k, Qk, sk, lk, g, bits)
+    vc, vs = oracle.quantize_dense(v, Qv, sv, lv, g, bits)
+    return dict(q=q, K=(kc, ks, sk, lk), V=(vc, vs, sv, lv), g=g, bits=bits, rot="dense", T=T, Qk=Qk, Qv=Qv)
+
+
 def run_gpu(c, lengths=None, scale=None):
     K, V = c["K"], c["V"]
-    out = S.decode_attention(dev(c["q"]), dev(K[0]), dev(K[1].view(np.float16)), dev(V[0]),
-                             dev(V[1].view(np.float16)), dev(K[2]), dev(K[3]), dev(V[2]), dev(V[3]),
-                             lengths=dev(lengths), T=c["T"], scale=scale, group=c["g"], bits=c["bits"],
-                             rot=c["rot"])
+    args = (dev(c["q"]), dev(K[0]), dev(K[1].view(np.float16)), dev(V[0]), dev(V[1].view(np.float16)))
+    kw = dict(k_signs=dev(K[2]), k_lam=dev(K[3]), v_signs=dev(V[2]), v_lam=dev(V[3]), lengths=dev(lengths),
+              T=c["T"], scale=scale, group=c["g"], bits=c["bits"])
+    if c["rot"] == "dense":
+        out = S.decode_attention_dense(*args, dev(c["Qk"]), dev(c["Qv"]), **kw)
+    else:
+        out = S.decode_attention(*args, rot=c["rot"], **kw)
     torch.cuda.synchronize()
     return host(out)
 
@@ -71,18 +90,29 @@ def check(c, got, lengths=None, scale=None):
     H = K[0].shape[1]
     R, T, g, bits, rot = HR // H, c["T"], c["g"], c["bits"], c["rot"]
     scale = 1.0 / np.sqrt(d) if scale is None else scale
-    ref = oracle.decode_attention(q, K[0], K[1], V[0], V[1], T=T, lengths=lengths, signs_k=K[2],
-                                  lam_k=K[3], signs_v=V[2], lam_v=V[3], group=g, bits=bits, rot=rot,
-                                  scale=scale)
+    kw = dict(T=T, lengths=lengths, signs_k=K[2], lam_k=K[3], signs_v=V[2], lam_v=V[3], group=g, bits=bits,
+              scale=scale)
+    if rot == "dense":
+        ref = oracle.decode_attention_dense(q, K[0], K[1], V[0], V[1], c["Qk"], c["Qv"], **kw)
+        _, vh = oracle.dequantize_dense(V[0][:, :, :T], V[1][:, :, :T], c["Qv"], V[2], V[3], g, bits, d=d,
+                                        return_f64=True)
+    else:
+        ref = oracle.decode_attention(q, K[0], K[1], V[0], V[1], rot=rot, **kw)
+        _, vh = oracle.dequantize(V[0][:, :, :T], V[1][:, :, :T], V[2], V[3], g, bits, rot, d=d,
+                                  return_f64=True)
     assert np.all(np.isfinite(got))
     # per-vector bound
-    _, vh = oracle.dequantize(V[0][:, :, :T], V[1][:, :, :T], V[2], V[3], g, bits, rot, d=d, return_f64=True)
     vnorm = np.linalg.norm(vh, axis=-1)                                   # [B, T, H]
     ck = decode_codes(K[0][:, :, :T], bits, d).astype(np.float64)         # [B, H, T, d]
     sk = np.repeat(K[1][:, :, :T].view(np.float16).astype(np.float64), g, axis=-1)
     yk = ck * sk / (1.0 if K[3] is None else K[3][:, :, None].astype(np.float64))
-    u = oracle.rotate(q.reshape(B, 1, HR, d), np.repeat(K[2], R, axis=1) if K[2] is not None else None,
-                      rot)[:, 0] * scale                                  # [B, HR, d]
+    if rot == "dense":                                                    # u = Qk (s_k . q) * scale
+        Qk = np.broadcast_to(np.asarray(c["Qk"], np.float64), (B, H, d, d))
+        xs = q.astype(np.float64).reshape(B, H, R, d) * (1.0 if K[2] is None else K[2][:, :, None])
+        u = np.einsum("bhjm,bhrm->bhrj", Qk, xs).reshape(B, HR, d) * scale
+    else:
+        u = oracle.rotate(q.reshape(B, 1, HR, d), np.repeat(K[2], R, axis=1) if K[2] is not None else None,
+                          rot)[:, 0] * scale                              # [B, HR, d]
     worst = 0.0
     for b in range(B):
         L = T if lengths is None else min(max(int(lengths[b]), 0), T)
@@ -136,6 +166,43 @@ def test_attention_d96_lengths():
     c = make_case(7060, 8, 80, 1, 4, 96, 32, 4, "srft", cap=96)
     lengths = np.array([0, 1, 15, 16, 17, 63, 80, 500], dtype=np.int32)
     print(check(c, run_gpu(c, lengths), lengths))
+
+
+def _householder(seed, lead, d):
+    r = np.random.default_rng(seed)
+    return oracle.householder_matrix(r.standard_normal(tuple(lead) + (d // 2, d))).astype(np.float32)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("g,bits", [(16, 4), (32, 8)])
+def test_attention_dense(d, g, bits):
+    """Caches written with Householder rotations (one per head for K, one
+    shared matrix for V), four chunks, ragged lengths, lambda on for int4."""
+    B, T, H, R = 2, 1100, 2, {64: 2, 128: 6, 256: 8}[d]
+    Qk = _householder(7400 + d, (B, H), d)
+    Qv = _householder(7401 + d, (), d)
+    Qv = np.ascontiguousarray(np.broadcast_to(Qv, (B, H, d, d)))
+    c = make_case_dense(7402 + d + g, B, T, H, R, d, g, bits, Qk, Qv, lam=bits == 4)
+    lengths = np.array([1100, 681], dtype=np.int32)
+    print(f"[attention dense d={d} g={g} b={bits}]", flush=True)
+    print(check(c, run_gpu(c, lengths), lengths))
+
+
+def test_attention_dense_shared_matrix_and_identity():
+    """One matrix for every head (q_stride 0); the identity matrix gives the
+    rot = none attention of the same caches."""
+    B, T, H, R, d, g, bits = 2, 300, 2, 3, 128, 16, 4
+    Q = _householder(7410, (), d)
+    c = make_case_dense(7411, B, T, H, R, d, g, bits, Q, Q)
+    lengths = np.array([300, 17], dtype=np.int32)
+    print(check(c, run_gpu(c, lengths), lengths))
+    I = np.eye(d, dtype=np.float32)
+    c = make_case(7412, B, T, H, R, d, g, bits, "none")
+    got_none = run_gpu(c, lengths)
+    c.update(rot="dense", Qk=I, Qv=I)
+    got_eye = run_gpu(c, lengths)
+    print(check(c, got_eye, lengths))
+    assert np.allclose(got_eye, got_none, rtol=1e-5, atol=1e-5 * np.abs(got_none).max())
 
 
 def test_attention_lengths():
