@@ -284,3 +284,52 @@ def test_attention_bench_workload_sampled():
                     lam[2 * b + 1:2 * b + 2]),
                  g=w.group, bits=w.bits, rot="srft", T=w.T)
         print(f"[bench workload layer {b}]", check(c, out[b:b + 1]), flush=True)
+
+
+@pytest.mark.parametrize("kind", ["srft", "dense"])
+def test_attention_in_graph_replays(kind):
+    """One decode-attention call captured in a HIP graph (fixed workspace and
+    output) and replayed three times with new queries, eager work and
+    synchronisations in between: every replay equals the eager call bit for
+    bit (the launches hold no memsets and the plan depends on the shape only)."""
+    B, T, H, R, d, g, bits = 2, 600, 2, 6, 128, 16, 4
+    if kind == "dense":
+        Q = _householder(7500, (), d)
+        c = make_case_dense(7501, B, T, H, R, d, g, bits, Q, Q)
+    else:
+        c = make_case(7502, B, T, H, R, d, g, bits, "srft")
+    K, V = c["K"], c["V"]
+    lengths = dev(np.array([600, 333], dtype=np.int32))
+    caches = (dev(K[0]), dev(K[1].view(np.float16)), dev(V[0]), dev(V[1].view(np.float16)))
+    side = dict(k_signs=dev(K[2]), k_lam=dev(K[3]), v_signs=dev(V[2]), v_lam=dev(V[3]), lengths=lengths,
+                group=g, bits=bits)
+    if kind == "dense":
+        Qd = dev(Q)
+        call = lambda qq, **kw: S.decode_attention_dense(qq, *caches, Qd, Qd, **side, **kw)
+    else:
+        call = lambda qq, **kw: S.decode_attention(qq, *caches, rot="srft", **side, **kw)
+    r = np.random.default_rng(7503)
+    qs = [dev(r.standard_normal((B, H * R, d)).astype(np.float16)) for _ in range(3)]
+    eager = [call(qq).clone() for qq in qs]
+    torch.cuda.synchronize()
+
+    q_buf = qs[0].clone()
+    ws = torch.empty((S.srftq_attention_workspace_bytes(S.make_shape(B, T, H, d, g, bits), R),),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, H * R, d), dtype=torch.float32, device="cuda")
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):            # warm-up outside the capture
+        call(q_buf, workspace=ws, out=out)
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(q_buf, workspace=ws, out=out)
+    for i in range(3):
+        q_buf.copy_(qs[i])
+        out.fill_(float("nan"))
+        call(qs[(i + 1) % 3])              # eager work on the same buffers' neighbours in between
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager[i]), f"replay {i}"
