@@ -237,6 +237,15 @@ def test_attention_long_context():
     print(check(c, run_gpu(c, lengths), lengths))
 
 
+def test_attention_more_chunks_than_threads():
+    """One (tensor, KV head) pair with 70,000 tokens: 273 chunks, more than
+    the combine kernel's 256 threads, so its loops over the chunk maxima and
+    sums take more than one pass."""
+    c = make_case(7310, 1, 70000, 1, 2, 64, 16, 4, "srft")
+    lengths = np.array([69999], dtype=np.int32)
+    print(check(c, run_gpu(c, lengths), lengths))
+
+
 def test_attention_with_the_append_cache():
     """The container's caches, grown by a prefill and decode steps, read by
     decode attention at the container's lengths."""
