@@ -25,14 +25,7 @@ int device_cu_count() {
 
 const int8_t* plus_ones_ptr();   // defined with the device array in ones.hip
 
-int tiles_per_block(int d) {
-  static const int env = [] {
-    const char* e = getenv("SRFTQ_TILES_PER_BLOCK");
-    return e ? atoi(e) : -1;
-  }();
-  if (env >= 0) return env;
-  return d >= 256 ? 0 : 1;
-}
+int tiles_per_block(int d) { return d >= 256 ? 0 : 1; }
 
 int blocks_per_cu(const void* kernel, int block) {
   static std::mutex mu;

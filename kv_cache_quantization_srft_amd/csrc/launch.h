@@ -132,7 +132,6 @@ int blocks_per_cu(const void* kernel, int block);
 // per block lets the hardware dispatcher balance the load across CUs (waves
 // of a persistent grid finish up to 40 % apart); at d = 256, with one wave
 // per SIMD, the persistent grid's one-tile-ahead prefetch hides more latency.
-// SRFTQ_TILES_PER_BLOCK overrides it (tuning).
 int tiles_per_block(int d);
 
 // Persistent grid: at most (resident blocks per CU) x CUs, at least 1.
