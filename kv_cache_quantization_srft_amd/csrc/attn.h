@@ -308,7 +308,8 @@ __global__ __launch_bounds__(256) void attn_qprep_kernel(const uint16_t* __restr
   constexpr bool kSplit = ROT == ROT_SRFT || ROT == ROT_DENSE;
   __shared__ __attribute__((aligned(16))) float xs[kSplit ? D : 4];
   __shared__ __attribute__((aligned(16))) float tw[ROT == ROT_SRFT ? 2 * D : 4];
-  __shared__ __attribute__((aligned(16))) float red[kSplit ? 4 * NO * 64 : 4];   // [wave][o][lane]
+  __shared__ __attribute__((aligned(16))) float red[ROT == ROT_SRFT ? 4 * NO * 64 : 4];   // [wave][o][lane]
+  __shared__ float usum[ROT == ROT_DENSE ? D : 1];                                 // matrix rows' sums
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int64_t v = xcd_head((int64_t)a.BH * a.R);
@@ -367,7 +368,7 @@ __global__ __launch_bounds__(256) void attn_qprep_kernel(const uint16_t* __restr
     }
     __syncthreads();
     const int m0 = wave * MQ;
-    float part[NO];
+    float part[NO];   // SRFT: this wave's quarter of each bin
     if constexpr (ROT == ROT_SRFT) {
       static_for<KPL>([&](auto kk) {
         constexpr int i = decltype(kk)::value;
@@ -392,37 +393,61 @@ __global__ __launch_bounds__(256) void attn_qprep_kernel(const uint16_t* __restr
         part[2 * i + 1] = (im[0] + im[1]) + (im[2] + im[3]);
       });
     } else {
-      // u_j = sum_m Q[j][m] x_m, rows j = lane + 64 o of this head's matrix
-      const float* Qh = Qk + bh * q_stride;
-      static_for<NO>([&](auto oo) {
-        constexpr int o = decltype(oo)::value;
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
-        if (jo[o] >= 0) {
-          const float4* row = (const float4*)(Qh + (int64_t)jo[o] * D + m0);
-          float4 w[MQ / 4];
-          static_for<MQ / 4>([&](auto mm) { w[decltype(mm)::value] = row[decltype(mm)::value]; });
-          static_for<MQ / 4>([&](auto mm) {
-            constexpr int m = decltype(mm)::value;
-            const float4 xv = *(const float4*)&xs[m0 + 4 * m];
-            acc[0] = __builtin_fmaf(w[m].x, xv.x, acc[0]);
-            acc[1] = __builtin_fmaf(w[m].y, xv.y, acc[1]);
-            acc[2] = __builtin_fmaf(w[m].z, xv.z, acc[2]);
-            acc[3] = __builtin_fmaf(w[m].w, xv.w, acc[3]);
+      // u_j = sum_m Q[j][m] x_m.  Wave w takes rows [w d/4, (w + 1) d/4).  A
+      // load instruction covers RPI whole rows, LPR lanes of 16 bytes each
+      // (1 KiB contiguous), so each lane holds one 4-column partial per
+      // instruction; a transposing butterfly over the LPR lanes of a row
+      // (halving the values at each step) leaves row i of the wave's rows on
+      // lanes lr = i SPL .. i SPL + SPL - 1 of each group.
+      constexpr int LPR = D / 4, RPI = 64 / LPR, NI = D * D / 1024, SPL = LPR / NI;
+      constexpr int BATCH = NI < 16 ? NI : 16;
+      const int lr = lane % LPR, grp = lane / LPR;
+      const float4 xv = *(const float4*)&xs[4 * lr];
+      const float4* src = (const float4*)(Qk + bh * q_stride) + (int64_t)wave * (D / 4) * LPR + lane;
+      float pv[NI];
+      static_for<NI / BATCH>([&](auto bb) {
+        constexpr int b0 = decltype(bb)::value * BATCH;
+        float4 w[BATCH];
+        static_for<BATCH>([&](auto ii) { w[decltype(ii)::value] = src[(b0 + decltype(ii)::value) * 64]; });
+        static_for<BATCH>([&](auto ii) {
+          constexpr int i = decltype(ii)::value;
+          pv[b0 + i] = __builtin_fmaf(w[i].x, xv.x, w[i].y * xv.y) + __builtin_fmaf(w[i].z, xv.z, w[i].w * xv.w);
+        });
+      });
+      static_for<6>([&](auto ss) {
+        constexpr int st = decltype(ss)::value;
+        constexpr int half = NI >> (st + 1), mask = LPR >> (st + 1);
+        if constexpr (half >= 1) {
+          const bool up = (lane & mask) != 0;
+          static_for<half>([&](auto kk) {
+            constexpr int k = decltype(kk)::value;
+            const float send = up ? pv[k] : pv[k + half];
+            const float keep = up ? pv[k + half] : pv[k];
+            pv[k] = keep + __shfl_xor(send, mask);
           });
         }
-        part[o] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+      });
+      static_for<6>([&](auto ss) {
+        constexpr int mask = SPL >> (decltype(ss)::value + 1);
+        if constexpr (mask >= 1) pv[0] += __shfl_xor(pv[0], mask);
+      });
+      if (lr % SPL == 0) usum[wave * (D / 4) + (lr / SPL) * RPI + grp] = pv[0];
+    }
+    if constexpr (ROT == ROT_SRFT) {
+      static_for<NO>([&](auto oo) {
+        constexpr int o = decltype(oo)::value;
+        red[(wave * NO + o) * 64 + lane] = part[o];
       });
     }
-    static_for<NO>([&](auto oo) {
-      constexpr int o = decltype(oo)::value;
-      red[(wave * NO + o) * 64 + lane] = part[o];
-    });
     __syncthreads();
     if (wave != 0) return;
     static_for<NO>([&](auto oo) {
       constexpr int o = decltype(oo)::value;
-      y[o] = (red[o * 64 + lane] + red[(NO + o) * 64 + lane]) +
-             (red[(2 * NO + o) * 64 + lane] + red[(3 * NO + o) * 64 + lane]);
+      if constexpr (ROT == ROT_DENSE)
+        y[o] = jo[o] >= 0 ? usum[jo[o]] : 0.0f;
+      else
+        y[o] = (red[o * 64 + lane] + red[(NO + o) * 64 + lane]) +
+               (red[(2 * NO + o) * 64 + lane] + red[(3 * NO + o) * 64 + lane]);
     });
     if constexpr (ROT == ROT_SRFT) {
       // X_{d/2} = sum_m (-1)^m x_m (P is even: element P l + t has the sign of t)
