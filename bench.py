@@ -449,8 +449,8 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(every KV vector is independent; see the sharding notes in DESIGN.md)", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (every KV vector is "
+              "independent, so the path shards by heads or tokens with no exchange)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
