@@ -311,8 +311,9 @@ def test_many_tensors_single_token():
 @pytest.mark.parametrize("d", [64, 128, 256])
 def test_few_tokens_one_vector_per_lane(T, d):
     """Up to 8 tokens per tensor quantize one vector per lane over the
-    flattened (tensor, token, head) index (decode steps); 9 takes the tiled
-    kernel.  Many tensors and heads, every rotation path, lambda on and off."""
+    flattened (tensor, token, head) index (decode steps) at d <= 128; 9
+    tokens, and any count at d = 256, take the tiled kernel.  Many tensors
+    and heads, every rotation path, lambda on and off."""
     B, H = 37, 3
     for i, (rot, variant) in enumerate(ROTS):
         lam = (i + T) % 2 == 0
