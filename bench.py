@@ -189,6 +189,25 @@ def decode_append_latency(steps: int = 1000, graph_steps: int = 100) -> dict:
     wall = np.array(wall)
     eager_codes, eager_scales = codes.clone(), scales.clone()
 
+    # the same eager steps through a CacheAppender (arguments checked once)
+    app = S.CacheAppender(codes, scales, pos, sd, None, w.group, w.bits)
+    pos.zero_()
+    for i in range(20):
+        app(xs[i % graph_steps])
+        pos.add_(1)
+    pos.zero_()
+    torch.cuda.synchronize()
+    wall_p = []
+    for i in range(steps):
+        t = time.perf_counter()
+        app(xs[i % graph_steps])
+        pos.add_(1)
+        torch.cuda.synchronize()
+        wall_p.append((time.perf_counter() - t) * 1e6)
+    wall_p = np.array(wall_p)
+    prepared_same = bool(torch.equal(codes, eager_codes)
+                         and torch.equal(scales.view(torch.int16), eager_scales.view(torch.int16)))
+
     # the same steps captured once and replayed (positions keep advancing on
     # the device; rows past the capacity would be dropped, none are reached)
     pos.zero_()
@@ -227,6 +246,9 @@ def decode_append_latency(steps: int = 1000, graph_steps: int = 100) -> dict:
             "vectors_per_step": B * H,
             "eager_us_per_step": {"mean": float(wall.mean()), "p50": float(np.percentile(wall, 50)),
                                   "p99": float(np.percentile(wall, 99))},
+            "eager_prepared_us_per_step": {"mean": float(wall_p.mean()), "p50": float(np.percentile(wall_p, 50)),
+                                           "p99": float(np.percentile(wall_p, 99)),
+                                           "rows_match_eager": prepared_same},
             "graph_us_per_step": graph_us,
             "graph_ns_per_vector": graph_us * 1e3 / (B * H),
             "graph_rows_match_eager": same,

@@ -341,6 +341,49 @@ def cache_append(x, codes, scales, pos=None, signs=None, lam=None, group=16, bit
     return codes, scales
 
 
+class CacheAppender:
+    """srftq_cache_append with everything but the new tokens checked once.
+
+    For decode loops, where the per-call checks of cache_append cost more host
+    time than the kernel: the caches, positions, signs, lambda, sizes and
+    stream are fixed at construction (stream None: the current stream at that
+    moment); each call passes x fp16 [B, tokens, H, d] of the same shape
+    every time and runs srftq_cache_append on it.  The positions are read by
+    the kernel when it runs, so the caller may advance them on the device
+    between calls.  Not for use inside a graph capture on another stream."""
+
+    def __init__(self, codes, scales, pos, signs=None, lam=None, group=16, bits=4, rot="srft",
+                 variant="default", tokens=1, stream=None):
+        import torch
+        for t, dt, n in ((codes, torch.uint8, "codes"), (scales, torch.float16, "scales"),
+                         (pos, torch.int32, "pos"), (signs, torch.int8, "signs"),
+                         (lam, torch.float32, "lambda")):
+            _req(t, dt, n)
+        if pos is None:
+            raise ValueError("pos is required")
+        d = codes.shape[-1] * 8 // bits
+        B, H, t_cap = _cache_dims(codes, scales, d, bits, group)
+        if tuple(pos.shape) != (B,):
+            raise ValueError(f"pos must have shape ({B},)")
+        self._shape = make_shape(B, int(tokens), H, d, group, bits, rot, variant)
+        st = srftq_validate(self._shape)
+        if st != SRFTQ_OK:
+            _check(st, "srftq_validate")
+        self.x_shape = (B, int(tokens), H, d)
+        self._keep = (codes, scales, pos, signs, lam)        # the tensors outlive the appender's calls
+        self._fn = lib().srftq_cache_append
+        self._args = (ctypes.byref(self._shape), int(t_cap), _dp(pos))
+        self._rest = (_dp(signs), _dp(lam), _dp(codes), _dp(scales), _stream(stream))
+        self._f16 = torch.float16
+
+    def __call__(self, x):
+        if tuple(x.shape) != self.x_shape or x.dtype != self._f16 or not x.is_contiguous():
+            raise ValueError(f"x must be a contiguous fp16 tensor of shape {self.x_shape}")
+        st = self._fn(*self._args, x.data_ptr(), *self._rest)
+        if st != SRFTQ_OK:
+            _check(st, "srftq_cache_append")
+
+
 def cache_read(codes, scales, T, signs=None, lam=None, group=16, bits=4, rot="srft", variant="default",
                d=None, out=None, stream=None):
     """Dequantize + unrotate rows [0, T) of every head of a cache

@@ -208,3 +208,33 @@ def test_append_in_graph_replays():
         assert torch.equal(pos, torch.full((B,), steps, dtype=torch.int32, device="cuda"))
         S.quantize(xs[0], s, None, g, bits)   # eager work between replays
         torch.cuda.synchronize()
+
+
+def test_prepared_appender_matches_cache_append():
+    """CacheAppender (arguments checked once, positions advanced on the device
+    between calls) writes exactly what cache_append writes, with lambda, and
+    rejects an input of another shape or type."""
+    B, H, d, g, bits, steps, cap = 16, 4, 128, 16, 4, 5, 8
+    r = np.random.default_rng(5500)
+    xs = [dev(r.standard_normal((B, 1, H, d)).astype(np.float16)) for _ in range(steps)]
+    s = dev((1 - 2 * r.integers(0, 2, (B, H, d))).astype(np.int8))
+    lam = dev(r.uniform(0.5, 2.0, (B, H, d)).astype(np.float32))
+    start = torch.from_numpy(r.integers(0, 3, B).astype(np.int32)).cuda()
+    ce, se = sentinel_cache(B, H, cap, d, g, bits)
+    pos = start.clone()
+    for i in range(steps):
+        S.cache_append(xs[i], ce, se, pos, s, lam, g, bits)
+        pos += 1
+    cp, sp = sentinel_cache(B, H, cap, d, g, bits)
+    pos = start.clone()
+    app = S.CacheAppender(cp, sp, pos, s, lam, g, bits)
+    for i in range(steps):
+        app(xs[i])
+        pos += 1
+    torch.cuda.synchronize()
+    assert torch.equal(cp, ce)
+    assert torch.equal(sp.view(torch.int16), se.view(torch.int16))
+    with pytest.raises(ValueError):
+        app(xs[0].float())
+    with pytest.raises(ValueError):
+        app(torch.cat([xs[0], xs[1]], dim=1))
