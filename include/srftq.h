@@ -21,11 +21,18 @@
  *       y = [Re X_0, sqrt2 Re X_1 .. sqrt2 Re X_{N-1}, Re X_N,
  *            sqrt2 Im X_1 .. sqrt2 Im X_{N-1}],  N = d/2.
  *     SRHT: y = H_d (s . x) / sqrt(d), H_d in Sylvester (natural) order.
- *   - z_j = lambda_j * y_j.  Per group G of `group` consecutive coordinates:
- *       a = max |z_j|, sigma = fp16_rne(min(a * fp32(1/qmax), 65504)),
+ *   - z_j = lambda_j * y_j.  Per group G of `group` consecutive coordinates
+ *     the definition is
+ *       a = max |z_j|, sigma = fp16_rne(min(a / qmax, 65504)),
  *       q_j = 0 if sigma == 0 else clamp(rne(z_j / sigma), -qmax, qmax),
- *     qmax = 7 (bits 4) or 127 (bits 8); the decision is taken in fp32 and
- *     against the stored fp16 sigma.
+ *     qmax = 7 (bits 4) or 127 (bits 8), the codes taken against the stored
+ *     fp16 sigma.  The kernels compute it in fp32: z, a and a * fp32(1/qmax)
+ *     in fp32, and the quotient as the exact product z_j * r rounded half to
+ *     even, r = fp32(1/sigma) correctly rounded.  r differs from 1/sigma by
+ *     at most 2^-24 relative, so a code can differ from the definition's
+ *     only where z_j / sigma lies within 2^-24 * |z_j / sigma| (plus the
+ *     fp32 rotation error) of a half-integer, and then by +-1; sigma = 1/2^k
+ *     makes r exact, so exact ties then round to even as defined.
  *   - int4 codes: two's-complement nibbles, coordinate 2i in the low nibble
  *     of byte i.  int8 codes: one two's-complement byte per coordinate.
  *   - Dequantize: yhat_j = q_j * sigma_G / lambda_j, x = s . (M^T yhat),

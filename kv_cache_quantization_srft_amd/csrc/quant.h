@@ -3,11 +3,14 @@
 // "When Quantization Is Free" (gist.science summary), "Metodologia" 2 step 4
 // (per-channel lambda rescale, per-group absmax, rounding to signed
 // int4/int8) and step 5 (two int4 per byte), with "Metodologia" 3
-// (per-channel + per-group scaling).  Decision rule (fp32):
-//   z = lambda * y;  a = max_G |z|;  sigma = fp16(min(a * fp32(1/qmax), 65504));
-//   r = fp32(1/sigma) correctly rounded;
-//   q = clamp(rne(z * r), -qmax, qmax) with the product exact  (q = 0 when
-//   sigma == 0).
+// (per-channel + per-group scaling).  The definition is
+//   z = lambda * y;  a = max_G |z|;  sigma = fp16(min(a / qmax, 65504));
+//   q = clamp(rne(z / sigma), -qmax, qmax)  (q = 0 when sigma == 0).
+// Computed here in fp32: z and a in fp32, sigma = fp16(min(a * fp32(1/qmax),
+// 65504)), and the quotient as rne(z * r) with r = fp32(1/sigma) correctly
+// rounded and the product exact.  r is within 2^-24 (relative) of 1/sigma,
+// so q can differ from rne(z / sigma), by +-1, only where z / sigma lies
+// within that distance (plus the rotation's fp32 error) of a half-integer.
 //
 // Implementation notes (gfx950):
 //   - The transform leaves y unscaled; the per-coordinate scale c_j is

@@ -122,15 +122,16 @@ def unrotate(y, signs=None, rot="srft") -> np.ndarray:
 
 
 def quantize(x16, signs=None, lam=None, group=16, bits=4, rot="srft", return_z=False):
-    """Return (codes uint8, scales fp16-bits uint16[, z fp32]) in the
+    """Return (codes uint8, scales fp16-bits uint16[, z fp64]) in the
     head-major cache layout: [B, H, T, .] for x [B, T, H, d] ([H, T, .] for
-    3-D x [T, H, d])."""
+    3-D x [T, H, d]).  z = lambda * y is the value each code was decided on:
+    sigma = fp16(min(max_G |z| / qmax, 65504)), q = clamp(rne(z / sigma))."""
     x, B, T, H, d = _as4(_bits(x16))
     s = _signs(signs, B, H, d)
     l = _lam(lam, B, H, d)
     codes = np.empty((B, H, T, d * bits // 8), dtype=np.uint8)
     scales = np.empty((B, H, T, d // group), dtype=np.uint16)
-    z = np.empty((B, H, T, d), dtype=np.float32) if return_z else None
+    z = np.empty((B, H, T, d), dtype=np.float64) if return_z else None
     _check(lib().oracle_quantize(B, T, H, d, group, bits, ROT[rot], _ptr(x), _ptr(s), _ptr(l),
                                  _ptr(codes), _ptr(scales), _ptr(z)), "quantize")
     out = (codes, scales) + ((z,) if return_z else ())
@@ -204,7 +205,7 @@ def quantize_dense(x16, Q, signs=None, lam=None, group=16, bits=4, return_z=Fals
     q, qs = _dense_q(Q, B, H, d)
     codes = np.empty((B, H, T, d * bits // 8), dtype=np.uint8)
     scales = np.empty((B, H, T, d // group), dtype=np.uint16)
-    z = np.empty((B, H, T, d), dtype=np.float32) if return_z else None
+    z = np.empty((B, H, T, d), dtype=np.float64) if return_z else None
     _check(lib().oracle_quantize_dense(B, T, H, d, group, bits, _ptr(q), qs, _ptr(x), _ptr(s), _ptr(l),
                                        _ptr(codes), _ptr(scales), _ptr(z)), "quantize_dense")
     out = (codes, scales) + ((z,) if return_z else ())

@@ -34,14 +34,11 @@
  *   - lambda multiplies the rotated coordinate (after the unpack);
  *     dequantization divides by it.
  *   - Symmetric code range [-qmax, qmax], qmax = 7 (int4) or 127 (int8).
- *   - The quantization decision is taken in fp32, the precision of the GPU
- *     kernel: z = fp32(lambda * y); a = max |z| over the group;
- *     t = min(a * fp32(1/qmax), 65504) (fp32 multiply);
- *     sigma = fp16 round-to-nearest-even(t), stored;
- *     r = fp32(1 / sigma), correctly rounded;
- *     q = 0 if sigma == 0 else clamp(rne(z * r), -qmax, qmax), with the
- *     product z * r taken exactly, and the codes taken against the stored
- *     fp16 sigma.
+ *   - The quantizer is the plain definition, in fp64: z = lambda * y;
+ *     a = max |z| over the group; sigma = fp16 round-to-nearest-even of
+ *     min(a / qmax, 65504), stored; q = 0 if sigma == 0, else
+ *     clamp(rne(z / sigma), -qmax, qmax), the quotient taken against the
+ *     stored fp16 sigma and rounded half to even.
  *   - int4 nibbles are two's complement, even coordinate in the low nibble.
  *   - signs == NULL means s = +1; lambda == NULL means lambda = 1.
  *
@@ -54,7 +51,7 @@
  *   lambda     fp32       [B, H, d]
  *   codes      uint8      [B, H, T, d*bits/8]
  *   scales     fp16 bits  [B, H, T, d/group]
- *   z_out      fp32       [B, H, T, d]   (rows aligned with codes)
+ *   z_out      fp64       [B, H, T, d]   (rows aligned with codes)
  *   Q          fp32       row-major d x d at Q + (b*H + h) * q_stride
  */
 #include <math.h>
@@ -347,14 +344,15 @@ static void dense_apply_t(int d, const float *Q, const double *y, double *xs)
 }
 
 /*
- * Quantize every vector.  z_out (optional, fp32 [B,H,T,d]) receives the fp32
- * values the decision was taken on.  Q (optional) replaces the rotation.
+ * Quantize every vector.  z_out (optional, fp64 [B,H,T,d]) receives the
+ * values z = lambda * y the decision was taken on.  Q (optional) replaces
+ * the rotation.
  */
 static int quantize_impl(int64_t B, int64_t T, int H, int d, int group, int bits,
                          int rot, const float *Q, int64_t q_stride, const uint16_t *x,
                          const int8_t *signs,
                          const float *lambda, uint8_t *codes, uint16_t *scales,
-                         float *z_out)
+                         double *z_out)
 {
     int st = check_shape(B, T, H, d, rot);
     if (!st)
@@ -363,7 +361,6 @@ static int quantize_impl(int64_t B, int64_t T, int H, int d, int group, int bits
         return st;
     int64_t nvec = B * T * H;
     int qmax = (bits == 4) ? 7 : 127;
-    float qinv = (float)(1.0 / (double)qmax);   /* fp32(1/qmax) */
     int ng = d / group;
     size_t code_row = (size_t)d * (size_t)bits / 8;
     double *cs = (double *)malloc(sizeof(double) * (size_t)d);
@@ -373,7 +370,7 @@ static int quantize_impl(int64_t B, int64_t T, int H, int d, int group, int bits
     {
         double *xs = (double *)malloc(sizeof(double) * (size_t)d);
         double *y = (double *)malloc(sizeof(double) * (size_t)d);
-        float *z = (float *)malloc(sizeof(float) * (size_t)d);
+        double *z = (double *)malloc(sizeof(double) * (size_t)d);
         int *q = (int *)malloc(sizeof(int) * (size_t)d);
 #pragma omp for schedule(static)
         for (int64_t v = 0; v < nvec; ++v) {
@@ -387,34 +384,30 @@ static int quantize_impl(int64_t B, int64_t T, int H, int d, int group, int bits
                 dense_apply(d, Q + ((size_t)b * H + h) * (size_t)q_stride, xs, y);
             else
                 rotate_one(d, rot, xs, y, cs, sn);
+            /* per-channel rescale after the rotation */
             for (int j = 0; j < d; ++j) {
                 double lam = lambda ? (double)lambda[((size_t)b * H + h) * d + j] : 1.0;
-                z[j] = (float)(lam * y[j]);
+                z[j] = lam * y[j];
             }
+            /* per-group absmax scale, stored as fp16; codes against it */
             for (int g = 0; g < ng; ++g) {
-                float a = 0.0f;
+                double a = 0.0;
                 for (int j = g * group; j < (g + 1) * group; ++j) {
-                    float m = fabsf(z[j]);
+                    double m = fabs(z[j]);
                     if (m > a)
                         a = m;
                 }
-                float t = a * qinv;
-                if (t > 65504.0f)
-                    t = 65504.0f;
-                uint16_t sh = oracle_f64_to_f16((double)t);
-                float sg = (float)oracle_f16_to_f64(sh);
+                double t = a / (double)qmax;
+                if (t > 65504.0)
+                    t = 65504.0;
+                uint16_t sh = oracle_f64_to_f16(t);
+                double sg = oracle_f16_to_f64(sh);
                 scales[c * ng + g] = sh;
-                /* fp32 reciprocal of the stored scale, correctly rounded:
-                 * the double quotient is exact to 2^-53 and 1/sigma never
-                 * sits within 2^-36 of an fp32 midpoint, so one rounding
-                 * of it to float is the correct rounding. */
-                float r = sg == 0.0f ? 0.0f : (float)(1.0 / (double)sg);
                 for (int j = g * group; j < (g + 1) * group; ++j) {
-                    if (sg == 0.0f) {
+                    if (sg == 0.0) {
                         q[j] = 0;
                     } else {
-                        /* 24-bit x 24-bit product: exact in double */
-                        double n = nearbyint((double)z[j] * (double)r);   /* ties to even */
+                        double n = nearbyint(z[j] / sg);   /* ties to even */
                         if (n > (double)qmax)
                             n = (double)qmax;
                         if (n < (double)-qmax)
@@ -432,7 +425,7 @@ static int quantize_impl(int64_t B, int64_t T, int H, int d, int group, int bits
                     row[i] = (uint8_t)((q[2 * i] & 0xF) | ((q[2 * i + 1] & 0xF) << 4));
             }
             if (z_out)
-                memcpy(z_out + c * d, z, sizeof(float) * (size_t)d);
+                memcpy(z_out + c * d, z, sizeof(double) * (size_t)d);
         }
         free(xs);
         free(y);
@@ -447,7 +440,7 @@ static int quantize_impl(int64_t B, int64_t T, int H, int d, int group, int bits
 int oracle_quantize(int64_t B, int64_t T, int H, int d, int group, int bits,
                     int rot, const uint16_t *x, const int8_t *signs,
                     const float *lambda, uint8_t *codes, uint16_t *scales,
-                    float *z_out)
+                    double *z_out)
 {
     return quantize_impl(B, T, H, d, group, bits, rot, NULL, 0, x, signs, lambda, codes, scales, z_out);
 }
@@ -459,7 +452,7 @@ int oracle_quantize(int64_t B, int64_t T, int H, int d, int group, int bits,
 int oracle_quantize_dense(int64_t B, int64_t T, int H, int d, int group, int bits,
                           const float *Q, int64_t q_stride, const uint16_t *x, const int8_t *signs,
                           const float *lambda, uint8_t *codes, uint16_t *scales,
-                          float *z_out)
+                          double *z_out)
 {
     if (!Q)
         return 1;

@@ -109,6 +109,29 @@ def test_constructed_ties_exact():
         run_and_check(x, None, None, g, bits, "none", "default")
 
 
+def test_ties_with_a_non_power_of_two_scale():
+    """sigma = 3: the oracle rounds the exact ties z / sigma = +-2.5, +-0.5 half
+    to even (the definition); the kernel multiplies by fp32(1/3), slightly
+    above 1/3, and may land on the other neighbour.  Codes may differ there
+    only, by one, and everywhere else bit for bit."""
+    d, g = 128, 16
+    for bits, qmax in ((4, 7), (8, 127)):
+        vals = [3.0 * qmax, 7.5, -7.5, 10.5, 4.5, 1.5, -1.5, 16.5, -10.5, 0.0, 3.0, -3.0, 6.0, 9.0, 12.0, 4.0]
+        x = np.tile(np.array(vals), (2, 70, 1, d // g)).astype(np.float16).reshape(2, 70, 1, d)
+        codes_g, scales_g = S.quantize(dev(x), None, None, g, bits, "none")
+        codes_o, scales_o, z_o = oracle.quantize(x, None, None, g, bits, "none", return_z=True)
+        assert np.array_equal(host(scales_g).view(np.uint16), scales_o)
+        qg = compare.decode_codes(host(codes_g), bits, d).reshape(-1, g)
+        qo = compare.decode_codes(codes_o, bits, d).reshape(-1, g)
+        diff = np.nonzero((qg != qo).any(axis=0))[0]
+        assert set(diff.tolist()) <= {1, 2, 5, 6}, diff
+        assert np.all(np.abs(qg - qo) <= 1)
+        # every difference sits on an exact tie of the oracle's quotient
+        ratio = z_o.reshape(-1, g) / 3.0
+        assert np.all(np.abs(ratio[qg != qo] % 1.0) == 0.5)
+        print(f"[ties sigma=3 bits={bits}] columns differing: {diff.tolist()}", flush=True)
+
+
 def test_zero_subnormal_and_saturated_groups():
     d, g = 128, 16
     x = np.zeros((1, 66, 2, d), dtype=np.float16)

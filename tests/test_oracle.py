@@ -240,30 +240,33 @@ def test_quantizer_invariants(rot, bits, group):
     q = decode_codes(codes, bits, d)
     sig = scales.view(np.float16).astype(np.float64)
     assert np.all(np.abs(q) <= qmax)
-    # z is the fp32 rounding of lambda * y (the decision input)
+    # z is lambda * y (the decision input), fp64
     y = oracle.rotate(x, s, rot)
-    zref = (lam[:, None].astype(np.float64) * y).astype(np.float32)
+    zref = lam[:, None].astype(np.float64) * y
     # codes, scales and z are head-major [B, H, T, .]; y is [B, T, H, d]
     assert np.array_equal(z, zref.transpose(0, 2, 1, 3))
-    zg = _groups(z.astype(np.float64), group)
+    zg = _groups(z, group)
     qg = _groups(q, group)
     a = np.max(np.abs(zg), axis=-1)
-    # sigma within fp16 + fp32 rounding of a / qmax
-    rel = np.abs(sig - a / qmax) / (a / qmax)
-    assert np.all(rel <= 2.0 ** -11 + 2.0 ** -22)
+    # sigma is numpy's correctly rounded fp16 of a / qmax
+    assert np.array_equal(sig, (a / qmax).astype(np.float16).astype(np.float64))
     # every group reaches the end of the code range
     assert np.all(np.max(np.abs(qg), axis=-1) == qmax)
     # nearest code: |z - q sigma| <= sigma / 2
     err = np.abs(zg - qg * sig[..., None])
-    assert np.all(err <= sig[..., None] * (0.5 + 2.0 ** -20))
-    # brute force over every code value: oracle agrees except at exact ties
+    assert np.all(err <= sig[..., None] * (0.5 + 2.0 ** -40))
+    # brute force over every code value: the oracle's code is the nearest
+    # one, and where two are equally near (an exact tie), the even one
     cand = np.arange(-qmax, qmax + 1, dtype=np.float64)
     dist = np.abs(zg[..., None] - cand * sig[..., None, None])
-    best = cand[np.argmin(dist, axis=-1)]
-    dmin = np.min(dist, axis=-1)
-    dour = np.abs(zg - qg * sig[..., None])
-    mism = best != qg
-    assert np.all(np.isclose(dour[mism], dmin[mism], rtol=1e-6, atol=0))
+    dmin = np.min(dist, axis=-1, keepdims=True)
+    nearest = dist == dmin                                   # one or two candidates
+    n_near = nearest.sum(axis=-1)
+    best = cand[np.argmax(nearest, axis=-1)]
+    single = n_near == 1
+    assert np.array_equal(best[single], qg[single].astype(np.float64))
+    even = np.where(nearest & (cand % 2 == 0), cand, np.inf).min(axis=-1)
+    assert np.array_equal(even[~single], qg[~single].astype(np.float64))
 
 
 def test_quantizer_ties_round_half_even():
@@ -403,10 +406,35 @@ def test_byte_accounting_reproduces_pages_figures():
     assert round(gold["llama3_70b_128k_fp16_GB"] / ratio(64), 1) == gold["llama3_70b_128k_int4_GB"]
 
 
+def test_ties_follow_the_quotient_not_a_reciprocal():
+    """At an exact tie with a scale that is not a power of two, rne(z / sigma)
+    and rne(z * fp32(1 / sigma)) differ: the oracle gives the quotient's
+    answer (round half to even), the definition in the pages' pipeline order
+    (rescale, group absmax, rounding)."""
+    d, g = 16, 16
+    for bits, qmax in ((4, 7), (8, 127)):
+        # rot none, lambda 1, s = +1: z = x exactly; absmax 3 * qmax -> sigma = 3
+        vals = [3.0 * qmax, 7.5, -7.5, 10.5, 4.5, 1.5, -1.5, 16.5, -10.5, 0.0, 3.0, -3.0, 6.0, 9.0, 12.0, 4.0]
+        x = np.array(vals, dtype=np.float16).reshape(1, 1, 1, d)
+        assert np.array_equal(x.astype(np.float64).ravel(), np.array(vals))
+        codes, scales = oracle.quantize(x, None, None, g, bits, "none")
+        assert scales.view(np.float16)[0, 0, 0, 0] == 3.0
+        q = decode_codes(codes, bits, d)[0, 0, 0]
+        quotient = [qmax, 2, -2, 4, 2, 0, 0, 6, -4, 0, 1, -1, 2, 3, 4, 1]   # 4/3 -> 1
+        assert list(q) == quotient
+        # the reciprocal rule rounds the four ties 2.5, -2.5, 0.5 and -0.5 the other way
+        r = np.float64(np.float32(1.0 / 3.0))
+        recip = np.clip(np.rint(np.array(vals) * r), -qmax, qmax).astype(int)
+        differ = np.nonzero(recip != np.array(quotient))[0]
+        assert list(differ) == [1, 2, 5, 6]
+        assert np.all(np.abs(recip[differ] - np.array(quotient)[differ]) == 1)
+
+
 def test_fp32_reciprocal_of_every_fp16_is_correctly_rounded():
-    """The decision uses fp32(1/sigma) taken as one rounding of the double
-    quotient; check it is the correctly rounded fp32 reciprocal for every
-    positive finite fp16 sigma, with exact rational arithmetic."""
+    """A fact about fp16 values that a fast decision rule can rely on: for
+    every positive finite fp16 sigma, one rounding of the double quotient
+    1/sigma to fp32 is the correctly rounded fp32 reciprocal, and 1/sigma is
+    never an fp32 rounding tie (exact rational arithmetic)."""
     from fractions import Fraction
     sig = np.arange(1, 0x7c00, dtype=np.uint16).view(np.float16).astype(np.float64)
     r = (1.0 / sig).astype(np.float32)
