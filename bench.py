@@ -124,13 +124,13 @@ def write_traffic(fetch_csv: str, write_csv: str, workload: str) -> None:
         print(json.dumps(rec))
 
 
-def cpu_baseline(w, x, s, lam, target_s: float = 15.0):
-    """The oracle, as it stands, on the first tokens of every tensor."""
+def _oracle_sample(w, x, s, lam, target_s: float):
+    """The oracle, as it stands, on the first tokens of every tensor (quantize
+    then dequantize), sized by a pilot run to about target_s seconds."""
     import numpy as np
     from oracle import oracle
 
-    # pilot on a small slice to size the sample to ~target_s of CPU work
-    tp = 64
+    tp = 16
     xs = np.ascontiguousarray(x[:, :tp])
     t0 = time.perf_counter()
     c, sc = oracle.quantize(xs, s, lam, w.group, w.bits, "srft")
@@ -143,9 +143,24 @@ def cpu_baseline(w, x, s, lam, target_s: float = 15.0):
     oracle.dequantize(c, sc, s, lam, w.group, w.bits, "srft", d=w.d)
     dt = time.perf_counter() - t0
     nv = w.B * tn * w.H
-    return {"value": nv / dt, "unit": "KV vectors/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"first {tn} tokens of each of the {w.B} tensors ({nv} vectors), "
-                      f"quantize + dequantize, fp64 direct DFT, {dt:.1f} s"}
+    return nv / dt, (f"first {tn} tokens of each of the {w.B} tensors ({nv} vectors), "
+                     f"quantize + dequantize, fp64 direct DFT, {dt:.1f} s")
+
+
+def cpu_baseline(w, x, s, lam, target_s: float = 12.0):
+    """The oracle on all its threads (OpenMP over vectors), then on one core."""
+    from oracle import oracle
+
+    threads = oracle.num_threads()
+    v, sample = _oracle_sample(w, x, s, lam, target_s)
+    oracle.set_num_threads(1)
+    try:
+        v1, sample1 = _oracle_sample(w, x, s, lam, target_s / 2)
+    finally:
+        oracle.set_num_threads(threads)
+    return {"value": v, "unit": "KV vectors/s", "cores": threads, "kind": "oracle", "sample": sample,
+            "host_cpu_count": os.cpu_count(),
+            "one_core": {"value": v1, "unit": "KV vectors/s", "cores": 1, "sample": sample1}}
 
 
 def decode_append_latency(steps: int = 1000, graph_steps: int = 100) -> dict:
@@ -189,13 +204,18 @@ def decode_append_latency(steps: int = 1000, graph_steps: int = 100) -> dict:
     wall = np.array(wall)
     eager_codes, eager_scales = codes.clone(), scales.clone()
 
-    # the same eager steps through a CacheAppender (arguments checked once)
+    # the same eager steps through a CacheAppender (arguments checked once),
+    # into a cleared cache, so that matching rows show the appender wrote them
     app = S.CacheAppender(codes, scales, pos, sd, None, w.group, w.bits)
     pos.zero_()
+    codes.zero_()
+    scales.zero_()
     for i in range(20):
         app(xs[i % graph_steps])
         pos.add_(1)
     pos.zero_()
+    codes.zero_()
+    scales.zero_()
     torch.cuda.synchronize()
     wall_p = []
     for i in range(steps):
@@ -349,6 +369,152 @@ def non_pow2_timing(steps: int) -> dict:
             "vectors_per_s_step": n / ((q_ms + dq_ms) * 1e-3)}
 
 
+def _dist(ms_list) -> dict:
+    """Per-launch times (ms): mean, median and the 10th / 90th percentiles."""
+    import numpy as np
+    a = np.asarray(ms_list, dtype=np.float64)
+    return {"launches": int(a.size), "mean_ms": float(a.mean()), "p50_ms": float(np.percentile(a, 50)),
+            "p10_ms": float(np.percentile(a, 10)), "p90_ms": float(np.percentile(a, 90))}
+
+
+def _direction(ms_list, nvec, d, bpv) -> dict:
+    """Rates of one direction from its per-launch times (median launch)."""
+    t = _dist(ms_list)
+    sec = t["p50_ms"] * 1e-3
+    t.update({"vectors_per_s": nvec / sec, "fp16_GBps": 2 * d * nvec / sec / 1e9,
+              "algo_GBps": bpv * nvec / sec / 1e9, "hbm_frac": bpv * nvec / sec / 1e9 / HBM_PEAK_GBPS})
+    return t
+
+
+def rotating_roundtrip(x, s, lam, group, bits, rot, launches: int, sets: int = 4, settle_s: float = 0.5):
+    """Quantize and dequantize of x fp16 [B,T,H,d] (device) timed per launch
+    with HIP events on the launch stream, over `sets` input / output buffer
+    sets used in turn (every launch reads buffers last touched more than a
+    last-level cache's worth of traffic earlier): step i quantizes set i %
+    sets and dequantizes set (i + sets/2) % sets, written two steps before.
+    Returns (quantize ms list, dequantize ms list, reconstruction rel L2)."""
+    import torch
+
+    from kv_cache_quantization_srft_amd import srftq as S
+
+    B, T, H, d = x.shape
+    xs = [x] + [x.clone() for _ in range(sets - 1)]
+    cs = [torch.empty((B, H, T, d * bits // 8), dtype=torch.uint8, device=x.device) for _ in range(sets)]
+    ss = [torch.empty((B, H, T, d // group), dtype=torch.float16, device=x.device) for _ in range(sets)]
+    os_ = [torch.empty_like(x) for _ in range(sets)]
+    q = lambda k: S.quantize(xs[k], s, lam, group, bits, rot, codes=cs[k], scales=ss[k])
+    dq = lambda k: S.dequantize(cs[k], ss[k], s, lam, group, bits, rot, out=os_[k])
+    for k in range(sets):
+        q(k)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < settle_s or i < 4:
+        q(i % sets)
+        dq((i + sets // 2) % sets)
+        i += 1
+        if i % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(launches)]
+    for i in range(launches):
+        ev[i][0].record()
+        q(i % sets)
+        ev[i][1].record()
+        dq((i + sets // 2) % sets)
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    tq = [e[0].elapsed_time(e[1]) for e in ev]
+    tdq = [e[1].elapsed_time(e[2]) for e in ev]
+    xf = x.float()
+    rel = (torch.linalg.vector_norm(os_[0].float() - xf) / torch.linalg.vector_norm(xf)).item()
+    del xs, cs, ss, os_
+    return tq, tdq, rel
+
+
+def roundtrip_timing(launches: int) -> dict:
+    """The round trip at the 128K-token shape: fp16 [T=131072, H=8, d=128],
+    Student-t(3) values, SRFT, lambda 1, group 16, int4; each direction
+    timed per launch over four rotating buffer sets (1 GiB of inputs)."""
+    import torch
+
+    from kv_cache_quantization_srft_amd import workloads as W
+
+    w = W.WORKLOADS["roundtrip"]
+    x, s = W.generate(w)
+    xd = torch.from_numpy(x).to("cuda:0")              # [1, T, H, d]
+    sd = torch.from_numpy(s).to("cuda:0")
+    del x
+    tq, tdq, rel = rotating_roundtrip(xd, sd, None, w.group, w.bits, "srft", launches)
+    bpv = algorithmic_bytes_per_vector(w.d, w.group, w.bits)
+    return {"workload": f"roundtrip: fp16 [T={w.T}, H={w.H}, d={w.d}], Student-t(3), SRFT, lambda 1, "
+                        f"group {w.group}, int{w.bits}; 4 rotating buffer sets",
+            "vectors": w.nvec, "bytes_per_vector": bpv,
+            "quantize": _direction(tq, w.nvec, w.d, bpv), "dequantize": _direction(tdq, w.nvec, w.d, bpv),
+            "reconstruction_rel_l2": rel}
+
+
+def wide_timing(launches: int) -> dict:
+    """The wide head: fp16 [T=131072, H=4, d=256], lognormal channels with
+    sparse x30 outliers, lambda calibrated per rotation, group 16, int4;
+    SRFT and SRHT each timed per direction (four rotating buffer sets), with
+    the reconstruction error of each (the pages call the two equivalent in
+    quality)."""
+    import torch
+
+    from kv_cache_quantization_srft_amd import srftq as S
+    from kv_cache_quantization_srft_amd import workloads as W
+
+    w = W.WORKLOADS["wide"]
+    x, s = W.generate(w)
+    xd = torch.from_numpy(x).to("cuda:0")
+    sd = torch.from_numpy(s).to("cuda:0")
+    del x
+    bpv = algorithmic_bytes_per_vector(w.d, w.group, w.bits)
+    out = {"workload": f"wide: fp16 [T={w.T}, H={w.H}, d={w.d}], lognormal channels, "
+                       f"lambda calibrated, group {w.group}, int{w.bits}; 4 rotating buffer sets",
+           "vectors": w.nvec, "bytes_per_vector": bpv}
+    for rot in ("srft", "srht"):
+        lam = S.calibrate_lambda(xd, sd, rot)
+        tq, tdq, rel = rotating_roundtrip(xd, sd, lam, w.group, w.bits, rot, launches)
+        out[rot] = {"quantize": _direction(tq, w.nvec, w.d, bpv), "dequantize": _direction(tdq, w.nvec, w.d, bpv),
+                    "reconstruction_rel_l2": rel}
+    return out
+
+
+def tiny_timing(launches: int) -> dict:
+    """The tiny workload, fp16 [T=1024, H=8, d=128] (8,192 vectors, 2 MiB):
+    launch-bound, so microseconds per launch (HIP events), no roofline."""
+    import torch
+
+    from kv_cache_quantization_srft_amd import srftq as S
+    from kv_cache_quantization_srft_amd import workloads as W
+
+    w = W.WORKLOADS["tiny"]
+    x, s = W.generate(w)
+    xd = torch.from_numpy(x).to("cuda:0")
+    sd = torch.from_numpy(s).to("cuda:0")
+    codes, scales = S.quantize(xd, sd, None, w.group, w.bits)
+    xhat = S.dequantize(codes, scales, sd, None, w.group, w.bits)
+    for _ in range(50):
+        S.quantize(xd, sd, None, w.group, w.bits, codes=codes, scales=scales)
+        S.dequantize(codes, scales, sd, None, w.group, w.bits, out=xhat)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(launches)]
+    for i in range(launches):
+        ev[i][0].record()
+        S.quantize(xd, sd, None, w.group, w.bits, codes=codes, scales=scales)
+        ev[i][1].record()
+        S.dequantize(codes, scales, sd, None, w.group, w.bits, out=xhat)
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    us = lambda a: {k.replace("_ms", "_us"): (v * 1e3 if k.endswith("_ms") else v) for k, v in _dist(a).items()}
+    return {"workload": f"tiny: fp16 [T={w.T}, H={w.H}, d={w.d}], SRFT, lambda 1, group {w.group}, int{w.bits}",
+            "vectors": w.nvec,
+            "quantize": us([e[0].elapsed_time(e[1]) for e in ev]),
+            "dequantize": us([e[1].elapsed_time(e[2]) for e in ev])}
+
+
 MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix-core peak
 
 
@@ -492,55 +658,65 @@ def main():
     torch.cuda.synchronize()
     lam_h = lam.cpu().numpy() if lam is not None else None
 
-    # head-major quantized cache [B, H, T, .]
-    codes = torch.empty((w.B, w.H, w.T, w.d * w.bits // 8), dtype=torch.uint8, device=dev)
-    scales = torch.empty((w.B, w.H, w.T, w.d // w.group), dtype=torch.float16, device=dev)
+    # head-major quantized cache [B, H, T, .], two sets used in turn: step i
+    # quantizes the batch into set i % 2 and dequantizes set (i + 1) % 2,
+    # which the previous step wrote (2.5 GB of traffic ago, so dequantize
+    # reads its codes from HBM, as from a cache written earlier)
+    codes2 = [torch.empty((w.B, w.H, w.T, w.d * w.bits // 8), dtype=torch.uint8, device=dev) for _ in range(2)]
+    scales2 = [torch.empty((w.B, w.H, w.T, w.d // w.group), dtype=torch.float16, device=dev) for _ in range(2)]
+    codes, scales = codes2[0], scales2[0]
     xhat = torch.empty_like(xd)
 
-    def step(ev=None):
+    def step(i, ev=None, rot="srft"):
         if ev is not None:
             ev[0].record()
-        S.quantize(xd, sd, lam, w.group, w.bits, codes=codes, scales=scales)
+        S.quantize(xd, sd, lam, w.group, w.bits, rot, codes=codes2[i % 2], scales=scales2[i % 2])
         if ev is not None:
             ev[1].record()
-        S.dequantize(codes, scales, sd, lam, w.group, w.bits, out=xhat)
+        S.dequantize(codes2[(i + 1) % 2], scales2[(i + 1) % 2], sd, lam, w.group, w.bits, rot, out=xhat)
         if ev is not None:
             ev[2].record()
 
+    S.quantize(xd, sd, lam, w.group, w.bits, codes=codes2[1], scales=scales2[1])
     # the GPU's clocks need a sustained load to settle (the first ~100 calls of
     # a kernel run up to 15 % slower): untimed steps for settle_s seconds
     t_settle = time.perf_counter()
     n_settle = 0
     while time.perf_counter() - t_settle < args.settle_s:
         for _ in range(10):
-            step()
+            step(n_settle)
+            n_settle += 1
         torch.cuda.synchronize()
-        n_settle += 10
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(n_settle + i)
     torch.cuda.synchronize()
+    i0 = n_settle + args.warmup
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for i in range(args.steps):
-        step(evs[i])
+        step(i0 + i, evs[i])
     stop.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
-    q_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    dq_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    tq = [e[0].elapsed_time(e[1]) for e in evs]
+    tdq = [e[1].elapsed_time(e[2]) for e in evs]
+    q_ms = sum(tq) / args.steps
+    dq_ms = sum(tdq) / args.steps
     ms_step = total_ms / args.steps
+    # the last step dequantized the set quantized the step before, from the same x
+    rel = (torch.linalg.vector_norm(xhat.float() - xd.float()) / torch.linalg.vector_norm(xd.float())).item()
 
     nvec = w.nvec
     bpv = algorithmic_bytes_per_vector(w.d, w.group, w.bits)
     per_kernel = {
         "quantize": {"ms": q_ms, "vectors_per_s": nvec / (q_ms * 1e-3),
                      "fp16_GBps": 2 * w.d * nvec / (q_ms * 1e-3) / 1e9,
-                     "algo_GBps": bpv * nvec / (q_ms * 1e-3) / 1e9},
+                     "algo_GBps": bpv * nvec / (q_ms * 1e-3) / 1e9, **_dist(tq)},
         "dequantize": {"ms": dq_ms, "vectors_per_s": nvec / (dq_ms * 1e-3),
                        "fp16_GBps": 2 * w.d * nvec / (dq_ms * 1e-3) / 1e9,
-                       "algo_GBps": bpv * nvec / (dq_ms * 1e-3) / 1e9},
+                       "algo_GBps": bpv * nvec / (dq_ms * 1e-3) / 1e9, **_dist(tdq)},
     }
     for k in per_kernel.values():
         k["hbm_frac"] = k["algo_GBps"] / HBM_PEAK_GBPS
@@ -551,6 +727,27 @@ def main():
                 "frac": per_kernel[dom]["algo_GBps"] / HBM_PEAK_GBPS,
                 "traffic": traffic,
                 "bytes_per_vector": bpv, "vectors_per_launch": nvec}
+
+    # the same kernels with no rotation (rot none: loads, quantizer, stores):
+    # the memory path's own floor at this shape, for comparison
+    floor = None
+    if not args.no_decode:
+        fl = max(20, args.steps // 4)
+        for i in range(4):
+            step(i, rot="none")
+        torch.cuda.synchronize()
+        fev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(fl)]
+        for i in range(fl):
+            step(i, fev[i], rot="none")
+        torch.cuda.synchronize()
+        fq = _dist([e[0].elapsed_time(e[1]) for e in fev])
+        fdq = _dist([e[1].elapsed_time(e[2]) for e in fev])
+        floor = {"what": "the same workload with rot none: tile loads, lambda, quantizer and stores, "
+                         "no transform", "quantize": fq, "dequantize": fdq,
+                 "quantize_hbm_frac": bpv * nvec / (fq["mean_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                 "dequantize_hbm_frac": bpv * nvec / (fdq["mean_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+        step(0)            # leave set 0 holding the SRFT codes (decode attention reads it)
+        torch.cuda.synchronize()
 
     # plain copy kernel of the quantize input's size (fp16 negate: reads and
     # writes 2*d bytes per vector): achievable-bandwidth reference, and the
@@ -569,16 +766,20 @@ def main():
     copy_ms = c0.elapsed_time(c1) / args.steps
     copy_probe = {"bytes_read": src.numel() * 2, "bytes_written": dst.numel() * 2, "ms": copy_ms,
                   "GBps": 2 * src.numel() * 2 / (copy_ms * 1e-3) / 1e9}
-    del dst
+    del dst, src
 
-    # sanity: reconstruction error of the round trip
-    rel = (torch.linalg.vector_norm(xhat.float() - xd.float()) / torch.linalg.vector_norm(xd.float())).item()
-
+    del codes2[1], scales2[1]
     dec = None if args.no_decode else decode_append_latency()
     attn = None if args.no_decode else decode_attention_timing(w, codes, scales, sd, lam, args.steps)
     d96 = None if args.no_decode else non_pow2_timing(min(args.steps, 50))
     del xhat
     hh = None if args.no_decode else householder_timing(min(args.steps, 20))
+    del xd, codes, scales, codes2, scales2
+    torch.cuda.empty_cache()
+    launches = max(100, args.steps)
+    c5 = None if args.no_decode else roundtrip_timing(launches)
+    c4 = None if args.no_decode else wide_timing(launches)
+    tiny = None if args.no_decode else tiny_timing(launches)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -610,8 +811,13 @@ def main():
         "fp16_in_GBps_quantize": per_kernel["quantize"]["fp16_GBps"],
         "hbm_peak_frac_quantize": per_kernel["quantize"]["hbm_frac"],
         "hbm_peak_frac_dequantize": per_kernel["dequantize"]["hbm_frac"],
-        "step": "srftq_quantize then srftq_dequantize of every vector (one launch each)",
+        "step": "srftq_quantize of the batch into one of two code sets, then srftq_dequantize of "
+                "the set the previous step wrote (one launch each)",
         "reconstruction_rel_l2": rel,
+        "rot_none_floor": floor,
+        "roundtrip_128k": c5,
+        "wide_d256": c4,
+        "tiny_launch": tiny,
         "decode_append": dec,
         "decode_attention": attn,
         "non_pow2_d96": d96,

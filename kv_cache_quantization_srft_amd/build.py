@@ -1,6 +1,6 @@
 """Build libsrftq.so (HIP kernels for gfx950 + the C ABI) in the package dir.
 
-    python -m kv_cache_quantization_srft_amd.build [--jobs N]
+    python -m kv_cache_quantization_srft_amd.build [--jobs N] [--incremental]
 
 Each translation unit is compiled by hipcc in parallel, then linked into one
 shared library next to this file.
@@ -33,36 +33,58 @@ def sources():
     return sorted(f for f in os.listdir(CSRC) if f.endswith(".hip") or f.endswith(".cpp"))
 
 
-# Development only: a comma-separated list of name fragments (e.g. "d256")
-# whose already-built objects are linked as they are instead of recompiled.
-# Unset (the default), every unit is compiled.
-_REUSE = [f for f in os.environ.get("SRFTQ_REUSE_OBJECTS", "").split(",") if f]
+def _deps(obj: str) -> list[str]:
+    """Files an object was built from, as the compiler's -MMD output lists them."""
+    dep = obj + ".d"
+    if not os.path.exists(dep):
+        return []
+    text = open(dep).read().replace("\\\n", " ")
+    body = text.split(":", 1)[1] if ":" in text else ""
+    return [f for f in body.split() if f]
 
 
-def _compile(src: str) -> str:
+def _up_to_date(src: str, obj: str, flags: list[str]) -> bool:
+    """make's rule: the object is newer than its source and every header the
+    compiler read for it, and was built with the same flags."""
+    if not os.path.exists(obj) or not os.path.exists(obj + ".flags"):
+        return False
+    if open(obj + ".flags").read() != " ".join(flags):
+        return False
+    deps = _deps(obj)
+    if not deps:
+        return False
+    t = os.path.getmtime(obj)
+    return all(os.path.exists(f) and os.path.getmtime(f) <= t for f in deps + [src])
+
+
+def _compile(src: str, incremental: bool = False) -> str:
     obj = os.path.join(BUILD, src + ".o")
-    if any(f in src for f in _REUSE) and os.path.exists(obj):
-        return obj
     path = os.path.join(CSRC, src)
     flags = DEVICE_FLAGS if src.endswith(".hip") else HOST_FLAGS
     if src.startswith("k_attn"):
         # MFMA results in VGPRs: the attention kernels read every score tile
         # back for VALU work, which AGPR results would have to copy first
         flags = flags + ["-mllvm", "-amdgpu-mfma-vgpr-form"]
-    cmd = [HIPCC] + flags + ["-c", path, "-o", obj]
+    if incremental and _up_to_date(path, obj, flags):
+        return obj
+    cmd = [HIPCC] + flags + ["-MMD", "-MF", obj + ".d", "-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    with open(obj + ".flags", "w") as f:
+        f.write(" ".join(flags))
     return obj
 
 
-def build(jobs: int | None = None, verbose: bool = False) -> str:
+def build(jobs: int | None = None, verbose: bool = False, incremental: bool = False) -> str:
+    """Compile every unit (incremental: only those whose object is older
+    than the source or a header it includes) and link libsrftq.so."""
     os.makedirs(BUILD, exist_ok=True)
     # the d = 256 units take several times longer: start them first
     srcs = sorted(sources(), key=lambda f: (0 if "d256" in f else 1, f))
     jobs = jobs or min(len(srcs), os.cpu_count() or 4, 16)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
+        objs = list(ex.map(lambda f: _compile(f, incremental), srcs))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -77,6 +99,8 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=None)
+    ap.add_argument("--incremental", action="store_true",
+                    help="recompile only units whose source or included headers changed")
     a = ap.parse_args()
-    build(a.jobs, verbose=True)
+    build(a.jobs, verbose=True, incremental=a.incremental)
     sys.exit(0)

@@ -2,6 +2,7 @@
 // the host, then dispatch to the per-head-size kernel translation units.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdlib>
 #include <mutex>
 #include <unordered_map>
@@ -11,16 +12,18 @@
 
 namespace srftq {
 
+// Per-device cache; concurrent first calls from several host threads may
+// both query the device, and store the same value.
 int device_cu_count() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
-  if (cache[dev] <= 0) {
-    int n = 0;
+  int n = cache[dev].load(std::memory_order_acquire);
+  if (n <= 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 1;
-    cache[dev] = n;
+    cache[dev].store(n, std::memory_order_release);
   }
-  return cache[dev];
+  return n;
 }
 
 const int8_t* plus_ones_ptr();   // defined with the device array in ones.hip
@@ -62,11 +65,14 @@ srftq_status validate(const srftq_shape* s) {
   // (the Walsh-Hadamard matrix and the paired complex FFT need a power of two)
   if (s->d == 96 && (s->rot == SRFTQ_ROT_SRHT || (s->rot == SRFTQ_ROT_SRFT && s->variant == 2)))
     return SRFTQ_ERR_UNSUPPORTED;
-  // 32-bit tile counters and per-lane byte offsets
+  // 32-bit tile counters and per-lane byte offsets; every product below is
+  // bounded before it is formed (B*H < 2^31, so B*H*d < 2^39)
   if (s->H > 65535) return SRFTQ_ERR_SHAPE;
-  const int64_t tiles_t = (s->T + 63) / 64;
-  if (s->B > 0 && tiles_t > 0 && (s->B * (int64_t)s->H) > (int64_t)0x7fffffff / tiles_t) return SRFTQ_ERR_SHAPE;
-  if (s->B > 0 && s->T > (int64_t)0x7fffffffffffLL / (s->B * (int64_t)s->H * s->d)) return SRFTQ_ERR_SHAPE;
+  if (s->B > (int64_t)0x7fffffff / s->H) return SRFTQ_ERR_SHAPE;
+  const int64_t BH = s->B * (int64_t)s->H;
+  const int64_t tiles_t = s->T / 32 + (s->T % 32 != 0);   // the smallest tiles (d = 256)
+  if (BH > 0 && tiles_t > (int64_t)0x7fffffff / BH) return SRFTQ_ERR_SHAPE;
+  if (BH > 0 && s->T > (int64_t)0x7fffffffffffLL / (BH * s->d)) return SRFTQ_ERR_SHAPE;
   return SRFTQ_OK;
 }
 
@@ -108,6 +114,7 @@ srftq_status check_side(const int8_t* signs, const float* lambda) {
 // (the same bound validate() puts on T).
 srftq_status validate_cache(const srftq_shape* s, int64_t t_cap) {
   if (t_cap < 0) return SRFTQ_ERR_SHAPE;
+  if (s->B > (int64_t)0x7fffffff / s->H) return SRFTQ_ERR_SHAPE;   // as validate(): B*H < 2^31
   if (s->B > 0 && t_cap > (int64_t)0x7fffffffffffLL / (s->B * (int64_t)s->H * s->d)) return SRFTQ_ERR_SHAPE;
   return SRFTQ_OK;
 }

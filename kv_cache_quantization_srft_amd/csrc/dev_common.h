@@ -142,6 +142,21 @@ __device__ __forceinline__ const_ptr<T> as_const(const T* p) {
   return (const_ptr<T>)(p);
 }
 
+// v_permlane32_swap on a register pair (X, Y): lanes 0..31 end with
+// (their own X, lane l+32's X), lanes 32..63 with (lane l-32's Y, their own
+// Y) -- a 2 x 2 transpose between the wave's halves and the two registers.
+__device__ __forceinline__ void swap32(uint32_t& x, uint32_t& y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, y, false, false);
+  x = r[0];
+  y = r[1];
+}
+__device__ __forceinline__ void swap32(float& x, float& y) {
+  uint32_t a = as_u32(x), b = as_u32(y);
+  swap32(a, b);
+  x = as_f32(a);
+  y = as_f32(b);
+}
+
 // Uniform value -> scalar register.
 __device__ __forceinline__ int uniform_i32(int v) { return __builtin_amdgcn_readfirstlane(v); }
 

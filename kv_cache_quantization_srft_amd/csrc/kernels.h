@@ -130,7 +130,7 @@ __device__ __forceinline__ int64_t cache_row(const Geo& a, int bh, int64_t t) {
 // every instruction reads whole rows, i.e. full cache lines.  The per-lane
 // source offsets depend on i only through i mod kPat and are computed once.
 // ----------------------------------------------------------------------------
-template <int ROWB>
+template <int ROWB, int NR = 64>
 struct RowTile {
   static_assert(ROWB == 2 || ROWB == 4 || ROWB == 8 || ROWB == 16 || ROWB == 32 || ROWB == 64 ||
                     ROWB == 128 || ROWB == 256 || ROWB == 512,
@@ -142,9 +142,11 @@ struct RowTile {
   static constexpr int kSlot = kElem < 4 ? 4 : kElem;
   static constexpr int kEpr = ROWB / kElem;                          // DMA elements per row
   static constexpr int kRpi = 64 / kEpr;                             // rows per instruction
-  static constexpr int kInst = kEpr;                                 // instructions per tile
+  // instructions per tile of NR rows (rows past NR, when one instruction
+  // covers more, re-read the tile's last row into slots past the tile)
+  static constexpr int kInst = NR * kEpr >= 64 ? NR * kEpr / 64 : 1;
   static constexpr int kRowLds = kEpr * kSlot;                       // LDS bytes per row
-  static constexpr int kBytes = 64 * kRowLds;
+  static constexpr int kBytes = (NR > kRpi ? NR : kRpi) * kRowLds;
   static constexpr int kCpr = kWide ? ROWB / 16 : 1;
   static constexpr int kPat = !kWide ? 1 : kCpr <= 4 ? 1 : kCpr == 8 ? 2 : kCpr == 16 ? 4 : 8;
 
@@ -170,7 +172,7 @@ struct RowTile {
     uint32_t off[kPat];
     __device__ __forceinline__ void init(int lane, uint32_t rsb) {
 #pragma unroll
-      for (int m = 0; m < kPat; ++m) off[m] = src_offset(lane, m, rsb, 64);
+      for (int m = 0; m < kPat; ++m) off[m] = src_offset(lane, m, rsb, NR);
     }
   };
 
@@ -179,7 +181,7 @@ struct RowTile {
   __device__ static __forceinline__ void issue(const uint8_t* base, uint32_t rsb, int nv, int lane,
                                                const Plan& plan, uint8_t* lds) {
     const uint32_t l0 = lds_addr(lds);
-    if (nv == 64) {
+    if (nv == NR) {
 #pragma unroll
       for (int i = 0; i < kInst; ++i) {
         const uint8_t* g = base + (size_t)(i / kPat) * (size_t)(kPat * kRpi) * rsb;

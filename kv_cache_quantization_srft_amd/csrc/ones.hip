@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace srftq {
 
 __device__ __attribute__((aligned(16))) int8_t g_plus_ones[256] = {
@@ -15,17 +17,18 @@ __device__ __attribute__((aligned(16))) int8_t g_plus_ones[256] = {
 #undef SRFTQ_ONE8
 };
 
-// Address of g_plus_ones on the current device (cached per device).
+// Address of g_plus_ones on the current device (cached per device; threads
+// racing on a device's first call look up and store the same address).
 const int8_t* plus_ones_ptr() {
-  static void* cache[64] = {nullptr};
+  static std::atomic<void*> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-  if (!cache[dev]) {
-    void* p = nullptr;
+  void* p = cache[dev].load(std::memory_order_acquire);
+  if (!p) {
     if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_plus_ones)) != hipSuccess) return nullptr;
-    cache[dev] = p;
+    cache[dev].store(p, std::memory_order_release);
   }
-  return (const int8_t*)cache[dev];
+  return (const int8_t*)p;
 }
 
 }  // namespace srftq

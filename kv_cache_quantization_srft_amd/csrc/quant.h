@@ -11,6 +11,11 @@
 // rounded and the product exact.  r is within 2^-24 (relative) of 1/sigma,
 // so q can differ from rne(z / sigma), by +-1, only where z / sigma lies
 // within that distance (plus the rotation's fp32 error) of a half-integer.
+// In fact the exact product z * r rounds differently from z / sigma only at
+// exact ties z = (q + 1/2) sigma (elsewhere z / sigma is more than r's error
+// away from a half-integer); without a rotation (fp16 inputs, where such
+// ties are common) one exact residual per code finds them, and q =
+// rne(z / sigma) exactly.
 //
 // Implementation notes (gfx950):
 //   - The transform leaves y unscaled; the per-coordinate scale c_j is
@@ -98,28 +103,46 @@ __device__ __forceinline__ uint32_t pack_codes(const uint32_t* t) {
   }
 }
 
-// Quantize one vector.  y: unscaled transform output (packed order).
-// lam: the head's lambda row in LDS (read broadcast) or unused.
-template <int D, int G, int BITS, int ROT, int VAR, bool LAM>
+// Whether group g of width G holds a coordinate with the edge scale.
+template <class Sc, int G>
+constexpr bool group_has_edge(int g) {
+  for (int j = g * G; j < (g + 1) * G; ++j)
+    if (Sc::is_edge(j)) return true;
+  return false;
+}
+
+// Quantize one vector (or, with two lanes per vector, a lane's D of its
+// coordinates).  y: unscaled transform output (packed order).  lam: the
+// lambda values of these coordinates in LDS (read broadcast) or unused.
+// Sc: the per-coordinate scales (is_edge, kFwdBulk, kFwdEdge).  Coordinates
+// from NEG_FROM on hold negated values: their groups take sigma from |y| as
+// the others and round y * (neg * r), neg = -1 where they are negated.
+// XLANE: the one group (G = D) continues in the partner lane (l +- 32),
+// whose absmax joins this lane's.
+template <int D, int G, int BITS, int ROT, int VAR, bool LAM, class Sc = Scales<D, ROT, VAR>, int NEG_FROM = D,
+          bool XLANE = false>
 __device__ __forceinline__ void quantize_tail(float (&y)[D], const float* __restrict__ lam,
                                               uint32_t (&codes)[CodeWords<D, BITS>::kWords],
-                                              uint32_t (&scales)[ScaleWords<D, G>::kWords]) {
-  using Sc = Scales<D, ROT, VAR>;
+                                              uint32_t (&scales)[ScaleWords<D, G>::kWords],
+                                              float neg = 1.0f) {
   using Q = QConst<BITS>;
+  static_assert(NEG_FROM % G == 0, "negated coordinates fill whole groups");
   constexpr int NG = D / G;
   constexpr float cB = (float)Sc::kFwdBulk;
   constexpr float cE = (float)Sc::kFwdEdge;
 
   if constexpr (LAM) {
-    // z = lambda * y group by group; the next group's lambda (LDS
-    // broadcast) is requested before this group's multiplies, so the LDS
-    // latency overlaps them instead of stalling each read.
-    static_assert(G % 4 == 0, "lambda groups are read four floats at a time");
-    float lc[G], ln[G];
-    auto fetch = [&](float (&dst)[G], int g) {
-      static_for<G / 4>([&](auto qq) {
+    // z = lambda * y, C coordinates at a time; the next block's lambda (LDS
+    // broadcast) is requested before this block's multiplies, so the LDS
+    // latency overlaps them instead of stalling each read.  C is at most 16
+    // whatever the group size, which bounds the registers this takes.
+    constexpr int C = G < 16 ? G : 16;
+    static_assert(C % 4 == 0 && D % C == 0, "lambda blocks are read four floats at a time");
+    float lc[C], ln[C];
+    auto fetch = [&](float (&dst)[C], int i) {
+      static_for<C / 4>([&](auto qq) {
         constexpr int q = decltype(qq)::value;
-        const float4 v = *(const float4*)(lam + g * G + 4 * q);
+        const float4 v = *(const float4*)(lam + i * C + 4 * q);
         dst[4 * q + 0] = v.x;
         dst[4 * q + 1] = v.y;
         dst[4 * q + 2] = v.z;
@@ -127,20 +150,22 @@ __device__ __forceinline__ void quantize_tail(float (&y)[D], const float* __rest
       });
     };
     fetch(lc, 0);
-    static_for<NG>([&](auto gg) {
-      constexpr int g = decltype(gg)::value;
-      if constexpr (g + 1 < NG) fetch(ln, g + 1);
-      static_for<G>([&](auto kk) {
+    static_for<D / C>([&](auto ii) {
+      constexpr int i = decltype(ii)::value;
+      if constexpr (i + 1 < D / C) fetch(ln, i + 1);
+      static_for<C>([&](auto kk) {
         constexpr int k = decltype(kk)::value;
-        y[g * G + k] = y[g * G + k] * lc[k];
+        y[i * C + k] = y[i * C + k] * lc[k];
       });
-      if constexpr (g + 1 < NG) {
-        static_for<G>([&](auto kk) { lc[decltype(kk)::value] = ln[decltype(kk)::value]; });
+      if constexpr (i + 1 < D / C) {
+        static_for<C>([&](auto kk) { lc[decltype(kk)::value] = ln[decltype(kk)::value]; });
       }
     });
   }
 
   float rB[NG], rE[NG];
+  // rot none's exact decision: sigma and 2^26/sigma per group
+  [[maybe_unused]] float sgs[NG], rts[NG];
   uint32_t need_clamp = 0;
   static_for<(NG + 1) / 2>([&](auto pp) {
     constexpr int g0 = 2 * decltype(pp)::value;
@@ -156,8 +181,14 @@ __device__ __forceinline__ void quantize_tail(float (&y)[D], const float* __rest
           mb = __builtin_fmaxf(mb, __builtin_fabsf(y[j]));
       });
       float a = mb * cB;
-      constexpr bool has_edge = Sc::is_edge(g * G) || (Sc::kEdges && (g * G <= D / 2) && (D / 2 < (g + 1) * G));
+      constexpr bool has_edge = group_has_edge<Sc, G>(g);
       if constexpr (has_edge) a = __builtin_fmaxf(a, me * cE);
+      if constexpr (XLANE) {
+        static_assert(G == D, "a group shared by the lane pair is the lanes' whole half");
+        float u = a, v = a;
+        swap32(u, v);   // both lanes: (lane 0's a, lane 1's a)
+        a = __builtin_fmaxf(u, v);
+      }
       const float tt = a * Q::kQinv;
       need_clamp |= (tt > 65504.0f) ? 1u : 0u;
       t[decltype(ii)::value] = __builtin_fminf(tt, 65504.0f);
@@ -174,7 +205,12 @@ __device__ __forceinline__ void quantize_tail(float (&y)[D], const float* __rest
       const float sg = ii == 0 ? hlo(sw) : hhi(sw);
       // sigma subnormal (and nonzero): rounding alone may leave the range
       need_clamp |= (sg != 0.0f && sg < 6.103515625e-05f) ? 1u : 0u;
-      const float r = sg == 0.0f ? 0.0f : recip_f16_value(sg);
+      float r = sg == 0.0f ? 0.0f : recip_f16_value(sg);
+      if constexpr (g * G >= NEG_FROM) r *= neg;
+      if constexpr (ROT == ROT_NONE) {
+        sgs[g] = sg;
+        rts[g] = r * 67108864.0f;
+      }
       rB[g] = r * cB;
       rE[g] = r * cE;
     });
@@ -192,6 +228,27 @@ __device__ __forceinline__ void quantize_tail(float (&y)[D], const float* __rest
         constexpr int g = j / G;
         const float r = Sc::is_edge(j) ? rE[g] : rB[g];
         uint32_t b = as_u32(__builtin_fmaf(y[j], r, magic));
+        if constexpr (ROT == ROT_NONE) {
+          // Without a rotation the inputs are fp16 values, and exact ties
+          // z = (q + 1/2) sigma are common.  The fma takes z * r exactly, so
+          // rne(z * r) can differ from rne(z / sigma) only at an exact tie:
+          // elsewhere z / sigma lies at least one ulp of z (> 2^-24
+          // relative) from a half-integer, farther than r's relative error
+          // (< 2^-24).  At a tie the residual e = z - q sigma is exact and
+          // equals +-sigma/2; adding +-1/2 to the magic-biased value then
+          // lands on the midpoint, and the fp32 rounding takes the even code.
+          // The tie test is arithmetic (no compare): off a tie ||e| - sigma/2|
+          // is at least sigma 2^-24, which 2^26 / sigma lifts past 1/2, so
+          // the clamped 1/2 - ||e| - sigma/2| 2^26 / sigma is 1/2 exactly at
+          // a tie and 0 elsewhere.
+          // (sigma = 0 needs no case of its own: f = magic then, and adding
+          // +-1/2 rounds back to the even code 0.)
+          const float f = as_f32(b);
+          const float e = __builtin_fmaf(-(f - magic), sgs[g], y[j]);
+          const float m = __builtin_fmaf(-0.5f, sgs[g], __builtin_fabsf(e));
+          const float ind = __builtin_amdgcn_fmed3f(__builtin_fmaf(-__builtin_fabsf(m), rts[g], 0.5f), 0.0f, 1.0f);
+          b = as_u32(f + __builtin_copysignf(ind, e));
+        }
         if constexpr (CLAMP) {
           // signed compare: huge negative products give negative bit patterns
           int bi = (int)b;
@@ -202,6 +259,9 @@ __device__ __forceinline__ void quantize_tail(float (&y)[D], const float* __rest
         t[decltype(ii)::value] = b;
       });
       codes[w] = pack_codes<BITS>(t);
+      // one code word's temporaries at a time (the exact decision's
+      // residuals would otherwise be scheduled for many words at once)
+      if constexpr (ROT == ROT_NONE) __builtin_amdgcn_sched_barrier(0);
     });
   };
   if (__builtin_amdgcn_ballot_w64(need_clamp != 0) == 0) {
@@ -214,12 +274,14 @@ __device__ __forceinline__ void quantize_tail(float (&y)[D], const float* __rest
 // Dequantizer head: codes + scales of one vector -> coordinates multiplied
 // by sigma_G * e_j / lambda_j, where e_j is the inverse transform's input
 // scale.  lam: table of e_j / lambda_j for the head (LAM) or unused.
-template <int D, int G, int BITS, int ROT, int VAR, bool LAM>
+// Sc and NEG_FROM as for quantize_tail: the coordinates from NEG_FROM on are
+// produced negated (their group scales are multiplied by neg).
+template <int D, int G, int BITS, int ROT, int VAR, bool LAM, class Sc = Scales<D, ROT, VAR>, int NEG_FROM = D>
 __device__ __forceinline__ void dequantize_head(const uint32_t (&codes)[CodeWords<D, BITS>::kWords],
                                                 const uint32_t (&scales)[ScaleWords<D, G>::kWords],
-                                                const float* __restrict__ lam, float (&y)[D]) {
-  using Sc = Scales<D, ROT, VAR>;
+                                                const float* __restrict__ lam, float (&y)[D], float neg = 1.0f) {
   constexpr int NG = D / G;
+  static_assert(NEG_FROM % G == 0, "negated coordinates fill whole groups");
   constexpr float eB = (float)Sc::kInvBulk;
   constexpr float eE = (float)Sc::kInvEdge;
   constexpr float off = BITS == 4 ? 8.0f : 128.0f;
@@ -228,6 +290,7 @@ __device__ __forceinline__ void dequantize_head(const uint32_t (&codes)[CodeWord
   static_for<NG>([&](auto gg) {
     constexpr int g = decltype(gg)::value;
     sg[g] = (g % 2 == 0) ? hlo(scales[g / 2]) : hhi(scales[g / 2]);
+    if constexpr (g * G >= NEG_FROM) sg[g] *= neg;
   });
 
   // u = q + off as fp32, exactly: bytes of (codes ^ bias) -> v_cvt_f32_ubyteN

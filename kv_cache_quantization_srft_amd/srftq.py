@@ -240,6 +240,28 @@ def _req(t, dtype, name):
     return t
 
 
+def _head_rows(t, B, H, d, name, flat_ok=False, device=None):
+    """signs / lambda must hold one row of d per (tensor, head): [B, H, d]
+    (or [H, d] when B == 1 and flat_ok), on the data's device; the kernels
+    index them as [B, H, d], so a shorter tensor would be read past its end."""
+    if t is None:
+        return None
+    want = (B, H, d)
+    ok = tuple(t.shape) == want or (flat_ok and B == 1 and tuple(t.shape) == (H, d))
+    if not ok:
+        raise ValueError(f"{name} must have shape {want}" + (f" or {(H, d)}" if flat_ok and B == 1 else "")
+                         + f", got {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the data on {device}")
+    return t
+
+
+def _same_device(device, **tensors):
+    for name, t in tensors.items():
+        if t is not None and t.device != device:
+            raise ValueError(f"{name} is on {t.device}, the data on {device}")
+
+
 def _cache_lead(x):
     """Leading dims of the head-major cache for x [B,T,H,d] / [T,H,d]."""
     if x.dim() == 4:
@@ -269,9 +291,12 @@ def quantize(x, signs=None, lam=None, group=16, bits=4, rot="srft", variant="def
     _req(x, torch.float16, "x")
     _req(signs, torch.int8, "signs")
     _req(lam, torch.float32, "lambda")
+    _head_rows(signs, B, H, d, "signs", x.dim() == 3, x.device)
+    _head_rows(lam, B, H, d, "lambda", x.dim() == 3, x.device)
     lead = _cache_lead(x)
     codes = _out(codes, lead + (d * bits // 8,), torch.uint8, x.device, "codes")
     scales = _out(scales, lead + (max(d // max(group, 1), 1),), torch.float16, x.device, "scales")
+    _same_device(x.device, codes=codes, scales=scales)
     sh = make_shape(B, T, H, d, group, bits, rot, variant)
     _check(srftq_quantize(sh, x, signs, lam, codes, scales, stream), "srftq_quantize")
     return codes, scales
@@ -296,10 +321,20 @@ def dequantize(codes, scales, signs=None, lam=None, group=16, bits=4, rot="srft"
         oshape = (B, T, H, d)
     else:
         raise ValueError("codes must be [H,T,*] or [B,H,T,*]")
+    _check_scales(scales, codes.shape[:-1], d, group)
+    _head_rows(signs, B, H, d, "signs", codes.dim() == 3, codes.device)
+    _head_rows(lam, B, H, d, "lambda", codes.dim() == 3, codes.device)
     out = _out(out, oshape, torch.float16, codes.device, "out")
+    _same_device(codes.device, scales=scales, out=out)
     sh = make_shape(B, T, H, d, group, bits, rot, variant)
     _check(srftq_dequantize(sh, codes, scales, signs, lam, out, stream), "srftq_dequantize")
     return out
+
+
+def _check_scales(scales, lead, d, group):
+    want = tuple(lead) + (max(d // max(group, 1), 1),)
+    if tuple(scales.shape) != want:
+        raise ValueError(f"scales must have shape {want}, got {tuple(scales.shape)}")
 
 
 def _cache_dims(codes, scales, d, bits, group, name="codes"):
@@ -336,6 +371,9 @@ def cache_append(x, codes, scales, pos=None, signs=None, lam=None, group=16, bit
         raise ValueError(f"cache is for B={Bc}, H={Hc}; x has B={B}, H={H}")
     if pos is not None and tuple(pos.shape) != (B,):
         raise ValueError(f"pos must have shape ({B},)")
+    _head_rows(signs, B, H, d, "signs", device=x.device)
+    _head_rows(lam, B, H, d, "lambda", device=x.device)
+    _same_device(x.device, codes=codes, scales=scales, pos=pos)
     sh = make_shape(B, T, H, d, group, bits, rot, variant)
     _check(srftq_cache_append(sh, t_cap, pos, x, signs, lam, codes, scales, stream), "srftq_cache_append")
     return codes, scales
@@ -365,6 +403,10 @@ class CacheAppender:
         B, H, t_cap = _cache_dims(codes, scales, d, bits, group)
         if tuple(pos.shape) != (B,):
             raise ValueError(f"pos must have shape ({B},)")
+        _head_rows(signs, B, H, d, "signs", device=codes.device)
+        _head_rows(lam, B, H, d, "lambda", device=codes.device)
+        _same_device(codes.device, scales=scales, pos=pos)
+        self._device = codes.device
         self._shape = make_shape(B, int(tokens), H, d, group, bits, rot, variant)
         st = srftq_validate(self._shape)
         if st != SRFTQ_OK:
@@ -377,8 +419,9 @@ class CacheAppender:
         self._f16 = torch.float16
 
     def __call__(self, x):
-        if tuple(x.shape) != self.x_shape or x.dtype != self._f16 or not x.is_contiguous():
-            raise ValueError(f"x must be a contiguous fp16 tensor of shape {self.x_shape}")
+        if (tuple(x.shape) != self.x_shape or x.dtype != self._f16 or not x.is_contiguous()
+                or x.device != self._device):
+            raise ValueError(f"x must be a contiguous fp16 tensor of shape {self.x_shape} on {self._device}")
         st = self._fn(*self._args, x.data_ptr(), *self._rest)
         if st != SRFTQ_OK:
             _check(st, "srftq_cache_append")
@@ -396,7 +439,10 @@ def cache_read(codes, scales, T, signs=None, lam=None, group=16, bits=4, rot="sr
     if d is None:
         d = codes.shape[-1] * 8 // bits
     B, H, t_cap = _cache_dims(codes, scales, d, bits, group)
+    _head_rows(signs, B, H, d, "signs", device=codes.device)
+    _head_rows(lam, B, H, d, "lambda", device=codes.device)
     out = _out(out, (B, int(T), H, d), torch.float16, codes.device, "out")
+    _same_device(codes.device, scales=scales, out=out)
     sh = make_shape(B, int(T), H, d, group, bits, rot, variant)
     _check(srftq_cache_read(sh, t_cap, codes, scales, signs, lam, out, stream), "srftq_cache_read")
     return out
@@ -443,6 +489,14 @@ def _attention(mats, q, k_codes, k_scales, v_codes, v_scales, k_signs, k_lam, v_
     if HR % H:
         raise ValueError(f"q has {HR} heads, not a multiple of the {H} KV heads")
     R = HR // H
+    _head_rows(k_signs, B, H, d, "k_signs", device=q.device)
+    _head_rows(k_lam, B, H, d, "k_lam", device=q.device)
+    _head_rows(v_signs, B, H, d, "v_signs", device=q.device)
+    _head_rows(v_lam, B, H, d, "v_lam", device=q.device)
+    if lengths is not None and tuple(lengths.shape) != (B,):
+        raise ValueError(f"lengths must have shape ({B},), got {tuple(lengths.shape)}")
+    _same_device(q.device, k_codes=k_codes, k_scales=k_scales, v_codes=v_codes, v_scales=v_scales,
+                 lengths=lengths, workspace=workspace, out=out)
     T = t_cap if T is None else int(T)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     sh = make_shape(B, T, H, d, group, bits, rot)
@@ -476,8 +530,12 @@ def rotate(x, signs=None, rot="srft", variant="default", out=None, stream=None):
     B, T, H, d = _dims(x)
     _req(x, torch.float16, "x")
     _req(signs, torch.int8, "signs")
+    _head_rows(signs, B, H, d, "signs", x.dim() == 3, x.device)
     if out is None:
         out = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+    elif tuple(out.shape) != tuple(x.shape):
+        raise ValueError(f"out must have shape {tuple(x.shape)}")
+    _req(out, torch.float32, "out")
     sh = make_shape(B, T, H, d, 8, 4, rot, variant)
     _check(srftq_rotate(sh, x, signs, out, stream), "srftq_rotate")
     return out
@@ -489,8 +547,12 @@ def unrotate(y, signs=None, rot="srft", variant="default", out=None, stream=None
     B, T, H, d = _dims(y)
     _req(y, torch.float32, "y")
     _req(signs, torch.int8, "signs")
+    _head_rows(signs, B, H, d, "signs", y.dim() == 3, y.device)
     if out is None:
         out = torch.empty(y.shape, dtype=torch.float16, device=y.device)
+    elif tuple(out.shape) != tuple(y.shape):
+        raise ValueError(f"out must have shape {tuple(y.shape)}")
+    _req(out, torch.float16, "out")
     sh = make_shape(B, T, H, d, 8, 4, rot, variant)
     _check(srftq_unrotate(sh, y, signs, out, stream), "srftq_unrotate")
     return out
@@ -502,8 +564,12 @@ def calibrate_lambda(x, signs=None, rot="srft", variant="default", out=None, str
     B, T, H, d = _dims(x)
     _req(x, torch.float16, "x")
     _req(signs, torch.int8, "signs")
+    _head_rows(signs, B, H, d, "signs", x.dim() == 3, x.device)
     if out is None:
         out = torch.empty((B, H, d), dtype=torch.float32, device=x.device)
+    elif tuple(out.shape) != (B, H, d):
+        raise ValueError(f"out must have shape {(B, H, d)}")
+    _req(out, torch.float32, "out")
     sh = make_shape(B, T, H, d, 8, 4, rot, variant)
     _check(srftq_calibrate_lambda(sh, x, signs, out, stream), "srftq_calibrate_lambda")
     return out if x.dim() == 4 else out[0]
@@ -541,6 +607,9 @@ def quantize_dense(x, Q, signs=None, lam=None, group=16, bits=4, codes=None, sca
     _req(signs, torch.int8, "signs")
     _req(lam, torch.float32, "lambda")
     qs = _q_stride(Q, B, H, d)
+    _head_rows(signs, B, H, d, "signs", x.dim() == 3, x.device)
+    _head_rows(lam, B, H, d, "lambda", x.dim() == 3, x.device)
+    _same_device(x.device, Q=Q)
     lead = _cache_lead(x)
     codes = _out(codes, lead + (d * bits // 8,), torch.uint8, x.device, "codes")
     scales = _out(scales, lead + (max(d // max(group, 1), 1),), torch.float16, x.device, "scales")
@@ -568,6 +637,10 @@ def dequantize_dense(codes, scales, Q, signs=None, lam=None, group=16, bits=4, d
     else:
         raise ValueError("codes must be [H,T,*] or [B,H,T,*]")
     qs = _q_stride(Q, B, H, d)
+    _check_scales(scales, codes.shape[:-1], d, group)
+    _head_rows(signs, B, H, d, "signs", codes.dim() == 3, codes.device)
+    _head_rows(lam, B, H, d, "lambda", codes.dim() == 3, codes.device)
+    _same_device(codes.device, scales=scales, Q=Q)
     out = _out(out, oshape, torch.float16, codes.device, "out")
     sh = make_shape(B, T, H, d, group, bits, "none")
     _check(srftq_dequantize_dense(sh, Q, qs, codes, scales, signs, lam, out, stream), "srftq_dequantize_dense")

@@ -56,6 +56,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_f64_to_f16.restype = ctypes.c_uint16
         L.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
         L.oracle_f16_to_f64.restype = ctypes.c_double
+        L.oracle_set_num_threads.argtypes = [ctypes.c_int]
+        L.oracle_set_num_threads.restype = None
         for f in ("oracle_rotate", "oracle_unrotate", "oracle_quantize",
                   "oracle_dequantize", "oracle_quantize_dense", "oracle_dequantize_dense",
                   "oracle_calibrate_lambda", "oracle_num_threads"):
@@ -351,3 +353,8 @@ def f64_to_f16(v) -> np.ndarray:
 
 def num_threads() -> int:
     return int(lib().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads the oracle's parallel loops use from now on."""
+    lib().oracle_set_num_threads(int(n))

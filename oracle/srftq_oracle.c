@@ -621,3 +621,14 @@ int oracle_num_threads(void)
     return 1;
 #endif
 }
+
+/* Threads the parallel loops use from now on (timing on one core). */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    omp_set_num_threads(n > 0 ? n : 1);
+#else
+    (void)n;
+#endif
+}

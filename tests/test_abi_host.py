@@ -289,3 +289,53 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in r.stderr
+
+
+# --------------------------------------------------------------------------
+# The Python binding rejects misshaped or misplaced side tensors before any
+# launch (the kernels index signs and lambda as [B, H, d] and lengths as [B]).
+# --------------------------------------------------------------------------
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros((2, 4, 3, 64), dtype=torch.float16)
+    with pytest.raises(ValueError, match="CUDA"):
+        S.quantize(x)
+    with pytest.raises(ValueError, match="CUDA"):
+        S.cache_append(x, torch.zeros((2, 3, 8, 32), dtype=torch.uint8),
+                       torch.zeros((2, 3, 8, 4), dtype=torch.float16))
+
+
+def test_head_rows_shapes():
+    import torch
+    B, H, d = 2, 3, 64
+    ok = torch.ones((B, H, d), dtype=torch.int8)
+    assert S._head_rows(ok, B, H, d, "signs") is ok
+    assert S._head_rows(None, B, H, d, "signs") is None
+    with pytest.raises(ValueError, match="signs must have shape"):
+        S._head_rows(torch.ones((H, d), dtype=torch.int8), B, H, d, "signs", flat_ok=True)
+    with pytest.raises(ValueError, match="lambda must have shape"):
+        S._head_rows(torch.ones((B, H, d // 2)), B, H, d, "lambda")
+    with pytest.raises(ValueError, match="lambda must have shape"):
+        S._head_rows(torch.ones((B + 1, H, d)), B, H, d, "lambda")
+    # one tensor, 3-D data: [H, d] and [1, H, d] both hold one row per head
+    assert S._head_rows(torch.ones((H, d)), 1, H, d, "lambda", flat_ok=True) is not None
+    assert S._head_rows(torch.ones((1, H, d)), 1, H, d, "lambda", flat_ok=True) is not None
+    with pytest.raises(ValueError, match="is on"):
+        S._same_device(torch.device("cuda", 0), pos=torch.zeros(2, dtype=torch.int32))
+
+
+def test_cache_appender_rejects_cpu_tokens():
+    """CacheAppender checks the new tokens' device on every call: a CPU
+    tensor of the right shape and dtype raises before its host pointer could
+    reach the kernel."""
+    import torch
+    app = object.__new__(S.CacheAppender)          # the fields __call__ reads, no device needed
+    app.x_shape = (2, 1, 3, 64)
+    app._f16 = torch.float16
+    app._device = torch.device("cuda", 0)
+    app._fn = None                                  # never reached
+    with pytest.raises(ValueError, match="on cuda:0"):
+        app(torch.zeros(app.x_shape, dtype=torch.float16))
+    with pytest.raises(ValueError, match="shape"):
+        app(torch.zeros((2, 2, 3, 64), dtype=torch.float16))

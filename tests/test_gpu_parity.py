@@ -3,8 +3,8 @@
 Every case runs the same seeded inputs through libsrftq on cuda:0 and through
 the oracle, and compares element by element (tolerances in
 oracle/compare.py).  Small cases are compared in full (several 64-token tiles
-and a ragged tail); the full-size workloads are compared on sampled vectors,
-in the launch configuration the benchmark times.
+and a ragged tail); the full-size workloads are compared in full too, every
+vector, in the launch configuration the benchmark times.
 """
 import numpy as np
 import pytest
@@ -95,10 +95,11 @@ def test_empty_tokens_no_op():
     assert codes.shape == (8, 0, 64) and scales.shape == (8, 0, 8)     # head-major [H, T, .]
 
 
-def test_constructed_ties_exact():
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_constructed_ties_exact(d):
     """rot none, lambda 1, group absmax 7 -> sigma 1: z/sigma lands exactly on
     half-integers; rounding must be to even, bit for bit."""
-    d, g = 128, 16
+    g = 16
     base = np.array([7.0, 2.5, 3.5, -2.5, -3.5, 0.5, 1.5, 6.5, -0.5, -1.5, 4.5, 5.5, 0.0, 1.0, -7.0, -6.5])
     x = np.tile(base, (3, 70, 1, d // g)).astype(np.float16).reshape(3, 70, 1, d)
     codes_g, scales_g = S.quantize(dev(x), None, None, g, 4, "none")
@@ -109,27 +110,37 @@ def test_constructed_ties_exact():
         run_and_check(x, None, None, g, bits, "none", "default")
 
 
-def test_ties_with_a_non_power_of_two_scale():
-    """sigma = 3: the oracle rounds the exact ties z / sigma = +-2.5, +-0.5 half
-    to even (the definition); the kernel multiplies by fp32(1/3), slightly
-    above 1/3, and may land on the other neighbour.  Codes may differ there
-    only, by one, and everywhere else bit for bit."""
-    d, g = 128, 16
-    for bits, qmax in ((4, 7), (8, 127)):
-        vals = [3.0 * qmax, 7.5, -7.5, 10.5, 4.5, 1.5, -1.5, 16.5, -10.5, 0.0, 3.0, -3.0, 6.0, 9.0, 12.0, 4.0]
-        x = np.tile(np.array(vals), (2, 70, 1, d // g)).astype(np.float16).reshape(2, 70, 1, d)
-        codes_g, scales_g = S.quantize(dev(x), None, None, g, bits, "none")
-        codes_o, scales_o, z_o = oracle.quantize(x, None, None, g, bits, "none", return_z=True)
-        assert np.array_equal(host(scales_g).view(np.uint16), scales_o)
-        qg = compare.decode_codes(host(codes_g), bits, d).reshape(-1, g)
-        qo = compare.decode_codes(codes_o, bits, d).reshape(-1, g)
-        diff = np.nonzero((qg != qo).any(axis=0))[0]
-        assert set(diff.tolist()) <= {1, 2, 5, 6}, diff
-        assert np.all(np.abs(qg - qo) <= 1)
-        # every difference sits on an exact tie of the oracle's quotient
-        ratio = z_o.reshape(-1, g) / 3.0
-        assert np.all(np.abs(ratio[qg != qo] % 1.0) == 0.5)
-        print(f"[ties sigma=3 bits={bits}] columns differing: {diff.tolist()}", flush=True)
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_ties_with_a_non_power_of_two_scale(d):
+    """sigma = 3: the exact ties z / sigma = +-2.5, +-0.5 round half to even as
+    the definition says.  Without a rotation the kernel finds the exact ties
+    from the residual z - q sigma (its fp32 reciprocal of 3 would otherwise
+    land on the odd neighbour), so the codes match bit for bit; through the
+    flattened one-vector-per-lane kernel (few tokens) as well."""
+    g = 16
+    for T in (70, 3):
+        for bits, qmax in ((4, 7), (8, 127)):
+            vals = [3.0 * qmax, 7.5, -7.5, 10.5, 4.5, 1.5, -1.5, 16.5, -10.5, 0.0, 3.0, -3.0, 6.0, 9.0, 12.0, 4.0]
+            x = np.tile(np.array(vals), (2, T, 1, d // g)).astype(np.float16).reshape(2, T, 1, d)
+            codes_g, scales_g = S.quantize(dev(x), None, None, g, bits, "none")
+            codes_o, scales_o = oracle.quantize(x, None, None, g, bits, "none")
+            assert np.array_equal(host(scales_g).view(np.uint16), scales_o)
+            assert np.array_equal(host(codes_g), codes_o), f"d={d} T={T} bits={bits}"
+            print(f"[ties sigma=3 d={d} T={T} bits={bits}] bit-exact", flush=True)
+
+
+@pytest.mark.parametrize("rot", ["srft", "srht", "none"])
+@pytest.mark.parametrize("group,bits", [(128, 4), (128, 8), (256, 4), (8, 8)])
+@pytest.mark.parametrize("lam", [False, True])
+def test_wide_head_groups(rot, group, bits, lam):
+    """d = 256 runs two lanes per vector: groups of 128 (one lane's whole
+    half; for the SRFT it mixes the half the lane carries negated), 256 (one
+    group over both lanes: the absmax crosses the lane pair) and 8 (32
+    scales per vector), over 32-token tiles with a ragged tail."""
+    x, s, l = rand_case(7000 + group + bits, 3, 77, 2, 256, scale=1.5, lam=lam)
+    x[1, 40, 1, 3] = 25.0
+    print(f"[wide groups {rot} g={group} b={bits} lam={lam}]", flush=True)
+    run_and_check(x, s, l, group, bits, rot, "default")
 
 
 def test_zero_subnormal_and_saturated_groups():
@@ -237,32 +248,40 @@ def test_decode_workload_step():
     print(run_and_check(x, s, None, w.group, w.bits, "srft", "default"))
 
 
-def _sample_rows(rng, B, T, H, n):
-    idx = [(0, 0, 0), (B - 1, T - 1, H - 1), (B - 1, T - 1, 0), (0, T - 1, H - 1)]
-    idx += [(int(rng.integers(B)), int(rng.integers(T)), int(rng.integers(H))) for _ in range(n)]
-    return np.array(idx)
-
-
-def _check_sampled(x, s, lam, codes_g, scales_g, xhat_g, w, rot, n=1536):
-    """Oracle on sampled vectors (one oracle 'head' per sample)."""
+def _check_full(x, s, lam, codes_g, scales_g, xhat_g, w, rot, chunk=1 << 18):
+    """Every vector against the oracle, in slices of about `chunk` vectors
+    (whole tensors, or token ranges of one tensor); the code-mismatch bound
+    holds in every slice.  Returns the totals."""
     B, T, H, d = x.shape
-    rng = np.random.default_rng(w.seed)
-    ix = _sample_rows(rng, B, T, H, n)
-    b, t, h = ix[:, 0], ix[:, 1], ix[:, 2]
-    xs = x[b, t, h][None, None]                     # [1, 1, n, d]
-    ss = s[b, h][None]                              # [1, n, d]
-    ls = None if lam is None else lam[b, h][None]
-    # the oracle's sample is B=1, H=n, T=1: its head-major cache is [1, n, 1, .]
-    cg = host(codes_g[b, h, t])[None, :, None]
-    sg = host(scales_g[b, h, t]).view(np.uint16)[None, :, None]
-    co, so, zo = oracle.quantize(xs, ss, ls, w.group, w.bits, rot, return_z=True)
-    st = compare.check_quantize(cg, sg, co, so, zo, w.bits, w.group, d)
-    xo = oracle.dequantize(cg, sg, ss, ls, w.group, w.bits, rot, d=d)
-    st.update(compare.check_dequantize(host(xhat_g[b, t, h])[None, None], xo))
-    return st
+    cg_all = host(codes_g)
+    sg_all = host(scales_g).view(np.uint16)
+    xg_all = host(xhat_g)
+    tot = {"vectors": 0, "code_mismatch": 0, "scale_mismatch": 0, "ulp_mismatch": 0}
+    per_tensor = T * H
+    bstep = max(1, chunk // per_tensor)
+    tstep = T if per_tensor <= chunk else max(1, chunk // H)
+    for b0 in range(0, B, bstep):
+        b1 = min(B, b0 + bstep)
+        for t0 in range(0, T, tstep):
+            t1 = min(T, t0 + tstep)
+            xs = np.ascontiguousarray(x[b0:b1, t0:t1])
+            ss = s[b0:b1]
+            ls = None if lam is None else lam[b0:b1]
+            cg = np.ascontiguousarray(cg_all[b0:b1, :, t0:t1])
+            sg = np.ascontiguousarray(sg_all[b0:b1, :, t0:t1])
+            co, so, zo = oracle.quantize(xs, ss, ls, w.group, w.bits, rot, return_z=True)
+            st = compare.check_quantize(cg, sg, co, so, zo, w.bits, w.group, d)
+            del co, so, zo
+            xo = oracle.dequantize(cg, sg, ss, ls, w.group, w.bits, rot, d=d)
+            st.update(compare.check_dequantize(xg_all[b0:b1, t0:t1], xo))
+            tot["vectors"] += xs.shape[0] * xs.shape[1] * H
+            for k in ("code_mismatch", "scale_mismatch", "ulp_mismatch"):
+                tot[k] += st[k]
+    assert tot["vectors"] == B * T * H
+    return tot
 
 
-def test_roundtrip_workload_full_size_sampled():
+def test_roundtrip_workload_full_size():
     w = W.WORKLOADS["roundtrip"]
     x, s = W.generate(w)
     print(f"[roundtrip full] {x.shape}", flush=True)
@@ -271,11 +290,11 @@ def test_roundtrip_workload_full_size_sampled():
     xhat = S.dequantize(codes, scales, sd, None, w.group, w.bits)
     torch.cuda.synchronize()
     rel = (torch.linalg.vector_norm((xhat.float() - xd.float())) / torch.linalg.vector_norm(xd.float())).item()
-    print(_check_sampled(x, s, None, codes, scales, xhat, w, "srft"), "rel_l2", rel)
+    print(_check_full(x, s, None, codes, scales, xhat, w, "srft"), "rel_l2", rel, flush=True)
     assert rel < 0.15
 
 
-def test_outlier_workload_full_size_sampled():
+def test_outlier_workload_full_size():
     w = W.WORKLOADS["outlier"]
     x, s = W.generate(w)
     # lambda input: the oracle's calibration over the first 512 tokens of
@@ -286,7 +305,7 @@ def test_outlier_workload_full_size_sampled():
     codes, scales = S.quantize(xd, sd, ld, w.group, w.bits)
     xhat = S.dequantize(codes, scales, sd, ld, w.group, w.bits)
     torch.cuda.synchronize()
-    print(_check_sampled(x, s, lam, codes, scales, xhat, w, "srft"))
+    print(_check_full(x, s, lam, codes, scales, xhat, w, "srft"), flush=True)
 
 
 @pytest.mark.parametrize("rot,variant", [("srft", "default"), ("srft", "paired"), ("srht", "default")])
@@ -299,7 +318,7 @@ def test_wide_workload_reduced(rot, variant):
 
 
 @pytest.mark.parametrize("rot", ["srft", "srht"])
-def test_wide_workload_full_size_sampled(rot):
+def test_wide_workload_full_size(rot):
     w = W.WORKLOADS["wide"]
     x, s = W.generate(w)
     # lambda input: the oracle's calibration over the first 512 tokens
@@ -310,7 +329,7 @@ def test_wide_workload_full_size_sampled(rot):
     xhat = S.dequantize(codes, scales, sd, ld, w.group, w.bits, rot)
     torch.cuda.synchronize()
     rel = (torch.linalg.vector_norm(xhat.float() - xd.float()) / torch.linalg.vector_norm(xd.float())).item()
-    print(_check_sampled(x, s, lam, codes, scales, xhat, w, rot), "rel_l2", rel)
+    print(_check_full(x, s, lam, codes, scales, xhat, w, rot), "rel_l2", rel, flush=True)
     assert rel < 0.2
 
 
@@ -376,3 +395,24 @@ def test_few_tokens_append_ragged_positions():
             if 0 <= r < cap:
                 zc[b, :, r] = z[b, :, t]
     print(compare.check_quantize(cg[written], sg[written], co[written], so[written], zc[written], bits, g, d))
+
+
+def test_binding_rejects_misshaped_side_tensors():
+    """Wrong-shaped signs / lambda / lengths raise before any launch."""
+    x, s, l = rand_case(9, 2, 70, 3, 128, lam=True)
+    xd = dev(x)
+    with pytest.raises(ValueError, match="signs must have shape"):
+        S.quantize(xd, dev(s[0]), None)                    # [H, d] for B = 2
+    with pytest.raises(ValueError, match="lambda must have shape"):
+        S.quantize(xd, dev(s), dev(l[:, :2]))
+    codes, scales = S.quantize(xd, dev(s), dev(l))
+    with pytest.raises(ValueError, match="lambda must have shape"):
+        S.dequantize(codes, scales, dev(s), dev(l[:1]))
+    q = dev(np.zeros((2, 6, 128), dtype=np.float16))
+    with pytest.raises(ValueError, match="lengths must have shape"):
+        S.decode_attention(q, codes, scales, codes, scales, dev(s), dev(l), dev(s), dev(l),
+                           lengths=dev(np.array([70], dtype=np.int32)))
+    app = S.CacheAppender(codes, scales, dev(np.zeros(2, dtype=np.int32)), dev(s), dev(l), tokens=1)
+    with pytest.raises(ValueError):
+        app(torch.zeros((2, 1, 3, 128), dtype=torch.float16))     # CPU tokens
+    torch.cuda.synchronize()
