@@ -79,7 +79,9 @@ typedef enum {
     SRFTQ_ERR_SHAPE = 2,       /* negative or inconsistent sizes */
     SRFTQ_ERR_UNSUPPORTED = 3, /* (rot, d, group, bits) combination not built */
     SRFTQ_ERR_ALIGN = 4,       /* a data pointer is not 16-byte aligned */
-    SRFTQ_ERR_HIP = 5          /* HIP runtime error (launch failure, no device) */
+    SRFTQ_ERR_HIP = 5,         /* HIP runtime error (launch failure, no device) */
+    SRFTQ_ERR_CAPACITY = 6     /* needs more scratch than the library's fixed buffer
+                                  (srftq_decode_attention_noalloc only) */
 } srftq_status;
 
 typedef enum {
@@ -249,6 +251,30 @@ srftq_status srftq_decode_attention(const srftq_shape* shape, int64_t t_cap, int
                                     const srftq_cache_view* v, const int32_t* lengths,
                                     float scale, float* out, void* workspace,
                                     size_t workspace_bytes, void* stream);
+
+/*
+ * srftq_decode_attention_noalloc: srftq_decode_attention for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  The workspace is the library's
+ * own static device array of SRFTQ_ATTENTION_SCRATCH_BYTES, one copy per
+ * GPU, held until the process ends; the caller passes inputs and outputs
+ * only.  Every other argument, layout and error as for
+ * srftq_decode_attention; a shape whose srftq_attention_workspace_bytes
+ * exceeds SRFTQ_ATTENTION_SCRATCH_BYTES is SRFTQ_ERR_CAPACITY, returned
+ * before anything is launched.  The call allocates nothing (no hipMalloc,
+ * no allocating library routine); on a device's first call it looks up the
+ * array's address on that device (hipGetSymbolAddress).  Each call writes
+ * every scratch byte it reads, so nothing needs clearing between calls; but
+ * all calls on one GPU share the one array, so calls that overlap on one GPU
+ * (several streams or host threads at once) race and give wrong results:
+ * serialize them, or use srftq_decode_attention with a workspace each.
+ */
+#define SRFTQ_ATTENTION_SCRATCH_BYTES ((size_t)16 << 20)
+
+srftq_status srftq_decode_attention_noalloc(const srftq_shape* shape, int64_t t_cap, int32_t q_per_kv,
+                                            const uint16_t* q, const srftq_cache_view* k,
+                                            const srftq_cache_view* v, const int32_t* lengths,
+                                            float scale, float* out, void* stream);
 
 /*
  * Rotations given as a matrix.  "When Quantization Is Free", Metodologia 3,

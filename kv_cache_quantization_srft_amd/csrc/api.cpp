@@ -243,12 +243,23 @@ srftq_status set_plus_ones(srftq::AttnArgs& a) {
   return SRFTQ_OK;
 }
 
+// The workspace carve-up of an attention plan (see AttnPlan).
+void set_workspace(srftq::AttnArgs& a, void* workspace, const AttnPlan& plan) {
+  a.uq = (float*)workspace;
+  a.uexp = (float*)((char*)workspace + plan.off_exp);
+  a.ws_ml = (float*)((char*)workspace + plan.off_ml);
+  a.ws_acc = (float*)((char*)workspace + plan.off_acc);
+}
+
 // Checks and launch arguments shared by the decode-attention entry points
 // (the shape already validated); `empty` when there is nothing to launch.
+// With `deferred`, the workspace is the library's own scratch array, looked
+// up after every check (it needs a device): only its size is checked here,
+// and a problem too large for it is SRFTQ_ERR_CAPACITY.
 srftq_status attention_args(const srftq_shape* s, int64_t t_cap, int32_t R, const uint16_t* q,
                             const srftq_cache_view* k, const srftq_cache_view* v, const int32_t* lengths,
                             float scale, float* out, void* workspace, size_t workspace_bytes,
-                            srftq::AttnArgs& a, bool& empty) {
+                            srftq::AttnArgs& a, bool& empty, bool deferred = false) {
   srftq_status st;
   if (R < 1 || R > 16) return SRFTQ_ERR_SHAPE;
   if (s->group < 16) return SRFTQ_ERR_UNSUPPORTED;
@@ -259,9 +270,10 @@ srftq_status attention_args(const srftq_shape* s, int64_t t_cap, int32_t R, cons
   if (!attn_plan(s, R, &plan)) return SRFTQ_ERR_SHAPE;
   empty = s->B * (int64_t)s->H == 0;
   if (empty) return SRFTQ_OK;
-  if (!q || !k || !v || !out || !workspace) return SRFTQ_ERR_NULL;
+  if (deferred && workspace_bytes < plan.bytes) return SRFTQ_ERR_CAPACITY;
+  if (!q || !k || !v || !out || (!workspace && !deferred)) return SRFTQ_ERR_NULL;
   if (!k->codes || !k->scales || !v->codes || !v->scales) return SRFTQ_ERR_NULL;
-  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace) || !aligned16(k->codes) ||
+  if (!aligned16(q) || !aligned16(out) || (!deferred && !aligned16(workspace)) || !aligned16(k->codes) ||
       !aligned16(k->scales) || !aligned16(v->codes) || !aligned16(v->scales))
     return SRFTQ_ERR_ALIGN;
   if (lengths && !aligned4(lengths)) return SRFTQ_ERR_ALIGN;
@@ -290,14 +302,48 @@ srftq_status attention_args(const srftq_shape* s, int64_t t_cap, int32_t R, cons
   a.lam_v = v->lambda;
   a.lengths = lengths;
   a.out = out;
-  a.uq = (float*)workspace;
-  a.uexp = (float*)((char*)workspace + plan.off_exp);
-  a.ws_ml = (float*)((char*)workspace + plan.off_ml);
-  a.ws_acc = (float*)((char*)workspace + plan.off_acc);
+  set_workspace(a, workspace, plan);
   return SRFTQ_OK;
 }
 
+// The one decode-attention path behind both entry points: `scratch` null
+// (caller's workspace) or the per-device scratch lookup of
+// srftq_decode_attention_noalloc.
+srftq_status decode_attention(const srftq_shape* s, int64_t t_cap, int32_t R, const uint16_t* q,
+                              const srftq_cache_view* k, const srftq_cache_view* v, const int32_t* lengths,
+                              float scale, float* out, void* workspace, size_t workspace_bytes,
+                              srftq::ScratchFn scratch, void* stream) {
+  srftq_status st = validate(s);
+  if (st != SRFTQ_OK) return st;
+  srftq::AttnArgs a = {};
+  bool empty = false;
+  if ((st = attention_args(s, t_cap, R, q, k, v, lengths, scale, out, workspace, workspace_bytes, a, empty,
+                           scratch != nullptr)) != SRFTQ_OK ||
+      empty)
+    return st;
+  a.rot = s->rot;
+  if ((st = set_plus_ones(a)) != SRFTQ_OK) return st;
+  if (scratch) {
+    void* ws = scratch();
+    if (!ws) return SRFTQ_ERR_HIP;
+    AttnPlan plan;
+    attn_plan(s, R, &plan);
+    set_workspace(a, ws, plan);
+  }
+  const int di = s->d == 64 ? 0 : s->d == 96 ? 1 : s->d == 128 ? 2 : 3;
+  return from_hip(kAttention[di](a, (hipStream_t)stream));
+}
+
 }  // namespace
+
+namespace srftq {
+srftq_status decode_attention_scratch(const srftq_shape* s, int64_t t_cap, int32_t R, const uint16_t* q,
+                                      const srftq_cache_view* k, const srftq_cache_view* v,
+                                      const int32_t* lengths, float scale, float* out, size_t scratch_bytes,
+                                      ScratchFn scratch, void* stream) {
+  return ::decode_attention(s, t_cap, R, q, k, v, lengths, scale, out, nullptr, scratch_bytes, scratch, stream);
+}
+}  // namespace srftq
 
 extern "C" {
 
@@ -312,17 +358,7 @@ srftq_status srftq_decode_attention(const srftq_shape* s, int64_t t_cap, int32_t
                                     const srftq_cache_view* k, const srftq_cache_view* v,
                                     const int32_t* lengths, float scale, float* out, void* workspace,
                                     size_t workspace_bytes, void* stream) {
-  srftq_status st = validate(s);
-  if (st != SRFTQ_OK) return st;
-  srftq::AttnArgs a = {};
-  bool empty = false;
-  if ((st = attention_args(s, t_cap, R, q, k, v, lengths, scale, out, workspace, workspace_bytes, a,
-                           empty)) != SRFTQ_OK || empty)
-    return st;
-  a.rot = s->rot;
-  if ((st = set_plus_ones(a)) != SRFTQ_OK) return st;
-  const int di = s->d == 64 ? 0 : s->d == 96 ? 1 : s->d == 128 ? 2 : 3;
-  return from_hip(kAttention[di](a, (hipStream_t)stream));
+  return decode_attention(s, t_cap, R, q, k, v, lengths, scale, out, workspace, workspace_bytes, nullptr, stream);
 }
 
 srftq_status srftq_decode_attention_dense(const srftq_shape* s, int64_t t_cap, int32_t R, const float* Qk,
@@ -516,6 +552,7 @@ const char* srftq_status_string(srftq_status status) {
     case SRFTQ_ERR_UNSUPPORTED: return "unsupported (d, group, bits, rot, variant) combination";
     case SRFTQ_ERR_ALIGN: return "misaligned pointer";
     case SRFTQ_ERR_HIP: return "HIP runtime error";
+    case SRFTQ_ERR_CAPACITY: return "problem needs more scratch memory than the library's fixed buffer holds";
     default: return "unknown status";
   }
 }

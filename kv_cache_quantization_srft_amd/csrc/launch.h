@@ -122,6 +122,16 @@ hipError_t run_dense_d256(const DenseArgs&, hipStream_t);
 // Q_m = H_1 ... H_k from V [n, k, d] into Q [n, d, d] (d <= 256, k <= 1024).
 hipError_t run_householder(int d, int k, int64_t n, const float* V, float* Q, hipStream_t st);
 
+// Decode attention with its workspace in the library's per-device scratch
+// array (srftq_decode_attention_noalloc): every argument is checked first,
+// then `scratch` returns the current device's array address (null on a HIP
+// error); scratch_bytes is the array's size.
+using ScratchFn = void* (*)();
+srftq_status decode_attention_scratch(const srftq_shape* s, int64_t t_cap, int32_t R, const uint16_t* q,
+                                      const srftq_cache_view* k, const srftq_cache_view* v,
+                                      const int32_t* lengths, float scale, float* out, size_t scratch_bytes,
+                                      ScratchFn scratch, void* stream);
+
 // Number of compute units of the current device (cached per device).
 int device_cu_count();
 

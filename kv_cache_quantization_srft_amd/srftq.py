@@ -19,7 +19,10 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libsrftq.so")
 
-SRFTQ_OK, SRFTQ_ERR_NULL, SRFTQ_ERR_SHAPE, SRFTQ_ERR_UNSUPPORTED, SRFTQ_ERR_ALIGN, SRFTQ_ERR_HIP = range(6)
+(SRFTQ_OK, SRFTQ_ERR_NULL, SRFTQ_ERR_SHAPE, SRFTQ_ERR_UNSUPPORTED, SRFTQ_ERR_ALIGN, SRFTQ_ERR_HIP,
+ SRFTQ_ERR_CAPACITY) = range(7)
+# size of the library's static attention scratch (srftq_decode_attention_noalloc)
+ATTENTION_SCRATCH_BYTES = 16 << 20
 ROT = {"srft": 0, "srht": 1, "none": 2}
 VARIANT = {"default": 0, "real": 1, "paired": 2}
 
@@ -82,6 +85,8 @@ def lib() -> ctypes.CDLL:
         L.srftq_attention_workspace_bytes.restype = ctypes.c_size_t
         L.srftq_decode_attention.argtypes = [sp, ctypes.c_int64, ctypes.c_int32, vp, cv, cv, vp,
                                              ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
+        L.srftq_decode_attention_noalloc.argtypes = [sp, ctypes.c_int64, ctypes.c_int32, vp, cv, cv, vp,
+                                                     ctypes.c_float, vp, vp]
         L.srftq_householder_matrix.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, vp, vp, vp]
         L.srftq_quantize_dense.argtypes = [sp, vp, ctypes.c_int64, vp, vp, vp, vp, vp, vp]
         L.srftq_dequantize_dense.argtypes = [sp, vp, ctypes.c_int64, vp, vp, vp, vp, vp, vp]
@@ -92,7 +97,8 @@ def lib() -> ctypes.CDLL:
         L.srftq_version.argtypes = []
         for f in ("srftq_validate", "srftq_quantize", "srftq_dequantize", "srftq_rotate",
                   "srftq_unrotate", "srftq_calibrate_lambda", "srftq_cache_append",
-                  "srftq_cache_read", "srftq_decode_attention", "srftq_householder_matrix",
+                  "srftq_cache_read", "srftq_decode_attention", "srftq_decode_attention_noalloc",
+                  "srftq_householder_matrix",
                   "srftq_quantize_dense", "srftq_dequantize_dense", "srftq_decode_attention_dense",
                   "srftq_version"):
             getattr(L, f).restype = ctypes.c_int
@@ -175,6 +181,14 @@ def srftq_decode_attention(shape, t_cap, q_per_kv, q, k_view, v_view, lengths, s
                                         None if v_view is None else ctypes.byref(v_view), _dp(lengths),
                                         float(scale), _dp(out), _dp(workspace), int(workspace_bytes),
                                         _stream(stream))
+
+
+def srftq_decode_attention_noalloc(shape, t_cap, q_per_kv, q, k_view, v_view, lengths, scale, out,
+                                   stream=None) -> int:
+    return lib().srftq_decode_attention_noalloc(ctypes.byref(shape), int(t_cap), int(q_per_kv), _dp(q),
+                                                None if k_view is None else ctypes.byref(k_view),
+                                                None if v_view is None else ctypes.byref(v_view), _dp(lengths),
+                                                float(scale), _dp(out), _stream(stream))
 
 
 def srftq_decode_attention_dense(shape, t_cap, q_per_kv, Qk, Qv, q_stride, q, k_view, v_view, lengths, scale,

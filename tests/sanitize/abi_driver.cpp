@@ -22,6 +22,7 @@ srftq_shape g_last_shape{};
 srftq::AttnArgs g_attn{};
 srftq::DenseArgs g_dense{};
 alignas(16) int8_t g_ones[256];
+alignas(256) uint8_t g_scratch[1 << 20];
 }  // namespace
 
 #define STUB_RUN(name)                                                          \
@@ -75,6 +76,8 @@ static int fails = 0;
       ++fails;                                                           \
     }                                                                    \
   } while (0)
+
+static void* scratch_fn() { return g_scratch; }
 
 int main() {
   alignas(16) static uint8_t buf[1 << 16];
@@ -149,7 +152,7 @@ int main() {
   EXPECT(srftq_calibrate_lambda(&ok, (uint16_t*)a, nullptr, (float*)a, nullptr) == SRFTQ_OK);
   EXPECT(srftq_rotate(&ok, nullptr, nullptr, (float*)a, nullptr) == SRFTQ_ERR_NULL);
 
-  // decode attention
+  // decode attention, with a workspace and with the deferred scratch
   const srftq_cache_view kv = {(uint8_t*)a, (uint16_t*)a, nullptr, nullptr};
   const size_t need = srftq_attention_workspace_bytes(&ok, 6);
   EXPECT(need > 0 && need <= sizeof buf);
@@ -163,6 +166,14 @@ int main() {
          SRFTQ_OK);
   EXPECT(g_launches == 1 && (void*)g_attn.uq == a && g_attn.signs_k == g_ones && g_attn.geo.R == 6);
   EXPECT((char*)g_attn.ws_acc + 4 <= (char*)a + need);
+  EXPECT(srftq::decode_attention_scratch(&ok, 100, 6, (uint16_t*)a, &kv, &kv, nullptr, 0.1f, (float*)a,
+                                         sizeof g_scratch, scratch_fn, nullptr) == SRFTQ_OK);
+  EXPECT(g_launches == 2 && (void*)g_attn.uq == g_scratch);
+  EXPECT(srftq::decode_attention_scratch(&ok, 100, 6, (uint16_t*)a, &kv, &kv, nullptr, 0.1f, (float*)a, need - 1,
+                                         scratch_fn, nullptr) == SRFTQ_ERR_CAPACITY);
+  EXPECT(srftq::decode_attention_scratch(&ok, 100, 6, nullptr, &kv, &kv, nullptr, 0.1f, (float*)a,
+                                         sizeof g_scratch, scratch_fn, nullptr) == SRFTQ_ERR_NULL);
+  EXPECT(g_launches == 2);
 
   // rotations given as matrices
   srftq_shape dn = ok;

@@ -29,8 +29,9 @@ def test_library_exports_every_declared_function():
 
 def test_version_and_status_strings():
     assert S.srftq_version() >= 100
-    for st in range(6):
+    for st in range(7):
         assert isinstance(S.status_string(st), str) and S.status_string(st)
+    assert S.status_string(7) == "unknown status"
 
 
 @pytest.mark.parametrize("kw,expect", [
@@ -181,6 +182,33 @@ def test_attention_workspace_and_argument_errors():
     assert call(nbytes=need - 1) == S.SRFTQ_ERR_SHAPE
     # no tensors or no heads: nothing to do
     assert call(shape=S.make_shape(0, 1000, 2, 128, 16, 4), q=None, out=None, ws=None) == S.SRFTQ_OK
+
+
+def test_noalloc_attention_argument_errors_return_before_launch():
+    """srftq_decode_attention_noalloc checks everything srftq_decode_attention
+    does, and a problem larger than the static scratch, before it touches a
+    device."""
+    sh = S.make_shape(2, 1000, 2, 128, 16, 4)
+    a, mis = _Fake(0x10000), _Fake(0x10008)
+    kv = S.CacheView(0x10000, 0x10000, None, None)
+    call = lambda shape=sh, t_cap=1000, R=6, q=a, k=kv, v=kv, lengths=None, scale=0.1, out=a: \
+        S.srftq_decode_attention_noalloc(shape, t_cap, R, q, k, v, lengths, scale, out, stream=0)
+    assert call(R=0) == S.SRFTQ_ERR_SHAPE
+    assert call(shape=S.make_shape(2, 1000, 2, 128, 8, 4)) == S.SRFTQ_ERR_UNSUPPORTED
+    assert call(t_cap=999) == S.SRFTQ_ERR_SHAPE
+    assert call(q=None) == S.SRFTQ_ERR_NULL
+    assert call(out=mis) == S.SRFTQ_ERR_ALIGN
+    assert call(shape=S.make_shape(0, 1000, 2, 128, 16, 4), q=None, out=None) == S.SRFTQ_OK
+    # a workspace beyond the static array: 1,200 (tensor, head) pairs of 16 query heads at d = 256
+    big = S.make_shape(600, 20000, 2, 256, 16, 4)
+    assert S.srftq_attention_workspace_bytes(big, 16) > S.ATTENTION_SCRATCH_BYTES
+    assert call(shape=big, t_cap=20000, R=16) == S.SRFTQ_ERR_CAPACITY
+    hdr = open(os.path.join(ROOT, "include", "srftq.h")).read()
+    m = re.search(r"#define SRFTQ_ATTENTION_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", hdr)
+    assert m and int(m.group(1)) << int(m.group(2)) == S.ATTENTION_SCRATCH_BYTES
+    # the benchmark's decode step fits
+    bench = S.make_shape(28, 32768, 2, 128, 16, 4)
+    assert 0 < S.srftq_attention_workspace_bytes(bench, 6) <= S.ATTENTION_SCRATCH_BYTES
 
 
 def test_dense_attention_argument_errors_return_before_launch():
