@@ -103,8 +103,15 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // issue no other vector-memory loads whose results the compiler tracks.
 // "s_nop 0" is the one wait state required between writing M0 and an LDS-DMA.
 template <int SIZE, bool STREAM = false>
-__device__ __forceinline__ void dma_to_lds(const void* sbase, uint32_t voff, uint32_t lds) {
+__device__ __forceinline__ void dma_to_lds(const void* sbase_in, uint32_t voff, uint32_t lds_in) {
   static_assert(SIZE == 16 || SIZE == 4 || SIZE == 2, "LDS-DMA size");
+  // Both are wave-uniform; readfirstlane tells the compiler so, which keeps
+  // them in scalar registers even where it had placed them in VGPRs.
+  const uint64_t sb = (uint64_t)(uintptr_t)sbase_in;
+  const uint64_t sbu = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(sb >> 32)) << 32) |
+                       (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)sb);
+  const void* sbase = (const void*)(uintptr_t)sbu;
+  const uint32_t lds = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_in);
   if constexpr (SIZE == 16 && STREAM)
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
                  :: "v"(voff), "s"(sbase), "s"(lds) : "memory", "m0");
@@ -155,6 +162,24 @@ __device__ __forceinline__ void swap32(float& x, float& y) {
   swap32(a, b);
   x = as_f32(a);
   y = as_f32(b);
+}
+
+// Debug builds only (SRFTQ_LDS_POISON=1): fill an LDS buffer of one
+// single-wave block with 0xff bytes (fp16 and fp32 NaN, all-ones codes and
+// masks) before the data meant for it is written, so that any read of a
+// byte the kernel did not write this time shows in its output.  The fill
+// has completed when this returns, so an LDS-DMA issued next lands after it.
+#ifndef SRFTQ_LDS_POISON
+#define SRFTQ_LDS_POISON 0
+#endif
+template <int BYTES>
+__device__ __forceinline__ void lds_poison([[maybe_unused]] void* buf, [[maybe_unused]] int lane) {
+  if constexpr (SRFTQ_LDS_POISON) {
+    static_assert(BYTES % 4 == 0, "dword fill");
+    uint32_t* w = (uint32_t*)buf;
+    for (int i = lane; i < BYTES / 4; i += 64) w[i] = 0xffffffffu;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
 }
 
 // Uniform value -> scalar register.

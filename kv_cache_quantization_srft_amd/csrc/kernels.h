@@ -225,7 +225,7 @@ struct RowTile {
 template <int D>
 __device__ __forceinline__ void issue_row_f32(const float* src, int lane, uint8_t* lds) {
   static_assert(D <= 256, "one DMA instruction per row");
-  if (lane < D / 4) dma_to_lds<16>(src, 16u * (uint32_t)lane, lds_addr(lds));
+  if (D / 4 == 64 || lane < D / 4) dma_to_lds<16>(src, 16u * (uint32_t)lane, lds_addr(lds));
 }
 
 // A head's D int8 signs fetched by LDS-DMA: pair m = 64i + l (lane l of

@@ -103,6 +103,10 @@ __device__ __forceinline__ uint32_t pack_codes(const uint32_t* t) {
   }
 }
 
+// Where the lambda entry of a lane's coordinate j lives: at lam + j for a
+// contiguous run of coordinates (a plain pointer), or as a LamAt gives it.
+__device__ __forceinline__ const float* lam_at(const float* lam, int j) { return lam + j; }
+
 // Whether group g of width G holds a coordinate with the edge scale.
 template <class Sc, int G>
 constexpr bool group_has_edge(int g) {
@@ -117,11 +121,11 @@ constexpr bool group_has_edge(int g) {
 // Sc: the per-coordinate scales (is_edge, kFwdBulk, kFwdEdge).  Coordinates
 // from NEG_FROM on hold negated values: their groups take sigma from |y| as
 // the others and round y * (neg * r), neg = -1 where they are negated.
-// XLANE: the one group (G = D) continues in the partner lane (l +- 32),
-// whose absmax joins this lane's.
+// XLANE: every group continues in the partner lane (l +- 32), whose absmax
+// for it joins this lane's (both lanes then hold the same scales).
 template <int D, int G, int BITS, int ROT, int VAR, bool LAM, class Sc = Scales<D, ROT, VAR>, int NEG_FROM = D,
-          bool XLANE = false>
-__device__ __forceinline__ void quantize_tail(float (&y)[D], const float* __restrict__ lam,
+          bool XLANE = false, class LamP = const float*>
+__device__ __forceinline__ void quantize_tail(float (&y)[D], LamP lam,
                                               uint32_t (&codes)[CodeWords<D, BITS>::kWords],
                                               uint32_t (&scales)[ScaleWords<D, G>::kWords],
                                               float neg = 1.0f) {
@@ -142,7 +146,7 @@ __device__ __forceinline__ void quantize_tail(float (&y)[D], const float* __rest
     auto fetch = [&](float (&dst)[C], int i) {
       static_for<C / 4>([&](auto qq) {
         constexpr int q = decltype(qq)::value;
-        const float4 v = *(const float4*)(lam + i * C + 4 * q);
+        const float4 v = *(const float4*)lam_at(lam, i * C + 4 * q);
         dst[4 * q + 0] = v.x;
         dst[4 * q + 1] = v.y;
         dst[4 * q + 2] = v.z;
@@ -184,7 +188,6 @@ __device__ __forceinline__ void quantize_tail(float (&y)[D], const float* __rest
       constexpr bool has_edge = group_has_edge<Sc, G>(g);
       if constexpr (has_edge) a = __builtin_fmaxf(a, me * cE);
       if constexpr (XLANE) {
-        static_assert(G == D, "a group shared by the lane pair is the lanes' whole half");
         float u = a, v = a;
         swap32(u, v);   // both lanes: (lane 0's a, lane 1's a)
         a = __builtin_fmaxf(u, v);
@@ -220,13 +223,28 @@ __device__ __forceinline__ void quantize_tail(float (&y)[D], const float* __rest
   auto emit = [&](auto clampc) {
     constexpr bool CLAMP = decltype(clampc)::value;
     constexpr int PER = BITS == 4 ? 8 : 4;
+    // The reciprocals pass through an empty asm on each path, so that the
+    // products common to both paths are not hoisted above the branch (all
+    // of them would be live at once).
+    float pB[NG], pE[NG];
+    static_for<NG>([&](auto gg) {
+      constexpr int g = decltype(gg)::value;
+      pB[g] = rB[g];
+      asm volatile("" : "+v"(pB[g]));
+      if constexpr (group_has_edge<Sc, G>(g)) {
+        pE[g] = rE[g];
+        asm volatile("" : "+v"(pE[g]));
+      } else {
+        pE[g] = pB[g];
+      }
+    });
     static_for<D / PER>([&](auto ww) {
       constexpr int w = decltype(ww)::value;
       uint32_t t[PER];
       static_for<PER>([&](auto ii) {
         constexpr int j = w * PER + decltype(ii)::value;
         constexpr int g = j / G;
-        const float r = Sc::is_edge(j) ? rE[g] : rB[g];
+        const float r = Sc::is_edge(j) ? pE[g] : pB[g];
         uint32_t b = as_u32(__builtin_fmaf(y[j], r, magic));
         if constexpr (ROT == ROT_NONE) {
           // Without a rotation the inputs are fp16 values, and exact ties
@@ -275,11 +293,14 @@ __device__ __forceinline__ void quantize_tail(float (&y)[D], const float* __rest
 // by sigma_G * e_j / lambda_j, where e_j is the inverse transform's input
 // scale.  lam: table of e_j / lambda_j for the head (LAM) or unused.
 // Sc and NEG_FROM as for quantize_tail: the coordinates from NEG_FROM on are
-// produced negated (their group scales are multiplied by neg).
-template <int D, int G, int BITS, int ROT, int VAR, bool LAM, class Sc = Scales<D, ROT, VAR>, int NEG_FROM = D>
+// produced negated (their group scales are multiplied by neg).  PER_GROUP:
+// the lambda table is read one group at a time (the scheduler would
+// otherwise issue every read at once, holding D more registers).
+template <int D, int G, int BITS, int ROT, int VAR, bool LAM, class Sc = Scales<D, ROT, VAR>, int NEG_FROM = D,
+          bool PER_GROUP = (D >= 256), class LamP = const float*>
 __device__ __forceinline__ void dequantize_head(const uint32_t (&codes)[CodeWords<D, BITS>::kWords],
                                                 const uint32_t (&scales)[ScaleWords<D, G>::kWords],
-                                                const float* __restrict__ lam, float (&y)[D], float neg = 1.0f) {
+                                                LamP lam, float (&y)[D], float neg = 1.0f) {
   constexpr int NG = D / G;
   static_assert(NEG_FROM % G == 0, "negated coordinates fill whole groups");
   constexpr float eB = (float)Sc::kInvBulk;
@@ -329,10 +350,9 @@ __device__ __forceinline__ void dequantize_head(const uint32_t (&codes)[CodeWord
       const float s = sg[g], ns = -off * sg[g];
       static_for<G>([&](auto kk) {
         constexpr int j = g * G + decltype(kk)::value;
-        y[j] = __builtin_fmaf(u[j], s, ns) * lam[j];
+        y[j] = __builtin_fmaf(u[j], s, ns) * *lam_at(lam, j);
       });
-      // d = 256 fills the register file: one group's table reads at a time
-      if constexpr (D >= 256) __builtin_amdgcn_sched_barrier(0);
+      if constexpr (PER_GROUP) __builtin_amdgcn_sched_barrier(0);
     });
   } else {
     static_for<NG>([&](auto gg) {

@@ -9,6 +9,12 @@ Buffers are torch tensors; every quantize and dequantize runs in libsrftq's
 kernels (``srftq_cache_append`` / ``srftq_cache_read``).  Per-sequence write
 positions live on the device, so a decode loop appends without a host round
 trip; ``advance`` moves them on the stream.
+
+``save`` / ``load`` keep a cache on disk in its compressed form (the pages'
+persistent-memory use of the codes): a safetensors file with the code and
+scale rows written so far, the write positions, the sign and lambda rows,
+and the format parameters as metadata.  Loading executes nothing from the
+file.
 """
 from __future__ import annotations
 
@@ -90,3 +96,51 @@ class QuantizedKVCache:
     def nbytes(self):
         """Bytes held for codes and scales."""
         return self.codes.numel() + 2 * self.scales.numel()
+
+    FORMAT = "srftq-kvcache-1"
+
+    def save(self, path):
+        """Write rows [0, max(pos)) of every layer's codes and scales, the
+        positions, signs, lambda and format parameters to ``path``
+        (safetensors)."""
+        from safetensors.torch import save_file
+        rows = min(int(self.pos.max().item()) if self.B else 0, self.capacity)
+        t = {"codes": self.codes[..., :rows, :].contiguous().cpu(),
+             "scales": self.scales[..., :rows, :].contiguous().cpu(),
+             "pos": self.pos.cpu()}
+        if self.signs is not None:
+            t["signs"] = self.signs.cpu()
+        if self.lam is not None:
+            t["lam"] = self.lam.cpu()
+        meta = {"format": self.FORMAT, "n_layers": self.n_layers, "batch": self.B, "heads": self.H, "d": self.d,
+                "capacity": self.capacity, "group": self.group, "bits": self.bits, "rot": self.rot,
+                "length": self.length, "rows": rows}
+        save_file(t, str(path), metadata={k: str(v) for k, v in meta.items()})
+
+    @classmethod
+    def load(cls, path, device="cuda", capacity=None):
+        """A cache read back from ``save``'s file, with ``capacity`` rows per
+        sequence (default: the saved capacity; never fewer than the saved
+        rows)."""
+        from safetensors import safe_open
+        with safe_open(str(path), framework="pt") as f:
+            meta = f.metadata() or {}
+            if meta.get("format") != cls.FORMAT:
+                raise ValueError(f"{path}: not a {cls.FORMAT} file")
+            t = {k: f.get_tensor(k) for k in f.keys()}
+        ints = {k: int(meta[k]) for k in ("n_layers", "batch", "heads", "d", "capacity", "group", "bits",
+                                          "length", "rows")}
+        cap = ints["capacity"] if capacity is None else int(capacity)
+        if cap < ints["rows"]:
+            raise ValueError(f"capacity {cap} is below the {ints['rows']} saved rows")
+        c = cls(ints["n_layers"], ints["batch"], ints["heads"], ints["d"], cap, ints["group"], ints["bits"],
+                meta["rot"], signs=t.get("signs"), lam=t.get("lam"), device=device)
+        rows = ints["rows"]
+        if tuple(t["codes"].shape) != tuple(c.codes.shape[:-2]) + (rows, c.codes.shape[-1]) or \
+                tuple(t["scales"].shape) != tuple(c.scales.shape[:-2]) + (rows, c.scales.shape[-1]):
+            raise ValueError(f"{path}: code or scale rows do not match the saved parameters")
+        c.codes[..., :rows, :].copy_(t["codes"])
+        c.scales[..., :rows, :].copy_(t["scales"])
+        c.pos.copy_(t["pos"])
+        c.length = ints["length"]
+        return c

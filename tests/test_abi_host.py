@@ -367,3 +367,41 @@ def test_cache_appender_rejects_cpu_tokens():
         app(torch.zeros(app.x_shape, dtype=torch.float16))
     with pytest.raises(ValueError, match="shape"):
         app(torch.zeros((2, 2, 3, 64), dtype=torch.float16))
+
+
+def test_cache_save_load_roundtrip(tmp_path):
+    """QuantizedKVCache.save / load on the host: the rows written so far, the
+    positions, signs, lambda and parameters come back unchanged, into a
+    larger capacity if asked; a smaller capacity or a foreign file is refused.
+    (No kernel runs: the buffers are filled directly.)"""
+    import torch
+
+    from kv_cache_quantization_srft_amd import kvcache
+    L, B, H, d, cap, g, bits = 2, 3, 2, 64, 40, 16, 4
+    r = np.random.default_rng(7100)
+    signs = torch.from_numpy((1 - 2 * r.integers(0, 2, (L, 2, B, H, d))).astype(np.int8))
+    lam = torch.from_numpy(r.uniform(0.5, 2.0, (L, 2, B, H, d)).astype(np.float32))
+    c = kvcache.QuantizedKVCache(L, B, H, d, cap, g, bits, "srht", signs, lam, device="cpu")
+    c.codes.copy_(torch.from_numpy(r.integers(0, 256, c.codes.shape).astype(np.uint8)))
+    c.scales.copy_(torch.from_numpy(r.standard_normal(c.scales.shape).astype(np.float16)))
+    c.pos.copy_(torch.tensor([7, 23, 11], dtype=torch.int32))
+    c.length = 23
+    f = tmp_path / "cache.safetensors"
+    c.save(f)
+    for capacity in (None, 64):
+        c2 = kvcache.QuantizedKVCache.load(f, device="cpu", capacity=capacity)
+        assert (c2.n_layers, c2.B, c2.H, c2.d, c2.group, c2.bits, c2.rot, c2.length) == \
+            (L, B, H, d, g, bits, "srht", 23)
+        assert c2.capacity == (cap if capacity is None else capacity)
+        assert torch.equal(c2.pos, c.pos)
+        assert torch.equal(c2.signs, signs) and torch.equal(c2.lam, lam)
+        assert torch.equal(c2.codes[..., :23, :], c.codes[..., :23, :])
+        assert torch.equal(c2.scales[..., :23, :].view(torch.int16), c.scales[..., :23, :].view(torch.int16))
+        assert int(c2.codes[..., 23:, :].abs().sum()) == 0   # rows past the saved ones start empty
+    with pytest.raises(ValueError):
+        kvcache.QuantizedKVCache.load(f, device="cpu", capacity=20)
+    from safetensors.torch import save_file
+    g2 = tmp_path / "other.safetensors"
+    save_file({"codes": torch.zeros(1, dtype=torch.uint8)}, str(g2), metadata={"format": "x"})
+    with pytest.raises(ValueError):
+        kvcache.QuantizedKVCache.load(g2, device="cpu")

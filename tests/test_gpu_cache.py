@@ -238,3 +238,32 @@ def test_prepared_appender_matches_cache_append():
         app(xs[0].float())
     with pytest.raises(ValueError):
         app(torch.cat([xs[0], xs[1]], dim=1))
+
+
+def test_container_saved_and_loaded_reads_the_same(tmp_path):
+    """A cache filled on the GPU, saved and loaded back (into a larger
+    capacity), reads back bit for bit what the original reads, and goes on
+    appending from the saved positions."""
+    L, B, H, d, cap, g, bits = 2, 2, 2, 128, 48, 16, 4
+    r = np.random.default_rng(5500)
+    signs = (1 - 2 * r.integers(0, 2, (L, 2, B, H, d))).astype(np.int8)
+    lam = r.uniform(0.5, 2.0, (L, 2, B, H, d)).astype(np.float32)
+    cache = kvcache.QuantizedKVCache(L, B, H, d, cap, g, bits, "srft", dev(signs), dev(lam))
+    for l in range(L):
+        cache.update(l, dev(r.standard_normal((B, 33, H, d)).astype(np.float16)),
+                     dev(r.standard_normal((B, 33, H, d)).astype(np.float16)))
+    torch.cuda.synchronize()
+    f = tmp_path / "c.safetensors"
+    cache.save(f)
+    back = kvcache.QuantizedKVCache.load(f, device="cuda", capacity=64)
+    for l in range(L):
+        for a, b in zip(cache.read(l), back.read(l)):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    k = dev(r.standard_normal((B, 1, H, d)).astype(np.float16))
+    for c in (cache, back):
+        for l in range(L):
+            c.update(l, k, k)
+    torch.cuda.synchronize()
+    for l in range(L):
+        for a, b in zip(cache.read(l), back.read(l)):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16))
