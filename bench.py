@@ -605,7 +605,9 @@ def householder_timing(steps: int) -> dict:
             "quantize_TFLOPs": tq_tf, "dequantize_TFLOPs": tdq_tf,
             "quantize_mfma_frac": tq_tf / MFMA_F16_PEAK_TFLOPS,
             "dequantize_mfma_frac": tdq_tf / MFMA_F16_PEAK_TFLOPS,
-            "executed_fp16_passes": {"quantize": 2, "dequantize": 3},
+            # fp16 MFMA passes over the product (hi/lo operand parts): groups
+            # of 16 and 32 dequantize in two, groups of 8 in three
+            "executed_fp16_passes": {"quantize": 2, "dequantize": 2 if w.group >= 16 else 3},
             "quantize_hbm_frac": bpv * n / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
             "dequantize_hbm_frac": bpv * n / (dq_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
             "reconstruction_rel_l2": rel,

@@ -1,9 +1,12 @@
 """Build libsrftq.so (HIP kernels for gfx950 + the C ABI) in the package dir.
 
-    python -m kv_cache_quantization_srft_amd.build [--jobs N] [--incremental]
+    python -m kv_cache_quantization_srft_amd.build [--jobs N] [--incremental] [--poison]
 
 Each translation unit is compiled by hipcc in parallel, then linked into one
-shared library next to this file.
+shared library next to this file.  --poison builds the debug variant
+libsrftq_poison.so instead (SRFTQ_LDS_POISON=1: the single-wave streaming
+kernels fill their LDS buffers with 0xff bytes before each use), which the
+tests load through SRFTQ_LIBRARY.
 """
 from __future__ import annotations
 
@@ -19,6 +22,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsrftq.so")
+BUILD_POISON = os.path.join(PKG, "_build_poison")
+LIB_POISON = os.path.join(PKG, "libsrftq_poison.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -57,10 +62,12 @@ def _up_to_date(src: str, obj: str, flags: list[str]) -> bool:
     return all(os.path.exists(f) and os.path.getmtime(f) <= t for f in deps + [src])
 
 
-def _compile(src: str, incremental: bool = False) -> str:
-    obj = os.path.join(BUILD, src + ".o")
+def _compile(src: str, incremental: bool = False, poison: bool = False) -> str:
+    obj = os.path.join(BUILD_POISON if poison else BUILD, src + ".o")
     path = os.path.join(CSRC, src)
     flags = DEVICE_FLAGS if src.endswith(".hip") else HOST_FLAGS
+    if poison:
+        flags = flags + ["-DSRFTQ_LDS_POISON=1"]
     if src.startswith("k_attn"):
         # MFMA results in VGPRs: the attention kernels read every score tile
         # back for VALU work, which AGPR results would have to copy first
@@ -76,24 +83,26 @@ def _compile(src: str, incremental: bool = False) -> str:
     return obj
 
 
-def build(jobs: int | None = None, verbose: bool = False, incremental: bool = False) -> str:
+def build(jobs: int | None = None, verbose: bool = False, incremental: bool = False, poison: bool = False) -> str:
     """Compile every unit (incremental: only those whose object is older
-    than the source or a header it includes) and link libsrftq.so."""
-    os.makedirs(BUILD, exist_ok=True)
+    than the source or a header it includes) and link libsrftq.so (poison:
+    the debug variant libsrftq_poison.so)."""
+    lib_path = LIB_POISON if poison else LIB
+    os.makedirs(BUILD_POISON if poison else BUILD, exist_ok=True)
     # the d = 256 units take several times longer: start them first
     srcs = sorted(sources(), key=lambda f: (0 if "d256" in f else 1, f))
     jobs = jobs or min(len(srcs), os.cpu_count() or 4, 16)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda f: _compile(f, incremental), srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda f: _compile(f, incremental, poison), srcs))
+    tmp = lib_path + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib_path)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib_path}")
+    return lib_path
 
 
 if __name__ == "__main__":
@@ -101,6 +110,7 @@ if __name__ == "__main__":
     ap.add_argument("--jobs", type=int, default=None)
     ap.add_argument("--incremental", action="store_true",
                     help="recompile only units whose source or included headers changed")
+    ap.add_argument("--poison", action="store_true", help="build the LDS-poison debug variant")
     a = ap.parse_args()
-    build(a.jobs, verbose=True, incremental=a.incremental)
+    build(a.jobs, verbose=True, incremental=a.incremental, poison=a.poison)
     sys.exit(0)

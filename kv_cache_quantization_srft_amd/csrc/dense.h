@@ -526,4 +526,274 @@ __global__ __launch_bounds__(2 * D, 2) void dequantize_dense_kernel(const float*
   }
 }
 
+// ----------------------------------------------------------------------------
+// x = s . Q^T yhat for groups of 16 or 32 coordinates, in two MFMA passes.
+//   The codes themselves are the B operand (small integers, exact in fp16);
+//   1/lambda_c rides in the A operand, 2^sh s_i Q[c, i] / lambda_c (sh per
+//   head, putting the largest 1/lambda_c in [2^13, 2^14), so that |A| stays
+//   below 2^14 for an orthogonal Q) as fp16 hi + lo parts; each group's
+//   partial sum over its one or two 16-wide k-blocks (two MFMAs each, the
+//   first with a zero accumulator) is multiplied in fp32 by the token's group
+//   scale sigma and added to the output accumulator.  Products are exact and
+//   sums fp32, as in the three-pass kernel; only the operand split differs.
+// ----------------------------------------------------------------------------
+template <int D, int G, int BITS>
+__global__ __launch_bounds__(2 * D, 2) void dequantize_dense2_kernel(const float* __restrict__ Q,
+                                                                  const uint8_t* __restrict__ codes,
+                                                                  const uint16_t* __restrict__ scales,
+                                                                  const int8_t* __restrict__ signs,
+                                                                  const float* __restrict__ lambda,
+                                                                  uint16_t* __restrict__ x_out,
+                                                                  DenseGeo a) {
+  static_assert(D == 64 || D == 128 || D == 256, "head size");
+  static_assert(G == 16 || G == 32, "a group is one or two 16-wide k-blocks");
+  constexpr int KS = D / 16;
+  constexpr int KPG = G / 16;             // k-blocks per group
+  constexpr int PITCH = 2 * D + 16;       // LDS row pitch of the fp16 code tile
+  constexpr int TILE = 64 * PITCH;
+  constexpr int NG = D / G;
+  constexpr int STAGE = TILE + 4 * 64 * NG;   // code tile, then sigma as [group][token] fp32
+  constexpr int NT = 2 * D;
+  constexpr int LPT = D / 32;             // prep lanes per token (32 coordinates each)
+  constexpr int CB = D * BITS / 8;
+  constexpr int GPL = 32 / G;             // groups per prep lane
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE + 4 * D];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = lane & 31, hf = lane >> 5;
+  const int64_t first = (int64_t)blockIdx.x * a.per_block;
+  int64_t last = first + a.per_block;
+  last = last < a.n_tiles ? last : a.n_tiles;
+  if (first >= last) return;
+  const uint32_t lds0 = lds_addr(smem);
+  const uint32_t ilam_lds = lds0 + 2 * STAGE;   // 1 / lambda of the current head
+
+  // prep role: token pr (0..63) of the tile, coordinates 32 pp .. +31
+  // (re-derived in each use, see build)
+  uint32_t cw[BITS];       // this lane's 32 codes: int4 4 dwords, int8 8 dwords
+  uint32_t sw[1];
+  auto prep_ids = [&](int& pr, int& pp) {
+    int t = tid;
+    asm volatile("" : "+v"(t));
+    pr = t / LPT;
+    pp = t % LPT;
+  };
+  // rows past T read 0 (codes 0, scale 0: their outputs are not stored)
+  auto load = [&](int bh, int k) {
+    int pr, pp;
+    prep_ids(pr, pp);
+    const int64_t t0 = (int64_t)k * 64;
+    const int64_t left = a.T - t0;
+    const uint32_t rows = left < 64 ? (uint32_t)left : 64u;
+    const int64_t row0 = (int64_t)bh * a.T + t0;
+    const auto crs = make_rsrc(codes + row0 * CB, rows * CB);
+    const auto srs = make_rsrc(scales + row0 * NG, rows * NG * 2);
+    static_for<BITS / 4>([&](auto ii) {
+      constexpr int i = decltype(ii)::value;
+      const w32x4_t v = __builtin_bit_cast(
+          w32x4_t, __builtin_amdgcn_raw_buffer_load_b128(crs, (uint32_t)(pr * CB + pp * (4 * BITS) + 16 * i), 0, kNT));
+      static_for<4>([&](auto ee) { cw[4 * i + decltype(ee)::value] = v[decltype(ee)::value]; });
+    });
+    const uint32_t soff = 2u * (uint32_t)(pr * NG + pp * GPL);
+    if constexpr (GPL == 1) sw[0] = __builtin_amdgcn_raw_buffer_load_b16(srs, soff, 0, 0);
+    else sw[0] = __builtin_amdgcn_raw_buffer_load_b32(srs, soff, 0, 0);
+  };
+  // the codes as fp16 integers q into the stage's tile, sigma into its table
+  auto prep = [&](int stage) {
+    int pr, pp;
+    prep_ids(pr, pp);
+    const uint32_t sb = lds0 + (uint32_t)(stage * STAGE);
+    w32x4_t ch[4];   // 16-byte chunks: coordinates 32 pp + 8 c .. + 7
+    if constexpr (BITS == 4) {
+      // nibble + 8 (offset binary) into the low mantissa bits of 1024.0h,
+      // then - 1032 per half: exact
+      static_for<4>([&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        const uint32_t v = cw[c] ^ 0x88888888u;
+        static_for<4>([&](auto kk) {
+          constexpr int k = decltype(kk)::value;
+          const uint32_t b = v >> (8 * k);
+          const uint32_t hw = 0x64006400u | (b & 0xfu) | ((b & 0xf0u) << 12);
+          half2_t h = __builtin_bit_cast(half2_t, hw) - half2_t{(_Float16)1032.0f, (_Float16)1032.0f};
+          ch[c][k] = __builtin_bit_cast(uint32_t, h);
+        });
+      });
+    } else {
+      static_for<4>([&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        static_for<2>([&](auto ww) {
+          constexpr int w = decltype(ww)::value;
+          const uint32_t v = cw[2 * c + w] ^ 0x80808080u;
+          static_for<2>([&](auto kk) {
+            constexpr int k = decltype(kk)::value;
+            const uint32_t b = v >> (16 * k);
+            const uint32_t hw = 0x64006400u | (b & 0xffu) | ((b & 0xff00u) << 8);
+            half2_t h = __builtin_bit_cast(half2_t, hw) - half2_t{(_Float16)1152.0f, (_Float16)1152.0f};
+            ch[c][2 * w + k] = __builtin_bit_cast(uint32_t, h);
+          });
+        });
+      });
+    }
+    // write k of lane pp stores chunk (k + 2 (pp / 4)) % 4: lanes pp and pp + 4
+    // (64 bytes x 4 apart) then hit different banks
+    const int rot = 2 * ((pp >> 2) & 1);
+    static_for<4>([&](auto kk) {
+      constexpr int k = decltype(kk)::value;
+      const int c = (k + rot) & 3;
+      lds_write128(sb + (uint32_t)(pr * PITCH + 16 * (4 * pp + c)), rot ? ch[(k + 2) & 3] : ch[k]);
+    });
+    static_for<GPL>([&](auto gg) {
+      constexpr int gi = decltype(gg)::value;
+      const int g = pp * GPL + gi;
+      lds_writef(sb + TILE + 4u * (uint32_t)(g * 64 + pr), gi == 0 ? hlo(sw[0]) : hhi(sw[0]));
+    });
+  };
+
+  f16x8_t ahi[KS], alo[KS];
+  int sh = 0;   // this head's A scaling exponent
+  auto build = [&](int bh) {
+    // lane indices re-derived here: the addresses built from them are not
+    // held in registers through the tile loop
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int jb = ln & 31, hb = ln >> 5;
+    // sh from the largest 1/lambda of the head (every wave computes it)
+    float m = 0.0f;
+    static_for<D / 64>([&](auto ii) {
+      m = __builtin_fmaxf(m, lds_readf(ilam_lds + 4u * (uint32_t)(ln + 64 * decltype(ii)::value)));
+    });
+    static_for<6>([&](auto ii) { m = __builtin_fmaxf(m, __shfl_xor(m, 1 << decltype(ii)::value)); });
+    sh = __builtin_amdgcn_readfirstlane(m > 0.0f ? 14 - __builtin_amdgcn_frexp_expf(m) : 0);
+    const float* Qh = Q + (int64_t)bh * a.q_stride;
+    const int8_t* sg = signs + (int64_t)bh * a.sign_stride;
+    const int r = dense_row(wave, jb);
+    const float s = __builtin_ldexpf(sg[r] < 0 ? -1.0f : 1.0f, sh);
+    static_for<KS>([&](auto kk) {
+      constexpr int ks = decltype(kk)::value;
+      const int c0 = 16 * ks + 8 * hb;
+      const w32x4_t l0 = lds_read128(ilam_lds + 4u * (uint32_t)c0);
+      const w32x4_t l1 = lds_read128(ilam_lds + 4u * (uint32_t)(c0 + 4));
+      float p[8];
+      static_for<8>([&](auto ee) {
+        constexpr int e = decltype(ee)::value;
+        const float il = as_f32(e < 4 ? l0[e] : l1[e - 4]);
+        p[e] = Qh[(int64_t)(c0 + e) * D + r] * il * s;
+      });
+      split8(p, ahi[ks], alo[ks]);
+      __builtin_amdgcn_sched_barrier(0);   // one block's loads at a time
+    });
+  };
+  auto build_ilam = [&](int bh) {
+    for (int c = tid; c < D; c += NT)
+      lds_writef(ilam_lds + 4u * (uint32_t)c, lambda ? 1.0f / lambda[(int64_t)bh * D + c] : 1.0f);
+  };
+
+  // Tiles first .. last-1 of the block, head by head; (bh, k) the current
+  // tile's head and index within the head, kept as counters.
+  int bh = (int)(first / a.tiles_t);
+  int k = (int)(first - (int64_t)bh * a.tiles_t);
+  // prologue: the first tile's B operands
+  build_ilam(bh);
+  load(bh, k);
+  __syncthreads();
+  prep(0);
+  const uint32_t xstride = (uint32_t)a.H * (2 * D);
+  const uint32_t xlane = (uint32_t)j * xstride + 2u * (uint32_t)(32 * wave + 16 * hf);
+  int64_t it = first;
+  while (it < last) {
+    // the matrix rows of this head; its loads waited for here, so nothing
+    // issued on this path is pending inside the tile loop
+    build(bh);
+    __builtin_amdgcn_s_waitcnt(0);
+    const int64_t seg_end = (it - k) + a.tiles_t < last ? (it - k) + a.tiles_t : last;
+    for (; it < seg_end; ++it, ++k) {
+      const int stage = (int)((it - first) & 1);
+      __syncthreads();   // this stage's tile is written; the other stage is no longer read
+      const bool more = it + 1 < last;
+      const bool head_ends = k + 1 == a.tiles_t;
+      if (more) load(head_ends ? bh + 1 : bh, head_ends ? 0 : k + 1);
+
+      const uint32_t sb = lds0 + (uint32_t)(stage * STAGE);
+      const uint32_t rb = sb + (uint32_t)(j * PITCH + 16 * hf);
+      const int64_t t0 = (int64_t)k * 64;
+      const int b = bh / a.H, h = bh - b * a.H;
+      const int64_t left = a.T - t0;
+      const int rows = left < 64 ? (int)left : 64;
+      const uint16_t* xbase = x_out + (((int64_t)b * a.T + t0) * a.H + h) * D;
+      static_for<2>([&](auto nn) {
+        constexpr int n = decltype(nn)::value;
+        const int tok = 32 * n + j;
+        f32x16_t acc = zero16();
+        f32x16_t part[2];
+        // software-pipelined by group: group gs's MFMAs are issued before
+        // group gs - 1's sigma scaling, so the VALU work overlaps the matrix
+        // cores; a scheduling barrier per step keeps the zero-accumulator
+        // MFMAs of later groups from being hoisted (each would hold 16 more
+        // registers)
+        constexpr int NGK = KS / KPG;
+        static_for<NGK + 1>([&](auto gg) {
+          constexpr int gs = decltype(gg)::value;
+          if constexpr (gs < NGK) {
+            f16x8_t bq[KPG];
+            static_for<KPG>([&](auto qq) {
+              constexpr int q = decltype(qq)::value;
+              bq[q] = __builtin_bit_cast(f16x8_t, lds_read128(rb + 32 * n * PITCH + 32 * (gs * KPG + q)));
+            });
+            static_for<KPG>([&](auto qq) {
+              constexpr int q = decltype(qq)::value;
+              constexpr int ks = gs * KPG + q;
+              if constexpr (q == 0)
+                part[gs & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[ks], bq[q], zero16(), 0, 0, 0);
+              else
+                part[gs & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[ks], bq[q], part[gs & 1], 0, 0, 0);
+              part[gs & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo[ks], bq[q], part[gs & 1], 0, 0, 0);
+            });
+          }
+          if constexpr (gs > 0) {
+            constexpr int g = gs - 1;
+            const float sgm = lds_readf(sb + TILE + 4u * (uint32_t)(g * 64 + tok));
+            static_for<16>([&](auto ee) {
+              constexpr int e = decltype(ee)::value;
+              acc[e] = __builtin_fmaf(sgm, part[g & 1][e], acc[e]);
+            });
+            // the sums stay here: sunk to the end, every group's partial
+            // would be live at once
+            asm volatile("" : "+v"(acc));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        });
+
+        // lane (j, hf): outputs 32w + 16hf .. +15 of token 32n + j
+        uint32_t o[8];
+        static_for<8>([&](auto ee) {
+          constexpr int e = decltype(ee)::value;
+          o[e] = pack_f16x2(__builtin_ldexpf(acc[2 * e], -sh), __builtin_ldexpf(acc[2 * e + 1], -sh));
+        });
+        // rows past T fall outside the resource's bounds and are dropped; one
+        // resource per 32-token block, so both share the lane offset
+        const int rn = rows - 32 * n;
+        const uint32_t nrec = rn > 0 ? (uint32_t)(rn - 1) * xstride + 2 * D : 0u;
+        const auto xrs = make_rsrc((const uint8_t*)xbase + (int64_t)(32 * n) * xstride, nrec);
+        const w32x4_t v0 = {o[0], o[1], o[2], o[3]}, v1 = {o[4], o[5], o[6], o[7]};
+        __builtin_amdgcn_raw_buffer_store_b128(v0, xrs, xlane, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(v1, xrs, xlane + 16, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);   // one block's state live at a time
+      });
+
+      if (more) {
+        if (head_ends) {
+          __syncthreads();   // every wave has built this head's A operands
+          build_ilam(bh + 1);
+          __syncthreads();
+        }
+        prep(stage ^ 1);
+      }
+    }
+    ++bh;
+    k = 0;
+  }
+}
+
 }  // namespace srftq

@@ -368,6 +368,9 @@ __global__ __launch_bounds__(64) SRFTQ_QUANT_OCC void quantize_kernel(const uint
     const int64_t t0 = (int64_t)c.k * 64;
     const int64_t left = a.T - t0;
     nv = left < 64 ? (int)left : 64;
+    lds_poison<XT::kBytes>(lds, lane);
+    if constexpr (LAM) lds_poison<4 * D>(lam_lds + buf * D, lane);
+    lds_poison<4 * SM>(smask + buf * SM, lane);
     XT::issue((const uint8_t*)x + row_index(a, c.bh, t0) * (int64_t)(2 * D), rsb, nv, lane, plan, lds);
     if constexpr (LAM) issue_row_f32<D>(lambda + (int64_t)c.bh * D, lane, (uint8_t*)(lam_lds + buf * D));
     issue_signs<D>(signs + (int64_t)c.bh * a.sign_stride, lane, smask + buf * SM);
@@ -494,6 +497,10 @@ __global__ __launch_bounds__(64) SRFTQ_DEQUANT_OCC void dequantize_kernel(const 
     const int64_t left = a.T - t0;
     nv = left < 64 ? (int)left : 64;
     const int64_t r0 = cache_row(a, c.bh, t0);
+    lds_poison<CT::kBytes>(ctile, lane);
+    lds_poison<sizeof(stile)>(stile, lane);
+    if constexpr (LAM) lds_poison<4 * D>(lam_lds + buf * D, lane);
+    lds_poison<4 * SM>(smask + buf * SM, lane);
     CT::issue(codes_in + r0 * CB, rsb_c, nv, lane, cplan, ctile);
     ST::issue((const uint8_t*)scales_in + r0 * SB, rsb_s, nv, lane, splan, stile);
     if constexpr (LAM) issue_row_f32<D>(lambda + (int64_t)c.bh * D, lane, (uint8_t*)(lam_lds + buf * D));
@@ -556,6 +563,7 @@ __global__ __launch_bounds__(64) SRFTQ_DEQUANT_OCC void dequantize_kernel(const 
     uint8_t* obase = (uint8_t*)x_out + row_index(a, now.bh, (int64_t)now.k * 64) * (int64_t)(2 * D);
     static_for<2>([&](auto hh) {
       constexpr int h = decltype(hh)::value;
+      lds_poison<OT::kBytes>(otile, lane);
       {
         uint8_t* row = otile + lane * D;
         int s = OT::swz(lane);

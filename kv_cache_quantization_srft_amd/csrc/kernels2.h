@@ -289,6 +289,9 @@ void quantize2_kernel(const uint16_t* __restrict__ x, const int8_t* __restrict__
     const int64_t t0 = (int64_t)c.k * 32;
     const int64_t left = a.T - t0;
     nv = left < 32 ? (int)left : 32;
+    lds_poison<XT::kBytes>(lds, lane);
+    if constexpr (LAM) lds_poison<4 * D>(lam_lds + buf * D, lane);
+    lds_poison<D>(sraw + buf * (D / 4), lane);
     // the DMA offsets are recomputed per tile rather than held in registers
     typename XT::Plan plan;
     plan.init(lane, rsb);
@@ -486,8 +489,12 @@ void dequantize2_kernel(const uint8_t* __restrict__ codes_in, const uint16_t* __
   constexpr int SEGW = Q * BITS / 32;                 // code words per run (balanced layout)
   using CT = RowTile<CB, 32>;
   using ST = RowTile<SB, 32>;
-  using OT = RowTile<D, 32>;             // one role's half rows (D bytes each)
-  constexpr int NST = 2 * OT::kInst;     // global stores per tile
+  // output staging in NR rounds (two at d = 256, where whole rows would not
+  // fit the LDS of two waves per SIMD), CPR chunks per lane and round
+  constexpr int NR = D >= 256 ? 2 : 1;
+  constexpr int CPR = L / 8 / NR;
+  using OT = RowTile<2 * D / NR, 32>;    // a round's share of the 32 rows
+  constexpr int NST = NR * OT::kInst;    // global stores per tile
   __shared__ __attribute__((aligned(16))) uint8_t ctile[CT::kBytes];
   __shared__ __attribute__((aligned(16))) uint8_t stile[ST::kBytes < 16 ? 16 : ST::kBytes];
   __shared__ __attribute__((aligned(16))) uint8_t otile[OT::kBytes];
@@ -511,6 +518,10 @@ void dequantize2_kernel(const uint8_t* __restrict__ codes_in, const uint16_t* __
     const int64_t left = a.T - t0;
     nv = left < 32 ? (int)left : 32;
     const int64_t r0 = cache_row(a, c.bh, t0);
+    lds_poison<CT::kBytes>(ctile, lane);
+    lds_poison<sizeof(stile)>(stile, lane);
+    if constexpr (LAM) lds_poison<4 * D>(lam_lds + buf * D, lane);
+    lds_poison<D>(sraw + buf * (D / 4), lane);
     typename CT::Plan cplan;
     cplan.init(lane, CB);
     typename ST::Plan splan;
@@ -706,9 +717,11 @@ void dequantize2_kernel(const uint8_t* __restrict__ codes_in, const uint16_t* __
     // Output dwords of lane p: SRFT and none: dwords 64p .. 64p+63 of the
     // row (L/2 = D/4 in general); SRHT: dwords 32p .. 32p+31 (top) and
     // 64 + 32p .. (bottom); gchunk(c, p) is the row chunk of the lane's
-    // chunk c.  They leave in two rounds: in round r every lane stages its
-    // chunks r L/16 .. (r+1) L/16 - 1, signs applied, into LDS row t (role
-    // 0's then role 1's), and the wave stores the staged rows.
+    // chunk c.  They leave in NR rounds: in round r every lane stages its
+    // chunks r CPR .. (r+1) CPR - 1, signs applied, into LDS row t (role 0's
+    // then role 1's), and the wave stores the staged rows (at d = 256 a
+    // round's pieces are 128-byte halves of the lanes' half rows, whole
+    // cache lines).
     auto gchunk = [&](int c, int role) {
       if constexpr (ROT == ROT_SRHT)
         return (c < L / 16) ? (L / 16) * role + c : L / 8 + (L / 16) * role + (c - L / 16);
@@ -723,17 +736,19 @@ void dequantize2_kernel(const uint8_t* __restrict__ codes_in, const uint16_t* __
     const uint32_t t_o = (uint32_t)lane_o & 31u, p_o = (uint32_t)lane_o >> 5;
     const uint32_t wrow = t_o * OT::kRowLds, wswz = (uint32_t)OT::swz((int)t_o);
     // stores: lane l moves chunk jl = l % kCpr of the staged rows v0 + i kRpi,
-    // which belongs to role jl / (L/16); g0 is its byte offset in round 0
+    // which belongs to role jl / CPR; g0 is its byte offset in round 0
     const uint32_t v0 = (uint32_t)lane_o / OT::kCpr, jl = (uint32_t)lane_o % OT::kCpr;
-    const uint32_t g0 = v0 * rsb_x + 16u * (uint32_t)gchunk((int)(jl % (L / 16)), (int)(jl / (L / 16)));
-    constexpr uint32_t kRoundStep = ROT == ROT_SRHT ? 2 * L : L;   // bytes between a chunk's rounds
-    static_for<2>([&](auto rr) {
+    const uint32_t g0 = v0 * rsb_x + 16u * (uint32_t)gchunk((int)(jl % CPR), (int)(jl / CPR));
+    // bytes between a chunk's rounds (two rounds: CPR = L/16)
+    constexpr uint32_t kRoundStep = ROT == ROT_SRHT ? 2 * L : L;
+    static_for<NR>([&](auto rr) {
       constexpr int r = decltype(rr)::value;
-      static_for<L / 16>([&](auto jj) {
+      lds_poison<OT::kBytes>(otile, lane_o);
+      static_for<CPR>([&](auto jj) {
         constexpr int j = decltype(jj)::value;
-        constexpr int c = r * (L / 16) + j;
+        constexpr int c = r * CPR + j;
         const uint4 m = *(const uint4*)(smask + 4 * gchunk(c, (int)p_o));
-        *(uint4*)(otile + wrow + 16 * (((L / 16) * p_o + j) ^ wswz)) =
+        *(uint4*)(otile + wrow + 16 * ((CPR * p_o + j) ^ wswz)) =
             make_uint4(o[4 * c] ^ m.x, o[4 * c + 1] ^ m.y, o[4 * c + 2] ^ m.z, o[4 * c + 3] ^ m.w);
       });
       wave_fence();

@@ -81,6 +81,7 @@ __global__ __launch_bounds__(64) void quantize_lane_kernel(const uint16_t* __res
   const int nv = a.T - t0 < 64 ? (int)(a.T - t0) : 64;
   // the tile by LDS-DMA: slot p = 64 i + lane holds chunk (p % CH) ^ swz of
   // row p / CH (rows past T re-read the last row)
+  lds_poison<64 * 2 * D>(xt, lane);
   {
     const uint8_t* base = (const uint8_t*)x + row_index(a, bh, t0) * (2 * D);
     const uint32_t stride = (uint32_t)a.H * (2 * D);
@@ -121,6 +122,7 @@ __global__ __launch_bounds__(64) void quantize_lane_kernel(const uint16_t* __res
   constexpr int SE = SB % 16 == 0 ? 16 : SB % 4 == 0 ? 4 : 2;   // scale store granule
   uint8_t* oc = xt;
   uint8_t* osc = xt + 64 * CB;
+  lds_poison<64 * 2 * D>(xt, lane);   // (debug builds; after the row reads, in LDS order)
   static_for<CB / 16>([&](auto cc) {
     constexpr int c = decltype(cc)::value;
     *(uint4*)(oc + lane * CB + 16 * c) = make_uint4(codes[4 * c], codes[4 * c + 1], codes[4 * c + 2], codes[4 * c + 3]);
@@ -245,6 +247,7 @@ __global__ __launch_bounds__(64) void dequantize_lane_kernel(const uint8_t* __re
   });
   // the output tile through LDS: lane writes its row, then every lane stores
   // slot p = 64 i + lane (chunk (p % CH) ^ swz of row p / CH), whole rows at a time
+  lds_poison<64 * 2 * D>(xo, lane);
   {
     const int sw = lane_swz(lane);
     static_for<CH>([&](auto cc) {

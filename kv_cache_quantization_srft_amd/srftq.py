@@ -17,7 +17,9 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libsrftq.so")
+# SRFTQ_LIBRARY: another build of the same library to load instead (the
+# LDS-poison debug build, libsrftq_poison.so, in the tests)
+LIB_PATH = os.environ.get("SRFTQ_LIBRARY") or os.path.join(_PKG, "libsrftq.so")
 
 (SRFTQ_OK, SRFTQ_ERR_NULL, SRFTQ_ERR_SHAPE, SRFTQ_ERR_UNSUPPORTED, SRFTQ_ERR_ALIGN, SRFTQ_ERR_HIP,
  SRFTQ_ERR_CAPACITY) = range(7)

@@ -7,8 +7,11 @@ GPU's own Householder builder is checked separately against the oracle's.
 Bars (oracle/compare.py): codes bit-exact except +-1 at rounding ties or in a
 group whose fp16 scale sits on a rounding boundary; scales within one fp16
 step; dequantized values within one fp16 ulp plus the fp32 budget
-2^-18 ||x||.  The GPU product splits Q (and yhat) into two fp16 parts
-(about 2^-22 relative) with fp32 sums, well inside both bars.
+2^-18 ||x||.  The GPU product splits Q into two fp16 parts (about 2^-22
+relative) with fp32 sums, well inside both bars; dequantize takes the codes
+themselves as the exact second operand (1/lambda inside Q's parts, each
+group's sigma applied to its fp32 partial) for groups of 16 and 32, and
+splits yhat = q sigma / lambda into two parts as well for groups of 8.
 """
 import numpy as np
 import pytest
