@@ -628,6 +628,9 @@ def main():
                          "steps run at the clocks a sustained load settles to")
     ap.add_argument("--workload", default="outlier")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--section-launches", type=int, default=None,
+                    help="launches per direction in the roundtrip, wide-head and tiny sections "
+                         "(default: max(100, steps)); fewer for profiler passes")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode-append, decode-attention and d = 96 figures")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -778,7 +781,7 @@ def main():
     hh = None if args.no_decode else householder_timing(min(args.steps, 20))
     del xd, codes, scales, codes2, scales2
     torch.cuda.empty_cache()
-    launches = max(100, args.steps)
+    launches = args.section_launches or max(100, args.steps)
     c5 = None if args.no_decode else roundtrip_timing(launches)
     c4 = None if args.no_decode else wide_timing(launches)
     tiny = None if args.no_decode else tiny_timing(launches)

@@ -733,30 +733,38 @@ __global__ __launch_bounds__(2 * D, 2) void dequantize_dense2_kernel(const float
         // MFMAs of later groups from being hoisted (each would hold 16 more
         // registers)
         constexpr int NGK = KS / KPG;
+        // B operands one group ahead, sigma one step ahead: the LDS reads'
+        // latency is covered by the step before their use
+        f16x8_t bq[2][KPG];
+        float sgm[2];
+        auto read_b = [&](auto gc) {
+          constexpr int gb = decltype(gc)::value;
+          static_for<KPG>([&](auto qq) {
+            constexpr int q = decltype(qq)::value;
+            bq[gb & 1][q] = __builtin_bit_cast(f16x8_t, lds_read128(rb + 32 * n * PITCH + 32 * (gb * KPG + q)));
+          });
+        };
+        read_b(std::integral_constant<int, 0>{});
         static_for<NGK + 1>([&](auto gg) {
           constexpr int gs = decltype(gg)::value;
+          if constexpr (gs + 1 < NGK) read_b(std::integral_constant<int, gs + 1>{});
           if constexpr (gs < NGK) {
-            f16x8_t bq[KPG];
-            static_for<KPG>([&](auto qq) {
-              constexpr int q = decltype(qq)::value;
-              bq[q] = __builtin_bit_cast(f16x8_t, lds_read128(rb + 32 * n * PITCH + 32 * (gs * KPG + q)));
-            });
+            sgm[gs & 1] = lds_readf(sb + TILE + 4u * (uint32_t)(gs * 64 + tok));
             static_for<KPG>([&](auto qq) {
               constexpr int q = decltype(qq)::value;
               constexpr int ks = gs * KPG + q;
               if constexpr (q == 0)
-                part[gs & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[ks], bq[q], zero16(), 0, 0, 0);
+                part[gs & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[ks], bq[gs & 1][q], zero16(), 0, 0, 0);
               else
-                part[gs & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[ks], bq[q], part[gs & 1], 0, 0, 0);
-              part[gs & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo[ks], bq[q], part[gs & 1], 0, 0, 0);
+                part[gs & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[ks], bq[gs & 1][q], part[gs & 1], 0, 0, 0);
+              part[gs & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo[ks], bq[gs & 1][q], part[gs & 1], 0, 0, 0);
             });
           }
           if constexpr (gs > 0) {
             constexpr int g = gs - 1;
-            const float sgm = lds_readf(sb + TILE + 4u * (uint32_t)(g * 64 + tok));
             static_for<16>([&](auto ee) {
               constexpr int e = decltype(ee)::value;
-              acc[e] = __builtin_fmaf(sgm, part[g & 1][e], acc[e]);
+              acc[e] = __builtin_fmaf(sgm[g & 1], part[g & 1][e], acc[e]);
             });
             // the sums stay here: sunk to the end, every group's partial
             // would be live at once

@@ -59,15 +59,17 @@ struct QConst {
   static constexpr uint32_t kHi = kMagicBits + (uint32_t)kQmax;   // bits of q = +qmax
 };
 
-// fp32(1/sigma), correctly rounded, for sigma an fp16 value.  1/sigma =
+// fp32(1/sigma), correctly rounded, for sigma an fp16 value (normal in fp32).
+// v_rcp_f32 gives r0 = (1 + d)/sigma with |d| below 2^-22; e = 1 - sigma r0
+// = -d is exact in one FMA (sigma has 11 significant bits, so the product is
+// a multiple of 2^-34 within 2^-22 of 1), and r0 + r0 e = (1 - d^2)/sigma
+// rounded once is within 2^-44 of 1/sigma before its rounding.  1/sigma =
 // 2^-e / m with an integer m < 2^11 is never within 2^-36 (relative) of an
-// fp32 rounding midpoint, so an fp64 reciprocal (plus one Newton step) rounded
-// to fp32 is the correctly rounded fp32 reciprocal.  One per group.
+// fp32 rounding midpoint, so that rounding is the correct one.  One per group.
 __device__ __forceinline__ float recip_f16_value(float sigma) {
-  const double s = (double)sigma;
-  double r = __builtin_amdgcn_rcp(s);
-  r = __builtin_fma(r, __builtin_fma(-s, r, 1.0), r);
-  return (float)r;
+  const float r0 = __builtin_amdgcn_rcpf(sigma);
+  const float e = __builtin_fmaf(-sigma, r0, 1.0f);
+  return __builtin_fmaf(r0, e, r0);
 }
 
 // Codes of one vector: int4 -> D/8 dwords, int8 -> D/4 dwords.

@@ -448,6 +448,41 @@ def test_fp32_reciprocal_of_every_fp16_is_correctly_rounded():
         assert e != abs(Fraction(u_) - exact) and e != abs(Fraction(d_) - exact)   # never a tie
 
 
+def test_fp32_newton_reciprocal_of_every_fp16_is_correctly_rounded():
+    """The kernels' reciprocal of an fp16 scale (quant.h recip_f16_value):
+    r0 within a few ulps of 1/sigma (the hardware estimate), e = fl(1 -
+    sigma r0) by one FMA, r = fl(r0 + r0 e) by another.  In exact rational
+    arithmetic, for every positive finite fp16 sigma and every r0 up to two
+    fp32 ulps off the correctly rounded reciprocal: e is exact, and r is the
+    correctly rounded fp32 reciprocal."""
+    from fractions import Fraction
+
+    def rn32(q):
+        # round a positive rational to the nearest fp32 (ties to even)
+        f = np.float32(float(q))   # float() rounds once to fp64: adjust to exact nearest below
+        cands = [np.nextafter(f, np.float32(0)), f, np.nextafter(f, np.float32(np.inf))]
+        best = min(cands, key=lambda c: (abs(Fraction(float(c)) - q),
+                                         int(np.array(c, np.float32).view(np.uint32)) & 1))
+        return best
+
+    sig = np.arange(1, 0x7c00, dtype=np.uint16).view(np.float16).astype(np.float64)
+    for s_ in sig.tolist():
+        S_ = Fraction(s_)
+        r = np.float32(1.0 / s_)
+        want = Fraction(float(r))
+        offs = [r]
+        for _ in range(2):
+            offs = [np.nextafter(offs[0], np.float32(0))] + offs + [np.nextafter(offs[-1], np.float32(np.inf))]
+        for r0 in offs:
+            R0 = Fraction(float(r0))
+            e_exact = 1 - S_ * R0
+            e = rn32(abs(e_exact)) if e_exact != 0 else np.float32(0)
+            e = Fraction(float(e)) * (1 if e_exact >= 0 else -1)
+            assert e == e_exact                     # the FMA's 1 - sigma r0 is exact
+            got = rn32(R0 + R0 * e)
+            assert Fraction(float(got)) == want, (s_, float(r0))
+
+
 # --------------------------------------------------------------------------
 # The growing cache: appending places per-vector results, nothing else.
 # --------------------------------------------------------------------------
