@@ -3,7 +3,8 @@
 // Free", Metodologia 1, and d = 3 * 2^k takes a radix-3 step, xform.h).
 //
 // One 64-token tile of one (tensor, head) per block (one wave), one vector
-// per lane as in kernels.h.  The fp16 rows (2D bytes, D/8 16-byte chunks;
+// per lane as in kernels.h, blocks ordered so that each XCD takes a
+// contiguous range of tiles (lane_item).  The fp16 rows (2D bytes, D/8 16-byte chunks;
 // 192 bytes at d = 96) pass through LDS so that global memory sees whole
 // rows: quantize fetches its tile by LDS-DMA, dequantize writes its output
 // tile from LDS.  Chunk c of row v sits at chunk position c ^ ((v >> 2) & 3)
@@ -63,6 +64,25 @@ __device__ __forceinline__ void load_row_bytes(const uint8_t* src, uint32_t (&v)
 // Chunk position of chunk c of tile row v (and back: the same XOR).
 __device__ __forceinline__ int lane_swz(int v) { return (v >> 2) & 3; }
 
+#ifndef SRFTQ_LANE_XCD
+#define SRFTQ_LANE_XCD 1
+#endif
+
+// Work item of this block out of n when neighbouring items should share an
+// XCD: the chip deals consecutive blocks to its 8 XCDs in turn, so block i
+// takes item (i mod 8) ceil(n / 8) + i / 8 and each XCD (its own L2) gets a
+// contiguous range.  Tiles of neighbouring heads then meet in one L2: at
+// d = 96 their 192-byte fp16 rows share 128-byte cache lines.  -1: none.
+// Launched on lane_grid(n) blocks.
+__device__ __forceinline__ int lane_item(int n) {
+  int i = (int)blockIdx.x;
+  if constexpr (SRFTQ_LANE_XCD) i = (i & 7) * ((n + 7) >> 3) + (i >> 3);
+  return i < n ? i : -1;
+}
+inline unsigned lane_grid(int n) { return SRFTQ_LANE_XCD ? (unsigned)(8 * ((n + 7) / 8)) : (unsigned)n; }
+
+// Quantize: one tile per block.  The tile's fp16 rows arrive by LDS-DMA;
+// every lane then stores its own code and scale row.
 template <int D, int G, int BITS, int ROT, int VAR, bool LAM>
 __global__ __launch_bounds__(64) void quantize_lane_kernel(const uint16_t* __restrict__ x,
                                                            const int8_t* __restrict__ signs,
@@ -75,7 +95,8 @@ __global__ __launch_bounds__(64) void quantize_lane_kernel(const uint16_t* __res
   static_assert(CH % 4 == 0, "chunk swizzle stays inside the row");
   __shared__ __attribute__((aligned(16))) uint8_t xt[64 * 2 * D];
   const int lane = threadIdx.x;
-  const int tile = blockIdx.x;
+  const int tile = lane_item(a.n_tiles);
+  if (tile < 0) return;
   const int k = tile / a.BH, bh = tile - k * a.BH;
   const int64_t t0 = (int64_t)k * 64;
   const int nv = a.T - t0 < 64 ? (int)(a.T - t0) : 64;
@@ -114,51 +135,19 @@ __global__ __launch_bounds__(64) void quantize_lane_kernel(const uint16_t* __res
   uint32_t codes[CodeWords<D, BITS>::kWords];
   uint32_t scales[ScaleWords<D, G>::kWords];
   quantize_tail<D, G, BITS, ROT, VAR, LAM>(y, LAM ? lambda + (int64_t)bh * D : nullptr, codes, scales);
-  // The tile's code and scale rows through LDS (the x tile is no longer
-  // read: every lane has its row), then out as two contiguous runs: cache
-  // row r0 + v for tile row v, r0 = t0 or the tensor's append position + t0;
-  // rows past T, and rows outside [0, pitch), are not written.
-  static_assert(CB % 16 == 0, "code rows are whole 16-byte chunks");
-  constexpr int SE = SB % 16 == 0 ? 16 : SB % 4 == 0 ? 4 : 2;   // scale store granule
-  uint8_t* oc = xt;
-  uint8_t* osc = xt + 64 * CB;
-  lds_poison<64 * 2 * D>(xt, lane);   // (debug builds; after the row reads, in LDS order)
-  static_for<CB / 16>([&](auto cc) {
-    constexpr int c = decltype(cc)::value;
-    *(uint4*)(oc + lane * CB + 16 * c) = make_uint4(codes[4 * c], codes[4 * c + 1], codes[4 * c + 2], codes[4 * c + 3]);
-  });
-  if constexpr (SB % 4 == 0) {
-    static_for<SB / 4>([&](auto ii) { *(uint32_t*)(osc + lane * SB + 4 * decltype(ii)::value) = scales[decltype(ii)::value]; });
-  } else {
-    static_for<SB / 2>([&](auto ii) {
-      constexpr int i = decltype(ii)::value;
-      *(uint16_t*)(osc + lane * SB + 2 * i) = (uint16_t)(scales[i / 2] >> (16 * (i % 2)));
-    });
+  // cache row r0 + lane for tile row lane, r0 = t0 or the tensor's append
+  // position + t0; rows past T, and rows outside [0, pitch), are not written
+  int64_t r0 = t0;
+  bool ok = lane < nv;
+  if (a.pos) {
+    r0 += a.pos[bh / a.H];
+    ok = ok && r0 + lane >= 0 && r0 + lane < a.pitch;
   }
-  wait_lgkm0();
-  wave_fence();
-  const int64_t r0 = t0 + (a.pos ? (int64_t)a.pos[bh / a.H] : 0);
-  uint8_t* cbase = codes_out + cache_row(a, bh, 0) * CB;
-  uint8_t* sbase = (uint8_t*)scales_out + cache_row(a, bh, 0) * SB;
-  auto row_ok = [&](int v) { return v < nv && r0 + v >= 0 && r0 + v < a.pitch; };
-  static_for<(64 * CB / 16 + 63) / 64>([&](auto ii) {
-    constexpr int i = decltype(ii)::value;
-    const int q = 64 * i + lane;   // 16-byte chunk of the tile's code rows
-    const int v = q * 16 / CB;
-    if (q < 64 * CB / 16 && row_ok(v))
-      *(uint4*)(cbase + (r0 + v) * CB + (q * 16 - v * CB)) = *(const uint4*)(oc + 16 * q);
-  });
-  static_for<(64 * SB / SE + 63) / 64>([&](auto ii) {
-    constexpr int i = decltype(ii)::value;
-    const int e = 64 * i + lane;   // granule of the tile's scale rows
-    const int v = e * SE / SB;
-    if (e < 64 * SB / SE && row_ok(v)) {
-      uint8_t* dst = sbase + (r0 + v) * SB + (e * SE - v * SB);
-      if constexpr (SE == 16) *(uint4*)dst = *(const uint4*)(osc + SE * e);
-      else if constexpr (SE == 4) *(uint32_t*)dst = *(const uint32_t*)(osc + SE * e);
-      else *(uint16_t*)dst = *(const uint16_t*)(osc + SE * e);
-    }
-  });
+  if (ok) {
+    const int64_t row = cache_row(a, bh, r0) + lane;
+    store_row_bytes<CB>(codes_out + row * CB, codes);
+    store_row_bytes<SB>((uint8_t*)scales_out + row * SB, scales);
+  }
 }
 
 // Quantize a few tokens per tensor (decode steps: T = 1 .. 8), one vector per
@@ -215,7 +204,8 @@ __global__ __launch_bounds__(64) void dequantize_lane_kernel(const uint8_t* __re
   __shared__ float lt[LAM ? D : 1];
   __shared__ __attribute__((aligned(16))) uint8_t xo[64 * 2 * D];
   const int lane = threadIdx.x;
-  const int tile = blockIdx.x;
+  const int tile = lane_item(a.n_tiles);
+  if (tile < 0) return;
   const int k = tile / a.BH, bh = tile - k * a.BH;
   if constexpr (LAM) {
     // e_j / lambda_j of the head (e_j the inverse transform's input scale)
