@@ -117,6 +117,27 @@ __device__ __forceinline__ uint32_t nib_f16x2(uint32_t z) {
   return ((z ^ 0x00080008u) & 0x000F000Fu) | 0x64006400u;
 }
 
+// v (own) and v of lane l ^ 16 / l ^ 32, as the two halves of a
+// v_permlane16_swap / v_permlane32_swap of (v, v): each lane keeps its own
+// value in one result and receives its partner's in the other, so one VALU
+// exchange (no LDS round trip) serves a butterfly reduction over 16 / 32.
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(as_u32(v), as_u32(v), false, false);
+  return __builtin_fmaxf(as_f32(r[0]), as_f32(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(as_u32(v), as_u32(v), false, false);
+  return __builtin_fmaxf(as_f32(r[0]), as_f32(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(as_u32(v), as_u32(v), false, false);
+  return as_f32(r[0]) + as_f32(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(as_u32(v), as_u32(v), false, false);
+  return as_f32(r[0]) + as_f32(r[1]);
+}
+
 // Wait until at most k * N vector-memory operations are in flight, k < NS.
 template <int N, int NS>
 __device__ __forceinline__ void wait_blocks(int k) {
@@ -669,8 +690,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const uint8_t* __rest
       S[e] = 4 * q + e < nv ? S[e] * uscale : -__builtin_inff();
     });
     float mx = __builtin_fmaxf(__builtin_fmaxf(S[0], S[1]), __builtin_fmaxf(S[2], S[3]));
-    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16));
-    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_xor32(max_xor16(mx));   // over the block's 16 tokens (lanes 16 apart)
     if (__builtin_amdgcn_ballot_w64(mx > m_run)) {
       const float m_new = __builtin_fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -718,8 +738,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const uint8_t* __rest
   }
 
   // softmax sum of head jl over the wave's tokens
-  float l_w = l_part + __shfl_xor(l_part, 16);
-  l_w += __shfl_xor(l_w, 32);
+  const float l_w = sum_xor32(sum_xor16(l_part));
 
   // ---- merge the 4 waves through LDS (the staging area is reused) ----
   __syncthreads();
