@@ -484,7 +484,9 @@ def wide_timing(launches: int) -> dict:
 
 def tiny_timing(launches: int) -> dict:
     """The tiny workload, fp16 [T=1024, H=8, d=128] (8,192 vectors, 2 MiB):
-    launch-bound, so microseconds per launch (HIP events), no roofline."""
+    launch-bound, so microseconds per launch (HIP events), no roofline: the
+    plain calls, the prepared ones (Quantizer / Dequantizer) and HIP-graph
+    replays."""
     import torch
 
     from kv_cache_quantization_srft_amd import srftq as S
@@ -509,10 +511,68 @@ def tiny_timing(launches: int) -> dict:
         ev[i][2].record()
     torch.cuda.synchronize()
     us = lambda a: {k.replace("_ms", "_us"): (v * 1e3 if k.endswith("_ms") else v) for k, v in _dist(a).items()}
+
+    # The prepared calls (arguments checked once, one library call per launch)
+    qz = S.Quantizer(xd.shape, codes, scales, sd, None, w.group, w.bits)
+    dqz = S.Dequantizer(xhat, sd, None, w.group, w.bits)
+    for _ in range(20):
+        qz(xd)
+        dqz(codes, scales)
+    torch.cuda.synchronize()
+    evp = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(launches)]
+    for i in range(launches):
+        evp[i][0].record()
+        qz(xd)
+        evp[i][1].record()
+        dqz(codes, scales)
+        evp[i][2].record()
+    torch.cuda.synchronize()
+
+    # The same launches captured in HIP graphs (50 of one direction each) and
+    # replayed: the device time per launch without the host's per-call work
+    # (argument checks, ctypes), which the events above include.
+    n_g, reps = 50, max(1, launches // 50)
+    codes_g, scales_g, xhat_g = torch.zeros_like(codes), torch.zeros_like(scales), torch.zeros_like(xhat)
+    q = lambda: S.quantize(xd, sd, None, w.group, w.bits, codes=codes_g, scales=scales_g)
+    dq = lambda: S.dequantize(codes_g, scales_g, sd, None, w.group, w.bits, out=xhat_g)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        q()
+        dq()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = {}
+    for name, f in (("quantize", q), ("dequantize", dq)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(n_g):
+                f()
+        graphs[name] = g
+    codes_g.zero_()
+    scales_g.zero_()
+    xhat_g.zero_()
+    torch.cuda.synchronize()
+    graph_us = {}
+    for name in ("quantize", "dequantize"):
+        graphs[name].replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            graphs[name].replay()
+        e1.record()
+        torch.cuda.synchronize()
+        graph_us[name] = e0.elapsed_time(e1) * 1e3 / (reps * n_g)
+    same = bool(torch.equal(codes_g, codes) and torch.equal(scales_g, scales) and torch.equal(xhat_g, xhat))
     return {"workload": f"tiny: fp16 [T={w.T}, H={w.H}, d={w.d}], SRFT, lambda 1, group {w.group}, int{w.bits}",
             "vectors": w.nvec,
             "quantize": us([e[0].elapsed_time(e[1]) for e in ev]),
-            "dequantize": us([e[1].elapsed_time(e[2]) for e in ev])}
+            "dequantize": us([e[1].elapsed_time(e[2]) for e in ev]),
+            "prepared_quantize": us([e[0].elapsed_time(e[1]) for e in evp]),
+            "prepared_dequantize": us([e[1].elapsed_time(e[2]) for e in evp]),
+            "graph_us_per_launch": graph_us, "graph_launches": reps * n_g,
+            "graph_outputs_match_eager": same}
 
 
 MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix-core peak

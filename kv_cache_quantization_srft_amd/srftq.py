@@ -443,6 +443,109 @@ class CacheAppender:
             _check(st, "srftq_cache_append")
 
 
+def _x_dims(x_shape):
+    """(B, T, H, d, flat) of an fp16 x shape [B,T,H,d] or [T,H,d]."""
+    x_shape = tuple(int(v) for v in x_shape)
+    if len(x_shape) == 4:
+        return x_shape + (False,)
+    if len(x_shape) == 3:
+        return (1,) + x_shape + (True,)
+    raise ValueError("x must be [B,T,H,d] or [T,H,d]")
+
+
+class Quantizer:
+    """srftq_quantize with everything but x checked once.
+
+    For small launches in a loop (decode steps), where quantize()'s per-call
+    checks cost more host time than the kernel: the output codes and scales,
+    signs, lambda, sizes and stream are fixed at construction (stream None:
+    the current stream at that moment); each call passes x fp16 of shape
+    x_shape ([B,T,H,d] or [T,H,d]) and overwrites codes and scales.  Not for
+    use inside a graph capture on another stream."""
+
+    def __init__(self, x_shape, codes, scales, signs=None, lam=None, group=16, bits=4, rot="srft",
+                 variant="default", stream=None):
+        import torch
+        B, T, H, d, flat = _x_dims(x_shape)
+        for t, dt, n in ((codes, torch.uint8, "codes"), (scales, torch.float16, "scales"),
+                         (signs, torch.int8, "signs"), (lam, torch.float32, "lambda")):
+            _req(t, dt, n)
+        if codes is None or scales is None:
+            raise ValueError("codes and scales are required")
+        lead = (H, T) if flat else (B, H, T)
+        if tuple(codes.shape) != lead + (d * bits // 8,):
+            raise ValueError(f"codes must have shape {lead + (d * bits // 8,)}")
+        _check_scales(scales, lead, d, group)
+        _head_rows(signs, B, H, d, "signs", flat, codes.device)
+        _head_rows(lam, B, H, d, "lambda", flat, codes.device)
+        _same_device(codes.device, scales=scales)
+        self._shape = make_shape(B, T, H, d, group, bits, rot, variant)
+        st = srftq_validate(self._shape)
+        if st != SRFTQ_OK:
+            _check(st, "srftq_validate")
+        self.x_shape = (T, H, d) if flat else (B, T, H, d)
+        self._device = codes.device
+        self._keep = (codes, scales, signs, lam)        # the tensors outlive the quantizer's calls
+        self._fn = lib().srftq_quantize
+        self._sh = ctypes.byref(self._shape)
+        self._rest = (_dp(signs), _dp(lam), _dp(codes), _dp(scales), _stream(stream))
+        self._f16 = torch.float16
+
+    def __call__(self, x):
+        if (tuple(x.shape) != self.x_shape or x.dtype != self._f16 or not x.is_contiguous()
+                or x.device != self._device):
+            raise ValueError(f"x must be a contiguous fp16 tensor of shape {self.x_shape} on {self._device}")
+        st = self._fn(self._sh, x.data_ptr(), *self._rest)
+        if st != SRFTQ_OK:
+            _check(st, "srftq_quantize")
+
+
+class Dequantizer:
+    """srftq_dequantize with everything but the codes and scales checked once.
+
+    The counterpart of Quantizer: the output out fp16 ([B,T,H,d] or
+    [T,H,d]), signs, lambda, sizes and stream are fixed at construction; each
+    call passes codes and scales of the head-major shapes that quantize()
+    writes for out's shape, and overwrites out."""
+
+    def __init__(self, out, signs=None, lam=None, group=16, bits=4, rot="srft", variant="default",
+                 stream=None):
+        import torch
+        _req(out, torch.float16, "out")
+        _req(signs, torch.int8, "signs")
+        _req(lam, torch.float32, "lambda")
+        if out is None:
+            raise ValueError("out is required")
+        B, T, H, d, flat = _x_dims(out.shape)
+        _head_rows(signs, B, H, d, "signs", flat, out.device)
+        _head_rows(lam, B, H, d, "lambda", flat, out.device)
+        self._shape = make_shape(B, T, H, d, group, bits, rot, variant)
+        st = srftq_validate(self._shape)
+        if st != SRFTQ_OK:
+            _check(st, "srftq_validate")
+        lead = (H, T) if flat else (B, H, T)
+        self.codes_shape = lead + (d * bits // 8,)
+        self.scales_shape = lead + (max(d // max(group, 1), 1),)
+        self._device = out.device
+        self._keep = (out, signs, lam)
+        self._fn = lib().srftq_dequantize
+        self._sh = ctypes.byref(self._shape)
+        self._mid = (_dp(signs), _dp(lam), _dp(out), _stream(stream))
+        self._u8, self._f16 = torch.uint8, torch.float16
+
+    def __call__(self, codes, scales):
+        if (tuple(codes.shape) != self.codes_shape or codes.dtype != self._u8 or not codes.is_contiguous()
+                or codes.device != self._device):
+            raise ValueError(f"codes must be a contiguous uint8 tensor of shape {self.codes_shape} on {self._device}")
+        if (tuple(scales.shape) != self.scales_shape or scales.dtype != self._f16 or not scales.is_contiguous()
+                or scales.device != self._device):
+            raise ValueError(f"scales must be a contiguous fp16 tensor of shape {self.scales_shape} "
+                             f"on {self._device}")
+        st = self._fn(self._sh, codes.data_ptr(), scales.data_ptr(), *self._mid)
+        if st != SRFTQ_OK:
+            _check(st, "srftq_dequantize")
+
+
 def cache_read(codes, scales, T, signs=None, lam=None, group=16, bits=4, rot="srft", variant="default",
                d=None, out=None, stream=None):
     """Dequantize + unrotate rows [0, T) of every head of a cache

@@ -369,6 +369,36 @@ def test_cache_appender_rejects_cpu_tokens():
         app(torch.zeros((2, 2, 3, 64), dtype=torch.float16))
 
 
+def test_quantizer_and_dequantizer_reject_bad_inputs():
+    """Quantizer / Dequantizer check every call's inputs (shape, dtype,
+    contiguity, device) before a pointer reaches the library, and refuse CPU
+    outputs at construction."""
+    import torch
+    q = object.__new__(S.Quantizer)                 # the fields __call__ reads, no device needed
+    q.x_shape = (2, 64, 3, 128)
+    q._f16 = torch.float16
+    q._device = torch.device("cuda", 0)
+    q._fn = None                                    # never reached
+    with pytest.raises(ValueError, match="on cuda:0"):
+        q(torch.zeros(q.x_shape, dtype=torch.float16))
+    with pytest.raises(ValueError, match="shape"):
+        q(torch.zeros((2, 65, 3, 128), dtype=torch.float16))
+    dq = object.__new__(S.Dequantizer)
+    dq.codes_shape, dq.scales_shape = (2, 3, 64, 64), (2, 3, 64, 8)
+    dq._u8, dq._f16 = torch.uint8, torch.float16
+    dq._device = torch.device("cuda", 0)
+    dq._fn = None
+    with pytest.raises(ValueError, match="codes"):
+        dq(torch.zeros(dq.codes_shape, dtype=torch.uint8), torch.zeros(dq.scales_shape, dtype=torch.float16))
+    with pytest.raises(ValueError, match="codes"):
+        dq(torch.zeros((2, 3, 64, 32), dtype=torch.uint8), torch.zeros(dq.scales_shape, dtype=torch.float16))
+    with pytest.raises(ValueError, match="CUDA"):
+        S.Quantizer((2, 64, 3, 128), torch.zeros((2, 3, 64, 64), dtype=torch.uint8),
+                    torch.zeros((2, 3, 64, 8), dtype=torch.float16))
+    with pytest.raises(ValueError, match="CUDA"):
+        S.Dequantizer(torch.zeros((2, 64, 3, 128), dtype=torch.float16))
+
+
 def test_cache_save_load_roundtrip(tmp_path):
     """QuantizedKVCache.save / load on the host: the rows written so far, the
     positions, signs, lambda and parameters come back unchanged, into a

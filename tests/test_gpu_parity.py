@@ -416,3 +416,33 @@ def test_binding_rejects_misshaped_side_tensors():
     with pytest.raises(ValueError):
         app(torch.zeros((2, 1, 3, 128), dtype=torch.float16))     # CPU tokens
     torch.cuda.synchronize()
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("d,rot,three", [(128, "srft", False), (256, "srft", False), (96, "srft", True),
+                                         (64, "srht", False)])
+def test_prepared_calls_equal_plain_calls(d, rot, three):
+    """Quantizer / Dequantizer (checked once, one library call per step) write
+    bit for bit what quantize() / dequantize() write, over several calls with
+    changing inputs (a ragged tail tile, lambda on, 3-D x for d = 96)."""
+    x, s, l = rand_case(9500 + d, 2, 70, 3, d, scale=2.0, lam=True)
+    if three:
+        x, s, l = x[0], s[0], l[0]
+    print(f"[prepared d={d} {rot} x{tuple(x.shape)}]", flush=True)
+    sd, ld = dev(s), dev(l)
+    codes_p, scales_p = S.quantize(dev(x), sd, ld, 16, 4, rot)
+    out_p = torch.empty(x.shape, dtype=torch.float16, device="cuda:0")
+    qz = S.Quantizer(x.shape, codes_p, scales_p, sd, ld, 16, 4, rot)
+    dqz = S.Dequantizer(out_p, sd, ld, 16, 4, rot)
+    r = np.random.default_rng(9600 + d)
+    for step in range(3):
+        xs = dev((x.astype(np.float32) * r.uniform(0.5, 2.0)).astype(np.float16))
+        codes, scales = S.quantize(xs, sd, ld, 16, 4, rot)
+        out = S.dequantize(codes, scales, sd, ld, 16, 4, rot)
+        qz(xs)
+        dqz(codes_p, scales_p)
+        torch.cuda.synchronize()
+        assert torch.equal(codes_p, codes) and torch.equal(scales_p, scales), step
+        assert torch.equal(out_p.view(torch.int16), out.view(torch.int16)), step
+    with pytest.raises(ValueError):
+        qz(xs[..., :-1].contiguous() if not three else xs[:-1].contiguous())
