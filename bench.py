@@ -369,6 +369,77 @@ def non_pow2_timing(steps: int) -> dict:
             "vectors_per_s_step": n / ((q_ms + dq_ms) * 1e-3)}
 
 
+def memory_floor_timing(nvec: int, pairs: int, q_ms: float, dq_ms: float) -> dict | None:
+    """HBM floor of the headline's two traffic mixes, measured in the same
+    run: libsrftq_memfloor.so's kernels move exactly a quantize launch's
+    bytes (16 KiB read, 5 KiB written per 64-vector tile) and a dequantize
+    launch's (5 KiB read, 16 KiB written), with no arithmetic, alternating
+    as the benchmark step does (the second reads what the first wrote).
+    Each launch shape (one tile per block; persistent grids of 2048 and
+    4096 waves) and store policy is timed over `pairs` pairs; the fastest
+    median per mix is the floor."""
+    import ctypes
+
+    import torch
+
+    path = os.path.join(ROOT, "kv_cache_quantization_srft_amd", "libsrftq_memfloor.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.srftq_memfloor.restype = ctypes.c_int
+    lib.srftq_memfloor.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    assert nvec % 64 == 0
+    n_tiles = nvec // 64
+    big = torch.empty(n_tiles * 16384, dtype=torch.uint8, device="cuda")
+    small = torch.empty(n_tiles * 5120, dtype=torch.uint8, device="cuda")
+    big.fill_(1)
+    small.fill_(2)
+    stream = torch.cuda.current_stream()
+    sh = ctypes.c_void_p(stream.cuda_stream)
+
+    def launch(mix, nt, grid):
+        src, dst = (big, small) if mix == 0 else (small, big)
+        rc = lib.srftq_memfloor(mix, nt, src.data_ptr(), dst.data_ptr(), n_tiles, grid, sh)
+        if rc != 0:
+            raise RuntimeError(f"srftq_memfloor failed: {rc}")
+
+    configs = []
+    for grid in (n_tiles, 2048, 4096):
+        for nt in (1, 0):
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(pairs)]
+            for _ in range(5):
+                launch(0, nt, grid)
+                launch(1, nt, grid)
+            for e in ev:
+                e[0].record(stream)
+                launch(0, nt, grid)
+                e[1].record(stream)
+                launch(1, nt, grid)
+                e[2].record(stream)
+            torch.cuda.synchronize()
+            configs.append({"grid": "one tile per block" if grid == n_tiles else f"persistent {grid}",
+                            "nontemporal_stores": bool(nt),
+                            "quantize_mix": _dist([e[0].elapsed_time(e[1]) for e in ev]),
+                            "dequantize_mix": _dist([e[1].elapsed_time(e[2]) for e in ev])})
+    del big, small
+    bq = min(configs, key=lambda c: c["quantize_mix"]["p50_ms"])
+    bd = min(configs, key=lambda c: c["dequantize_mix"]["p50_ms"])
+    fq, fd = bq["quantize_mix"]["p50_ms"], bd["dequantize_mix"]["p50_ms"]
+    tile_bytes = 21504
+    return {
+        "what": "kernels that move a launch's bytes (contiguous 64-vector tiles, 16 KiB + 5 KiB) with no "
+                "arithmetic, alternating like the benchmark step; fastest launch shape and store policy",
+        "quantize_mix_ms": fq, "dequantize_mix_ms": fd,
+        "quantize_mix_hbm_frac": tile_bytes * n_tiles / (fq * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "dequantize_mix_hbm_frac": tile_bytes * n_tiles / (fd * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "quantize_frac_of_floor": fq / q_ms, "dequantize_frac_of_floor": fd / dq_ms,
+        "best_quantize_mix_shape": {"grid": bq["grid"], "nontemporal_stores": bq["nontemporal_stores"]},
+        "best_dequantize_mix_shape": {"grid": bd["grid"], "nontemporal_stores": bd["nontemporal_stores"]},
+        "configs": configs,
+    }
+
+
 def _dist(ms_list) -> dict:
     """Per-launch times (ms): mean, median and the 10th / 90th percentiles."""
     import numpy as np
@@ -814,6 +885,12 @@ def main():
         step(0)            # leave set 0 holding the SRFT codes (decode attention reads it)
         torch.cuda.synchronize()
 
+    # the floor kernels move 16 KiB + 5 KiB per 64-vector tile: d = 128, int4, group 16
+    mfloor = None
+    if not args.no_decode and bpv == 336 and w.d == 128:
+        mfloor = memory_floor_timing(nvec, max(50, args.steps // 4), per_kernel["quantize"]["p50_ms"],
+                                     per_kernel["dequantize"]["p50_ms"])
+
     # plain copy kernel of the quantize input's size (fp16 negate: reads and
     # writes 2*d bytes per vector): achievable-bandwidth reference, and the
     # known-size kernel the HBM byte counters are scaled against
@@ -880,6 +957,7 @@ def main():
                 "the set the previous step wrote (one launch each)",
         "reconstruction_rel_l2": rel,
         "rot_none_floor": floor,
+        "memory_floor": mfloor,
         "roundtrip_128k": c5,
         "wide_d256": c4,
         "tiny_launch": tiny,

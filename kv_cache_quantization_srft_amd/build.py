@@ -6,7 +6,9 @@ Each translation unit is compiled by hipcc in parallel, then linked into one
 shared library next to this file.  --poison builds the debug variant
 libsrftq_poison.so instead (SRFTQ_LDS_POISON=1: the single-wave streaming
 kernels fill their LDS buffers with 0xff bytes before each use), which the
-tests load through SRFTQ_LIBRARY.
+tests load through SRFTQ_LIBRARY.  build_memfloor() links
+libsrftq_memfloor.so, the benchmark's memory-floor kernels (no arithmetic of
+the method; bench.py alone loads it).
 """
 from __future__ import annotations
 
@@ -24,6 +26,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsrftq.so")
 BUILD_POISON = os.path.join(PKG, "_build_poison")
 LIB_POISON = os.path.join(PKG, "libsrftq_poison.so")
+MEMFLOOR_SRC = os.path.join(PKG, "memfloor", "memfloor.hip")
+LIB_MEMFLOOR = os.path.join(PKG, "libsrftq_memfloor.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -83,6 +87,20 @@ def _compile(src: str, incremental: bool = False, poison: bool = False) -> str:
     return obj
 
 
+def build_memfloor(verbose: bool = False) -> str:
+    """Link libsrftq_memfloor.so: the benchmark's memory-floor kernels, kept
+    out of libsrftq.so (they compute nothing of the method)."""
+    tmp = LIB_MEMFLOOR + ".tmp"
+    cmd = [HIPCC] + DEVICE_FLAGS + ["-shared", "-o", tmp, MEMFLOOR_SRC]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, LIB_MEMFLOOR)
+    if verbose:
+        print(f"built {LIB_MEMFLOOR}")
+    return LIB_MEMFLOOR
+
+
 def build(jobs: int | None = None, verbose: bool = False, incremental: bool = False, poison: bool = False) -> str:
     """Compile every unit (incremental: only those whose object is older
     than the source or a header it includes) and link libsrftq.so (poison:
@@ -113,4 +131,6 @@ if __name__ == "__main__":
     ap.add_argument("--poison", action="store_true", help="build the LDS-poison debug variant")
     a = ap.parse_args()
     build(a.jobs, verbose=True, incremental=a.incremental, poison=a.poison)
+    if not a.poison:
+        build_memfloor(verbose=True)
     sys.exit(0)

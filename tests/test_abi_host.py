@@ -435,3 +435,22 @@ def test_cache_save_load_roundtrip(tmp_path):
     save_file({"codes": torch.zeros(1, dtype=torch.uint8)}, str(g2), metadata={"format": "x"})
     with pytest.raises(ValueError):
         kvcache.QuantizedKVCache.load(g2, device="cpu")
+
+
+def test_memfloor_library_rejects_bad_arguments_before_launch():
+    """The benchmark's memory-floor library loads, exports its one call and
+    turns a bad mix, size, grid or pointer into hipErrorInvalidValue (1)
+    before any launch."""
+    path = os.path.join(ROOT, "kv_cache_quantization_srft_amd", "libsrftq_memfloor.so")
+    L = ctypes.CDLL(path)
+    f = L.srftq_memfloor
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                  ctypes.c_int, ctypes.c_void_p]
+    a, b = 0x10000, 0x20000
+    assert f(3, 1, a, b, 64, 64, None) == 1           # unknown mix
+    assert f(0, 1, a, b, 0, 1, None) == 1             # no tiles
+    assert f(0, 1, a, b, 64, 65, None) == 1           # grid beyond the tiles
+    assert f(0, 1, a, b, 64, 0, None) == 1            # empty grid
+    assert f(1, 0, None, b, 64, 64, None) == 1        # NULL input
+    assert f(1, 0, a + 8, b, 64, 64, None) == 1       # misaligned
