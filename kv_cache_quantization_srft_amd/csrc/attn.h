@@ -93,6 +93,7 @@ struct AttnTile {
   static constexpr int LDS_BYTES = 4 * WAVE_BYTES > MERGE_BYTES ? 4 * WAVE_BYTES : MERGE_BYTES;
   static_assert(G >= 16 && G % 16 == 0, "a group spans whole MFMA k-blocks");
   static_assert(CT % 256 == 0, "V codes move in 256-byte DMA instructions");
+  static_assert(BITS != 4 || NB % 2 == 0, "int4 V codes unpack in blocks of 32 coordinates");
   static_assert(NS >= 2 && (NS - 1) * NDMA <= 63, "the blocks in flight fit the vmcnt counter");
 };
 
@@ -115,6 +116,12 @@ __device__ __forceinline__ lds_u32x4p lds_ptr128(uint32_t byte_addr) { return (l
 // 1024 + n (one v_bitop3).
 __device__ __forceinline__ uint32_t nib_f16x2(uint32_t z) {
   return ((z ^ 0x00080008u) & 0x000F000Fu) | 0x64006400u;
+}
+// ((z ^ 0x00800080) & 0x00F000F0) | 0x54005400: the nibbles at bits 4-7 and
+// 20-23, offset by 8, as the fp16 pair 64 + n without a shift: they fill
+// mantissa bits 4-7, where one unit is worth 2^(6-10+4) = 1 (one v_bitop3).
+__device__ __forceinline__ uint32_t nib_hi_f16x2(uint32_t z) {
+  return ((z ^ 0x00800080u) & 0x00F000F0u) | 0x54005400u;
 }
 
 // v (own) and v of lane l ^ 16 / l ^ 32, as the two halves of a
@@ -192,6 +199,16 @@ __device__ __forceinline__ uint32_t scale_pair(uint32_t tile, int row, int g) {
     return lds_u16(tile + (uint32_t)(2 * row * SRB + 4 * g)) |
            (lds_u16(tile + (uint32_t)(2 * (row + 1) * SRB + 4 * g)) << 16);
   }
+}
+
+// The same for group 2j + h (groups of 16, scale rows a whole number of
+// dwords): half h of dword j of each row; h may differ between lanes.
+template <int SRB>
+__device__ __forceinline__ uint32_t scale_pair_g16(uint32_t tile, int row, int j, int h) {
+  static_assert(SRB % 4 == 0, "scale rows of whole dwords");
+  const uint32_t w0 = lds_u32(tile + (uint32_t)(row * SRB + 4 * j));
+  const uint32_t w1 = lds_u32(tile + (uint32_t)((row + 1) * SRB + 4 * j));
+  return __builtin_amdgcn_perm(w1, w0, h ? 0x07060302u : 0x05040100u);
 }
 
 // ----------------------------------------------------------------------------
@@ -625,16 +642,9 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const uint8_t* __rest
 
   // per-lane constant selectors
   const uint32_t ksel = (q & 1) ? 0x0C030C02u : 0x0C010C00u;            // K int4: half q&1 of the dword
-  uint32_t vsel, vsh;
-  if constexpr (BITS == 4) {
-    const uint32_t bsel = (uint32_t)((jl & 7) >> 1);
-    vsel = 0x0C000C00u | bsel | ((4u + bsel) << 16);
-    vsh = (uint32_t)(jl & 1) * 4u;
-  } else {
-    const uint32_t bsel = (uint32_t)(jl & 3);
-    vsel = 0x0C000C00u | bsel | ((4u + bsel) << 16);
-    vsh = 0;
-  }
+  // V: byte jl & 3 of a dword (int4: byte jl of a 32-coordinate block,
+  // both of its nibbles; int8: the coordinate's byte)
+  const uint32_t vsel = 0x0C000C00u | (uint32_t)(jl & 3) | ((4u + (uint32_t)(jl & 3)) << 16);
 
   constexpr int NS = Tl::NS;
   for (int i = 0; i < NS - 1 && i < nblk; ++i) issue(i, i);
@@ -662,7 +672,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const uint8_t* __rest
       if constexpr (BITS == 4) {
         const uint32_t z = __builtin_amdgcn_perm(0u, krow[2 * kb], ksel);
         const uint32_t a0 = f16x2_minus(nib_f16x2(z), kBias);
-        const uint32_t a1 = f16x2_minus(nib_f16x2(z >> 4), kBias);
+        const uint32_t a1 = f16x2_minus(nib_hi_f16x2(z), 72.0f);   // 64 + offset of the code
         A = half4_of(a0, a1);
       } else {
         const uint32_t x = krow[4 * kb];
@@ -710,31 +720,55 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const uint8_t* __rest
 
     // ---- P.V: acc[coord][head] += sum_t fp16(c_v(t, coord) sigma_v(t, G)) fp16(2^14 p_t) ----
     const half4_t Bv = half4_of(pack_f16x2(p[0], p[1]), pack_f16x2(p[2], p[3]));
-    // transposed V tile: dword w of tokens 4q..4q+3 at 16-byte index 4w + q;
-    // this lane's coordinate sits in dword 2kb + jl/8 (int4) or 4kb + jl/4 (int8)
-    const lds_u32x4p vcol = lds_ptr128(base + Tl::OFF_VC) + (uint32_t)(4 * (BITS == 4 ? (jl >> 3) : (jl >> 2)) + q);
-    uint32_t sv01 = 0, sv23 = 0;   // sigma_v of the lane's tokens (4q, 4q+1), (4q+2, 4q+3), group of kb
-    static_for<NB>([&](auto kk) {
-      constexpr int kb = decltype(kk)::value;
-      if constexpr (kb % KB_PER_G == 0) {
-        constexpr int g = kb / KB_PER_G;
-        sv01 = scale_pair<SRB>(base + Tl::OFF_VS, 4 * q, g);
-        sv23 = scale_pair<SRB>(base + Tl::OFF_VS, 4 * q + 2, g);
-      }
-      // the four tokens 4q..4q+3 of one dword of the transposed V tile
-      const u32x4_t x = vcol[(BITS == 4 ? 2 : 4) * kb * 4];
-      uint32_t a0, a1;
-      if constexpr (BITS == 4) {
-        a0 = f16x2_minus(nib_f16x2(__builtin_amdgcn_perm(x.y, x.x, vsel) >> vsh), kBias);
-        a1 = f16x2_minus(nib_f16x2(__builtin_amdgcn_perm(x.w, x.z, vsel) >> vsh), kBias);
-      } else {
-        a0 = f16x2_minus(__builtin_amdgcn_perm(x.y, x.x, vsel) ^ 0x64806480u, kBias);
-        a1 = f16x2_minus(__builtin_amdgcn_perm(x.w, x.z, vsel) ^ 0x64806480u, kBias);
-      }
-      a0 = f16x2_mul(a0, sv01);
-      a1 = f16x2_mul(a1, sv23);
-      acc[kb] = __builtin_amdgcn_mfma_f32_16x16x16f16(half4_of(a0, a1), Bv, acc[kb], 0, 0, 0);
-    });
+    if constexpr (BITS == 4) {
+      // Block j of 32 coordinates: lane jl takes byte jl of each token's 16
+      // code bytes, i.e. coordinates 32j + 2jl (low nibble, into acc[2j]) and
+      // 32j + 2jl + 1 (high nibble, into acc[2j + 1]), so both nibbles unpack
+      // without a shift.  Transposed V tile: dword w of tokens 4q..4q+3 at
+      // 16-byte index 4w + q; the lane's byte sits in dword 4j + jl/4.
+      const lds_u32x4p vcol = lds_ptr128(base + Tl::OFF_VC) + (uint32_t)(4 * (jl >> 2) + q);
+      uint32_t sv01 = 0, sv23 = 0;   // sigma_v of the lane's tokens (4q, 4q+1), (4q+2, 4q+3)
+      static_for<NB / 2>([&](auto jj) {
+        constexpr int j = decltype(jj)::value;
+        if constexpr (G == 16) {
+          // the lane's group 2j + jl/8: its pair of scales is dword j of the
+          // row, half jl/8
+          sv01 = scale_pair_g16<SRB>(base + Tl::OFF_VS, 4 * q, j, jl >> 3);
+          sv23 = scale_pair_g16<SRB>(base + Tl::OFF_VS, 4 * q + 2, j, jl >> 3);
+        } else if constexpr ((32 * j) % G == 0) {
+          constexpr int g = 32 * j / G;
+          sv01 = scale_pair<SRB>(base + Tl::OFF_VS, 4 * q, g);
+          sv23 = scale_pair<SRB>(base + Tl::OFF_VS, 4 * q + 2, g);
+        }
+        const u32x4_t x = vcol[16 * j];
+        const uint32_t z01 = __builtin_amdgcn_perm(x.y, x.x, vsel);
+        const uint32_t z23 = __builtin_amdgcn_perm(x.w, x.z, vsel);
+        const uint32_t e0 = f16x2_mul(f16x2_minus(nib_f16x2(z01), kBias), sv01);
+        const uint32_t e1 = f16x2_mul(f16x2_minus(nib_f16x2(z23), kBias), sv23);
+        const uint32_t o0 = f16x2_mul(f16x2_minus(nib_hi_f16x2(z01), 72.0f), sv01);
+        const uint32_t o1 = f16x2_mul(f16x2_minus(nib_hi_f16x2(z23), 72.0f), sv23);
+        acc[2 * j] = __builtin_amdgcn_mfma_f32_16x16x16f16(half4_of(e0, e1), Bv, acc[2 * j], 0, 0, 0);
+        acc[2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(half4_of(o0, o1), Bv, acc[2 * j + 1], 0, 0, 0);
+      });
+    } else {
+      // lane jl takes coordinate 16kb + jl, the byte jl & 3 of dword 4kb + jl/4
+      const lds_u32x4p vcol = lds_ptr128(base + Tl::OFF_VC) + (uint32_t)(4 * (jl >> 2) + q);
+      uint32_t sv01 = 0, sv23 = 0;
+      static_for<NB>([&](auto kk) {
+        constexpr int kb = decltype(kk)::value;
+        if constexpr (kb % KB_PER_G == 0) {
+          constexpr int g = kb / KB_PER_G;
+          sv01 = scale_pair<SRB>(base + Tl::OFF_VS, 4 * q, g);
+          sv23 = scale_pair<SRB>(base + Tl::OFF_VS, 4 * q + 2, g);
+        }
+        const u32x4_t x = vcol[16 * kb];
+        uint32_t a0 = f16x2_minus(__builtin_amdgcn_perm(x.y, x.x, vsel) ^ 0x64806480u, kBias);
+        uint32_t a1 = f16x2_minus(__builtin_amdgcn_perm(x.w, x.z, vsel) ^ 0x64806480u, kBias);
+        a0 = f16x2_mul(a0, sv01);
+        a1 = f16x2_mul(a1, sv23);
+        acc[kb] = __builtin_amdgcn_mfma_f32_16x16x16f16(half4_of(a0, a1), Bv, acc[kb], 0, 0, 0);
+      });
+    }
   }
 
   // softmax sum of head jl over the wave's tokens
@@ -765,18 +799,37 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const uint8_t* __rest
     fw[w] = mw[w] == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(mw[w] - m);
   });
   const int64_t slot = ((int64_t)bh * a.n_chunks + c) * a.R + jl;   // valid for jl < R
-  static_for<NB>([&](auto kk) {
-    constexpr int kb = decltype(kk)::value;
-    if (kb % 4 == wave) {
-      float4_t s = (float4_t){0.f, 0.f, 0.f, 0.f};
-      static_for<4>([&](auto ww) {
-        constexpr int w = decltype(ww)::value;
-        const float4_t v = *(const __attribute__((address_space(3))) float4_t*)(uintptr_t)(macc + 16u * ((uint32_t)(w * NB + kb) * 64u + lane));
-        s += fw[w] * v;
-      });
-      if (jl < a.R) *(float4_t*)(ws_acc + slot * D + 16 * kb + 4 * q) = s;
-    }
-  });
+  auto merged = [&](int kb) {   // acc[kb] of this lane summed over the 4 waves
+    float4_t s = (float4_t){0.f, 0.f, 0.f, 0.f};
+    static_for<4>([&](auto ww) {
+      constexpr int w = decltype(ww)::value;
+      const float4_t v = *(const __attribute__((address_space(3))) float4_t*)(uintptr_t)(macc + 16u * ((uint32_t)(w * NB + kb) * 64u + lane));
+      s += fw[w] * v;
+    });
+    return s;
+  };
+  if constexpr (BITS == 4) {
+    // acc[2j] element e holds coordinate 32j + 8q + 2e, acc[2j + 1] the next
+    static_for<NB / 2>([&](auto jj) {
+      constexpr int j = decltype(jj)::value;
+      if (j % 4 == wave) {
+        const float4_t se = merged(2 * j), so = merged(2 * j + 1);
+        if (jl < a.R) {
+          float* dst = ws_acc + slot * D + 32 * j + 8 * q;
+          *(float4_t*)dst = (float4_t){se[0], so[0], se[1], so[1]};
+          *(float4_t*)(dst + 4) = (float4_t){se[2], so[2], se[3], so[3]};
+        }
+      }
+    });
+  } else {
+    static_for<NB>([&](auto kk) {
+      constexpr int kb = decltype(kk)::value;
+      if (kb % 4 == wave) {
+        const float4_t s = merged(kb);
+        if (jl < a.R) *(float4_t*)(ws_acc + slot * D + 16 * kb + 4 * q) = s;
+      }
+    });
+  }
   if (wave == 0 && q == 0 && jl < a.R) {
     float l = 0.0f;
     static_for<4>([&](auto ww) {
