@@ -163,6 +163,28 @@ def cpu_baseline(w, x, s, lam, target_s: float = 12.0):
             "one_core": {"value": v1, "unit": "KV vectors/s", "cores": 1, "sample": sample1}}
 
 
+SECTION_SETTLE_S = 0.3
+
+
+def _settle(fn, seconds: float = SECTION_SETTLE_S) -> int:
+    """Untimed calls of fn for `seconds` of sustained load before a section's
+    timed launches: after a light phase (single-token appends, host work)
+    the GPU's clocks need a sustained load to return to their working level,
+    and a section timed straight away can run several times slower for its
+    first tens of milliseconds.  Returns the number of calls."""
+    import torch
+
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        for _ in range(10):
+            fn()
+        n += 10
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return n
+
+
 def decode_append_latency(steps: int = 1000, graph_steps: int = 100) -> dict:
     """The decode-append shape: 256 sequences each append one token per step
     ([256, 1, H=8, d=64], int8, group 32) into a per-head cache of
@@ -303,9 +325,7 @@ def decode_attention_timing(w, codes, scales, sd, lam, steps: int, R: int = 6) -
         S.decode_attention(q, kc, ks, vc, vs, sk, lk, sv, lv, group=w.group, bits=w.bits,
                            workspace=ws, out=out)
 
-    for _ in range(20):
-        call()
-    torch.cuda.synchronize()
+    _settle(call)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for e0, e1 in evs:
         e0.record()
@@ -344,10 +364,10 @@ def non_pow2_timing(steps: int) -> dict:
     codes = torch.empty((B, H, T, d * bits // 8), dtype=torch.uint8, device=dev)
     scales = torch.empty((B, H, T, d // g), dtype=torch.float16, device=dev)
     xhat = torch.empty_like(x)
-    for _ in range(10):
+    def pair():
         S.quantize(x, s, None, g, bits, codes=codes, scales=scales)
         S.dequantize(codes, scales, s, None, g, bits, out=xhat)
-    torch.cuda.synchronize()
+    _settle(pair)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     tq = tdq = 0.0
     for _ in range(steps):
@@ -679,10 +699,10 @@ def householder_timing(steps: int) -> dict:
     build_ms = e0.elapsed_time(e1)
     codes, scales = S.quantize_dense(xd, Q, sd, None, w.group, w.bits)
     xhat = S.dequantize_dense(codes, scales, Q, sd, None, w.group, w.bits)
-    for _ in range(5):
+    def pair():
         S.quantize_dense(xd, Q, sd, None, w.group, w.bits, codes=codes, scales=scales)
         S.dequantize_dense(codes, scales, Q, sd, None, w.group, w.bits, out=xhat)
-    torch.cuda.synchronize()
+    _settle(pair)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     tq = tdq = 0.0
     for _ in range(steps):
@@ -710,9 +730,7 @@ def householder_timing(steps: int) -> dict:
     out = torch.empty((L, w.H * R, w.d), dtype=torch.float32, device=dev)
     attend = lambda: S.decode_attention_dense(qa, kc, ks, vc, vs, Qk, Qv, sk, None, sv, None, group=w.group,
                                               bits=w.bits, workspace=ws, out=out)
-    for _ in range(10):
-        attend()
-    torch.cuda.synchronize()
+    _settle(attend)
     ta = 0.0
     for _ in range(steps):
         ev[0].record()
