@@ -147,6 +147,19 @@ def test_attention_matrix(d, g, bits, rot):
     print(check(c, run_gpu(c, lengths), lengths))
 
 
+@pytest.mark.parametrize("d,g", [(64, 32), (64, 64), (128, 32), (128, 128), (256, 32), (256, 128), (256, 256)])
+def test_attention_int4_group_sizes(d, g):
+    """int4 V codes unpack in blocks of 32 coordinates, each lane taking both
+    nibbles of one byte, with the lane's group scale chosen per lane at
+    group 16 and per block otherwise: groups of 32 (one per block), 64 and
+    more (one per several blocks), up to the whole vector."""
+    R = {64: 2, 128: 6, 256: 8}[d]
+    c = make_case(7080 + d + g, 2, 1100, 2, R, d, g, 4, "srft", lam=True)
+    lengths = np.array([1100, 681], dtype=np.int32)
+    print(f"[attention int4 d={d} g={g}]", flush=True)
+    print(check(c, run_gpu(c, lengths), lengths))
+
+
 @pytest.mark.parametrize("g,bits", [(16, 4), (32, 4), (16, 8), (32, 8)])
 @pytest.mark.parametrize("rot", ["srft", "none"])
 def test_attention_d96(g, bits, rot):
