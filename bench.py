@@ -326,20 +326,37 @@ def decode_attention_timing(w, codes, scales, sd, lam, steps: int, R: int = 6) -
                            workspace=ws, out=out)
 
     _settle(call)
+    # calls back to back (a decode loop's pattern), one event pair around
+    # them, and the host's enqueue time of the same calls: the GPU time per
+    # call is the kernels' own only while the host enqueues faster
+    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    b0.record()
+    for _ in range(steps):
+        call()
+    b1.record()
+    host_us = (time.perf_counter() - h0) / steps * 1e6
+    torch.cuda.synchronize()
+    ms = b0.elapsed_time(b1) / steps
+    # and with an event pair around each call (which also drains the queue
+    # between calls)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for e0, e1 in evs:
         e0.record()
         call()
         e1.record()
     torch.cuda.synchronize()
-    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    per_call = _dist([e0.elapsed_time(e1) for e0, e1 in evs])
     bpv = w.d * w.bits // 8 + 2 * (w.d // w.group)
     nbytes = 2 * L * w.H * w.T * bpv
     fp16_bytes = 2 * L * w.H * w.T * 2 * w.d
     gbps = nbytes / (ms * 1e-3) / 1e9
     return {"workload": f"decode attention: {L} layers x K+V caches [T={w.T}, H={w.H}, d={w.d}], "
                         f"group {w.group}, int{w.bits}, {R} query heads per KV head, one query token",
-            "ms": ms, "algorithmic_bytes": nbytes, "GBps": gbps, "hbm_frac": gbps / HBM_PEAK_GBPS,
+            "ms": ms, "calls_back_to_back": steps, "host_enqueue_us_per_call": host_us,
+            "per_call_events": per_call,
+            "algorithmic_bytes": nbytes, "GBps": gbps, "hbm_frac": gbps / HBM_PEAK_GBPS,
             "cached_tokens_per_s": L * w.H * w.T / (ms * 1e-3),
             "fp16_cache_bytes": fp16_bytes,
             "fp16_cache_read_ms_at_same_GBps": fp16_bytes / (gbps * 1e9) * 1e3,
