@@ -339,6 +339,18 @@ def decode_attention_timing(w, codes, scales, sd, lam, steps: int, R: int = 6) -
     host_us = (time.perf_counter() - h0) / steps * 1e6
     torch.cuda.synchronize()
     ms = b0.elapsed_time(b1) / steps
+    # the same calls through srftq.DecodeAttention (arguments checked once)
+    att = S.DecodeAttention(q, kc, ks, vc, vs, sk, lk, sv, lv, group=w.group, bits=w.bits, workspace=ws, out=out)
+    att()
+    torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    b0.record()
+    for _ in range(steps):
+        att()
+    b1.record()
+    host_prep_us = (time.perf_counter() - h0) / steps * 1e6
+    torch.cuda.synchronize()
+    prep_ms = b0.elapsed_time(b1) / steps
     # and with an event pair around each call (which also drains the queue
     # between calls)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
@@ -355,6 +367,8 @@ def decode_attention_timing(w, codes, scales, sd, lam, steps: int, R: int = 6) -
     return {"workload": f"decode attention: {L} layers x K+V caches [T={w.T}, H={w.H}, d={w.d}], "
                         f"group {w.group}, int{w.bits}, {R} query heads per KV head, one query token",
             "ms": ms, "calls_back_to_back": steps, "host_enqueue_us_per_call": host_us,
+            "prepared": {"ms": prep_ms, "host_enqueue_us_per_call": host_prep_us,
+                         "call": "srftq.DecodeAttention (arguments checked once)"},
             "per_call_events": per_call,
             "algorithmic_bytes": nbytes, "GBps": gbps, "hbm_frac": gbps / HBM_PEAK_GBPS,
             "cached_tokens_per_s": L * w.H * w.T / (ms * 1e-3),

@@ -643,6 +643,77 @@ def _attention(mats, q, k_codes, k_scales, v_codes, v_scales, k_signs, k_lam, v_
     return out
 
 
+class DecodeAttention:
+    """srftq_decode_attention with every argument checked once.
+
+    For decode loops, where decode_attention()'s per-call checks take a
+    quarter of the kernels' time at a 28-layer, 32K-token step: the query
+    buffer q, the K and V caches, their signs and lambda, lengths, scale,
+    workspace, out and stream are fixed at construction (stream None: the
+    current stream at that moment; workspace and out allocated here when
+    None).  The caller refills q, appends to the caches and updates lengths
+    on the device between calls (they are read when the kernels run); each
+    call runs one step and returns out.  Not for use inside a graph capture
+    on another stream."""
+
+    def __init__(self, q, k_codes, k_scales, v_codes, v_scales, k_signs=None, k_lam=None, v_signs=None,
+                 v_lam=None, lengths=None, T=None, scale=None, group=16, bits=4, rot="srft", workspace=None,
+                 out=None, stream=None):
+        import math
+
+        import torch
+        _req(q, torch.float16, "q")
+        for t, dt, n in ((k_codes, torch.uint8, "k_codes"), (k_scales, torch.float16, "k_scales"),
+                         (v_codes, torch.uint8, "v_codes"), (v_scales, torch.float16, "v_scales"),
+                         (k_signs, torch.int8, "k_signs"), (v_signs, torch.int8, "v_signs"),
+                         (k_lam, torch.float32, "k_lam"), (v_lam, torch.float32, "v_lam"),
+                         (lengths, torch.int32, "lengths")):
+            _req(t, dt, n)
+        if q.dim() != 3:
+            raise ValueError("q must be [B, H*R, d]")
+        B, HR, d = q.shape
+        Bc, H, t_cap = _cache_dims(k_codes, k_scales, d, bits, group, "k_codes")
+        if _cache_dims(v_codes, v_scales, d, bits, group, "v_codes") != (Bc, H, t_cap) or Bc != B:
+            raise ValueError("K and V caches must both be [B, H, t_cap, .] for q's B")
+        if HR % H:
+            raise ValueError(f"q has {HR} heads, not a multiple of the {H} KV heads")
+        R = HR // H
+        for t, n in ((k_signs, "k_signs"), (k_lam, "k_lam"), (v_signs, "v_signs"), (v_lam, "v_lam")):
+            _head_rows(t, B, H, d, n, device=q.device)
+        if lengths is not None and tuple(lengths.shape) != (B,):
+            raise ValueError(f"lengths must have shape ({B},), got {tuple(lengths.shape)}")
+        _same_device(q.device, k_codes=k_codes, k_scales=k_scales, v_codes=v_codes, v_scales=v_scales,
+                     lengths=lengths, workspace=workspace, out=out)
+        T = t_cap if T is None else int(T)
+        scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+        self._shape = make_shape(B, T, H, d, group, bits, rot)
+        need = srftq_attention_workspace_bytes(self._shape, R)
+        if need == 0 and B * H > 0:
+            _check(SRFTQ_ERR_SHAPE, "srftq_attention_workspace_bytes")
+        if workspace is None:
+            workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous CUDA (HIP) tensor")
+        nbytes = workspace.numel() * workspace.element_size()
+        if nbytes < need:
+            raise ValueError(f"workspace holds {nbytes} bytes, the call needs {need}")
+        self.out = _out(out, (B, HR, d), torch.float32, q.device, "out")
+        self._kv = cache_view(k_codes, k_scales, k_signs, k_lam)
+        self._vv = cache_view(v_codes, v_scales, v_signs, v_lam)
+        self._keep = (q, k_codes, k_scales, v_codes, v_scales, k_signs, k_lam, v_signs, v_lam, lengths,
+                      workspace)      # the tensors outlive the calls
+        self._fn = lib().srftq_decode_attention
+        self._args = (ctypes.byref(self._shape), int(t_cap), int(R), _dp(q), ctypes.byref(self._kv),
+                      ctypes.byref(self._vv), _dp(lengths), float(scale), _dp(self.out), _dp(workspace),
+                      int(nbytes), _stream(stream))
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != SRFTQ_OK:
+            _check(st, "srftq_decode_attention")
+        return self.out
+
+
 def rotate(x, signs=None, rot="srft", variant="default", out=None, stream=None):
     """Rotated coordinates y = M (s . x), fp32, same shape as x."""
     import torch

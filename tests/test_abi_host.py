@@ -454,3 +454,14 @@ def test_memfloor_library_rejects_bad_arguments_before_launch():
     assert f(0, 1, a, b, 64, 0, None) == 1            # empty grid
     assert f(1, 0, None, b, 64, 64, None) == 1        # NULL input
     assert f(1, 0, a + 8, b, 64, 64, None) == 1       # misaligned
+
+
+def test_decode_attention_prepared_rejects_host_tensors():
+    """DecodeAttention checks every argument at construction: host tensors
+    raise before anything reaches the library."""
+    import torch
+    q = torch.zeros((1, 2, 128), dtype=torch.float16)
+    kc = torch.zeros((1, 1, 64, 64), dtype=torch.uint8)
+    ks = torch.zeros((1, 1, 64, 8), dtype=torch.float16)
+    with pytest.raises(ValueError):
+        S.DecodeAttention(q, kc, ks, kc, ks)

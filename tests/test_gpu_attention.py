@@ -355,3 +355,26 @@ def test_attention_in_graph_replays(kind):
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, eager[i]), f"replay {i}"
+
+
+def test_prepared_decode_attention_equals_plain_calls():
+    """DecodeAttention (arguments checked once, one library call per step)
+    gives the plain call's output bit for bit over two steps, with the query
+    refilled and the lengths changed on the device in between, and matches
+    the oracle."""
+    c = make_case(7090, 2, 700, 2, 6, 128, 16, 4, "srft", lam=True)
+    K, V = c["K"], c["V"]
+    q = dev(c["q"])
+    caches = (dev(K[0]), dev(K[1].view(np.float16)), dev(V[0]), dev(V[1].view(np.float16)))
+    side = dict(k_signs=dev(K[2]), k_lam=dev(K[3]), v_signs=dev(V[2]), v_lam=dev(V[3]))
+    lengths = dev(np.array([700, 333], dtype=np.int32))
+    att = S.DecodeAttention(q, *caches, lengths=lengths, group=16, bits=4, **side)
+    for step, (q_new, lens) in enumerate([(c["q"], [700, 333]), (c["q"][:, ::-1] * 0.5, [17, 700])]):
+        q.copy_(dev(np.ascontiguousarray(q_new)))
+        lengths.copy_(dev(np.array(lens, dtype=np.int32)))
+        got = host(att()).copy()
+        ref = host(S.decode_attention(q, *caches, lengths=lengths, group=16, bits=4, **side))
+        torch.cuda.synchronize()
+        assert np.array_equal(got, ref), f"step {step}"
+        cc = dict(c, q=np.ascontiguousarray(q_new).astype(np.float16))
+        print(step, check(cc, got, np.array(lens, dtype=np.int32)))
