@@ -254,7 +254,12 @@ __global__ __launch_bounds__(64) void dequantize_lane_kernel(const uint8_t* __re
       const int p = 64 * i + lane;
       const int v = p / CH;
       const int c = (p % CH) ^ lane_swz(v);
-      if (v < nv) *(uint4*)(base + v * stride + 16 * c) = *(const uint4*)(xo + 16 * p);
+      if (v < nv) {
+        const uint4 q = *(const uint4*)(xo + 16 * p);
+        typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+        const u32x4_t w = {q.x, q.y, q.z, q.w};
+        __builtin_nontemporal_store(w, (u32x4_t*)(base + v * stride + 16 * c));
+      }
     });
   }
 }
