@@ -532,9 +532,12 @@ __global__ __launch_bounds__(256) void attn_qprep_kernel(const uint16_t* __restr
 //   score MFMA  D[token][head]:  A = K codes, lane holds token jl, coordinates
 //               16kb + 4q + {0,2,1,3} (int4) or {0,1,2,3} (int8); B = u, lane
 //               holds head jl at the same coordinates; D: tokens 4q+e, head jl.
-//   P.V MFMA    D[coord][head]:  A = V codes, lane holds coordinate 16kb + jl
-//               of tokens 4q+e; B = fp16(p * sigma_v), tokens 4q+e, head jl
-//               (the score layout); D: coordinates 16kb + 4q + e, head jl.
+//   P.V MFMA    D[coord][head]:  A = V codes of tokens 4q+e, lane holds
+//               coordinate 16kb + jl (int8) or, per block j of 32
+//               coordinates, 32j + 2jl in acc[2j] and 32j + 2jl + 1 in
+//               acc[2j + 1] (int4: both nibbles of byte jl); B = fp16(p *
+//               sigma_v), tokens 4q+e, head jl (the score layout); D: those
+//               coordinates of rows 4q + e, head jl.
 // ----------------------------------------------------------------------------
 template <int D, int G, int BITS>
 __global__ __launch_bounds__(256) void attn_partial_kernel(const uint8_t* __restrict__ codes_k,
