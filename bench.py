@@ -11,8 +11,12 @@ coordinate, group 16, int4.
 
 Prints one JSON line: throughput in KV vectors per second (each vector
 quantized and dequantized), the per-kernel HBM roofline of the dominant
-kernel (algorithmic bytes / measured kernel time vs 8 TB/s), and the CPU
-oracle timed on a bounded sample of the same workload.
+kernel (algorithmic bytes / measured kernel time vs 8 TB/s), the memory
+floor of the same traffic (kernels that move a launch's bytes with no
+arithmetic), and the CPU oracle timed on a bounded sample of the same
+workload; then the other workloads' sections (the 128K-token roundtrip, the
+d = 256 wide head with SRFT and SRHT, tiny launches, decode appends, decode
+attention, d = 96 and rotation matrices).
 """
 from __future__ import annotations
 
