@@ -28,7 +28,7 @@ int device_cu_count() {
 
 const int8_t* plus_ones_ptr();   // defined with the device array in ones.hip
 
-int tiles_per_block(int d) { return d >= 256 ? 0 : 1; }
+int tiles_per_block(int d, int H) { return d >= 256 ? 0 : H >= 4 ? -1 : 1; }
 
 int blocks_per_cu(const void* kernel, int block) {
   static std::mutex mu;

@@ -49,7 +49,8 @@ struct Geo {
   int32_t tiles_t;       // ceil(T / 64)
   int32_t n_tiles;       // tiles_t * BH
   int32_t sign_stride;   // elements between heads' sign rows: D, or 0 for a shared row
-  int32_t tpb;           // streaming kernels: tiles per block (consecutive); 0 = persistent grid
+  int32_t tpb;           // streaming kernels: tiles per block (consecutive); 0 = persistent grid;
+                         // -1 = one tile per block in XCD-contiguous order
 };
 
 // Tiles of one block of a streaming kernel: either tpb consecutive tiles
@@ -57,7 +58,16 @@ struct Geo {
 struct TileRange {
   int first, step, remaining;   // remaining = tiles after the first
   __device__ __forceinline__ explicit TileRange(const Geo& a) {
-    if (a.tpb > 0) {
+    if (a.tpb < 0) {
+      // one tile per block, XCD-contiguous: the chip deals consecutive
+      // blocks to its 8 XCDs in turn, so block i takes tile
+      // (i mod 8) ceil(n / 8) + i / 8 and each XCD walks one contiguous
+      // eighth of the tiles (grid 8 ceil(n / 8); tiles past n exit)
+      const int per = (a.n_tiles + 7) >> 3;
+      first = (int)(blockIdx.x & 7u) * per + (int)(blockIdx.x >> 3);
+      step = 1;
+      remaining = 0;
+    } else if (a.tpb > 0) {
       first = (int)blockIdx.x * a.tpb;
       step = 1;
       const int n = a.n_tiles - first;

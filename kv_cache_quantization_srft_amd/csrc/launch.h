@@ -138,11 +138,14 @@ int device_cu_count();
 // Resident blocks per CU of a kernel at a block size (cached per kernel).
 int blocks_per_cu(const void* kernel, int block);
 
-// Tiles per block of the streaming kernels (0 = persistent grid).  One tile
-// per block lets the hardware dispatcher balance the load across CUs (waves
-// of a persistent grid finish up to 40 % apart); at d = 256, with one wave
-// per SIMD, the persistent grid's one-tile-ahead prefetch hides more latency.
-int tiles_per_block(int d);
+// Tiles per block of the streaming kernels (0 = persistent grid, -1 = one
+// tile per block in XCD-contiguous order).  One tile per block lets the
+// hardware dispatcher balance the load across CUs (waves of a persistent
+// grid finish up to 40 % apart); at d = 256, with one wave per SIMD, the
+// persistent grid's one-tile-ahead prefetch hides more latency.  With four
+// or more heads a token's rows of all heads lie within a few KB, and the
+// XCD-contiguous order keeps them on one XCD (its own L2).
+int tiles_per_block(int d, int H);
 
 // Persistent grid: at most (resident blocks per CU) x CUs, at least 1.
 inline int persistent_grid(const void* kernel, int n_tiles, int block) {
