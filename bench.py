@@ -880,15 +880,23 @@ def main():
         step(n_settle + i)
     torch.cuda.synchronize()
     i0 = n_settle + args.warmup
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # the timed steps: one event pair around all of them (events between the
+    # launches would add their own records to the step time)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for i in range(args.steps):
-        step(i0 + i, evs[i])
+        step(i0 + i)
     stop.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
+    # then the same number of steps with an event pair around each launch,
+    # for the per-kernel times and the roofline
+    i0 += args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(i0 + i, evs[i])
+    torch.cuda.synchronize()
     tq = [e[0].elapsed_time(e[1]) for e in evs]
     tdq = [e[1].elapsed_time(e[2]) for e in evs]
     q_ms = sum(tq) / args.steps
